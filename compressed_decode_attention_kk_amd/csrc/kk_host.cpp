@@ -1,0 +1,309 @@
+// Host side of the C ABI: validation, per-layer table resolution, the work
+// plan of one decode step, and kernel launches.  Nothing here allocates,
+// synchronizes or keeps state between calls.
+//
+// Table semantics follow the KV-Kaizen summary page (picx.dev): "Action Space
+// and Cost Model" (actions {inherit} U {(d, b)}, b in {2, 4, 8, 16}) and
+// "Three Non-Eviction Compression Axes" (inheriting layers read an anchor's
+// cache; the cache keeps the first d latent coordinates plus the RoPE key).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <vector>
+
+#include "kk.h"
+#include "kk_internal.h"
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool valid_bits(int b) { return b == 2 || b == 4 || b == 8 || b == 16; }
+
+// Layer table rules.  INVALID: breaks the method's rules; UNSUPPORTED: outside
+// this build's limits.
+kk_status check_model(const kk_model_cfg* c) {
+  if (!c || !c->layers) return KK_ERR_INVALID_ARGUMENT;
+  if (c->n_layers < 1 || c->n_heads < 1 || c->r < 1 || c->d_rope < 1) return KK_ERR_INVALID_ARGUMENT;
+  if (c->n_layers > KK_MAX_LAYERS) return KK_ERR_UNSUPPORTED;
+  if (c->r % 8 != 0 || c->d_rope % 16 != 0 || c->d_rope > 128) return KK_ERR_UNSUPPORTED;
+  if (c->n_heads > 4096) return KK_ERR_UNSUPPORTED;
+  for (int l = 0; l < c->n_layers; ++l) {
+    const kk_layer_cfg& L = c->layers[l];
+    if (!std::isfinite(L.sm_scale)) return KK_ERR_INVALID_ARGUMENT;
+    if (L.anchor == l) {
+      if (!valid_bits(L.bits) || L.d < 1 || L.d > c->r) return KK_ERR_INVALID_ARGUMENT;
+      if (L.d % 16 != 0 || L.d > KK_MAX_D || L.d + c->d_rope > KK_MAX_K) return KK_ERR_UNSUPPORTED;
+    } else {
+      if (l == 0 || L.anchor < 0 || L.anchor > l) return KK_ERR_INVALID_ARGUMENT;
+      if (c->layers[L.anchor].anchor != L.anchor) return KK_ERR_INVALID_ARGUMENT;
+    }
+  }
+  return KK_OK;
+}
+
+size_t stride_of(int d, int dr, int bits) {
+  if (!valid_bits(bits) || d < 1 || dr < 0) return 0;
+  const int64_t bitsum = (int64_t)(d + dr) * bits;
+  if (bitsum % 8) return 0;
+  return (size_t)((bitsum / 8 + 15) / 16 * 16);
+}
+
+struct Plan {
+  kk::DecodeArgs args;
+  kk::DecodeLaunch launch;
+  int entry_anchor[kk::kMaxEntries];   // anchor layer whose cache each entry reads
+  int64_t ws_floats = 0;
+};
+
+int bits_class(int bits) { return bits == 2 ? 0 : bits == 4 ? 1 : bits == 8 ? 2 : 3; }
+
+// Work plan of one decode step.  Groups: an anchor and the layers inheriting
+// its cache.  Each group's query rows (layer-major, head-minor) form entries of
+// <= 512 rows cut into chunks of <= 64 rows; an item is (chunk, seq, split).
+// Splits are chosen so that items carry similar byte counts; entries are
+// ordered by bytes per item, largest first.
+kk_status make_plan(const kk_model_cfg* c, int batch, int max_len, int split_tokens, Plan& P) {
+  kk::DecodeArgs& A = P.args;
+  std::memset(&A, 0, sizeof(A));
+  const int H = c->n_heads, L = c->n_layers;
+  std::vector<int> order;                              // layers grouped by anchor
+  std::vector<std::pair<int, int>> groups;             // (anchor, first index in order)
+  for (int a = 0; a < L; ++a) {
+    if (c->layers[a].anchor != a) continue;
+    groups.push_back({a, (int)order.size()});
+    for (int l = a; l < L; ++l)
+      if (c->layers[l].anchor == a) order.push_back(l);
+  }
+  for (int i = 0; i < L; ++i) A.group_layers[i] = (uint8_t)order[i];
+  int64_t off = 0;
+  for (int l = 0; l < L; ++l) {
+    const int a = c->layers[l].anchor;
+    A.layers[l].sm_scale = c->layers[l].sm_scale;
+    A.layers[l].d_eff = c->layers[a].d;
+    A.layers[l].out_off = off;
+    off += (int64_t)batch * H * c->layers[a].d;
+  }
+
+  struct Ent {
+    kk::EntryArg e;
+    int anchor;
+    int64_t bytes_item;
+  };
+  std::vector<Ent> ents;
+  const int kEntryRows = 64 * 8;
+  for (size_t gi = 0; gi < groups.size(); ++gi) {
+    const int a = groups[gi].first, begin = groups[gi].second;
+    const int end = gi + 1 < groups.size() ? groups[gi + 1].second : L;
+    const int rows = (end - begin) * H;
+    for (int rb = 0; rb < rows; rb += kEntryRows) {
+      Ent E;
+      std::memset(&E.e, 0, sizeof(E.e));
+      E.e.d = (int16_t)c->layers[a].d;
+      E.e.bits = (int16_t)c->layers[a].bits;
+      E.e.row_stride = (int32_t)stride_of(c->layers[a].d, c->d_rope, c->layers[a].bits);
+      E.e.row_begin = rb;
+      E.e.row_end = std::min(rows, rb + kEntryRows);
+      const int n = E.e.row_end - E.e.row_begin;
+      const int nrc = (n + 63) / 64;
+      E.e.nrc = (int16_t)nrc;
+      E.e.chunk_rows = (int16_t)(((n + nrc - 1) / nrc + 15) / 16 * 16);
+      E.e.lay_begin = (int16_t)begin;
+      E.anchor = a;
+      E.bytes_item = (int64_t)max_len * (E.e.row_stride + 4);
+      ents.push_back(E);
+    }
+  }
+  if ((int)ents.size() > kk::kMaxEntries) return KK_ERR_UNSUPPORTED;
+
+  int64_t total = 0;
+  for (auto& E : ents) total += E.bytes_item * E.e.nrc * batch;
+  const int64_t target = std::max<int64_t>(total / (4 * kk::kPlanCUs), 256 * 1024);
+  const int max_tiles = std::max(1, (max_len + kk::kTile - 1) / kk::kTile);
+  for (auto& E : ents) {
+    int64_t sp;
+    if (split_tokens > 0) sp = (max_len + split_tokens - 1) / split_tokens;
+    else sp = (E.bytes_item + target - 1) / target;
+    sp = std::max<int64_t>(1, std::min<int64_t>(sp, max_tiles));
+    sp = std::min<int64_t>(sp, 1024);
+    E.e.splits = (int16_t)sp;
+  }
+  std::stable_sort(ents.begin(), ents.end(), [](const Ent& x, const Ent& y) {
+    if (x.e.bits != y.e.bits) return x.e.bits < y.e.bits;
+    return x.bytes_item / x.e.splits > y.bytes_item / y.e.splits;
+  });
+  int64_t items = 0, ws = 0;
+  int merges = 0;
+  kk::DecodeLaunch& Lc = P.launch;
+  for (int c = 0; c < 4; ++c) Lc.item_begin[c] = Lc.item_end[c] = Lc.lds_bytes[c] = 0;
+  for (size_t i = 0; i < ents.size(); ++i) {
+    kk::EntryArg& e = ents[i].e;
+    e.merge_base = 0;
+    e.codes = nullptr;
+    e.scales = nullptr;
+    e.item_base = (int32_t)items;
+    const int cls = bits_class(e.bits);
+    if (Lc.item_end[cls] == Lc.item_begin[cls]) Lc.item_begin[cls] = (int)items;
+    items += (int64_t)e.nrc * batch * e.splits;
+    Lc.item_end[cls] = (int)std::min<int64_t>(items, 0x7fffffff);
+    if (e.splits > 1) {
+      e.ws_off = ws;
+      ws += (int64_t)e.nrc * batch * e.splits * kk::partial_slot_floats(e.d);
+      e.merge_base = merges;
+      merges += e.nrc * batch;
+    }
+    Lc.lds_bytes[cls] = std::max(Lc.lds_bytes[cls], kk::decode_lds_bytes(e.row_stride, e.d + c->d_rope, e.bits));
+    if (Lc.lds_bytes[cls] > 160 * 1024) return KK_ERR_UNSUPPORTED;
+    A.entries[i] = e;
+    P.entry_anchor[i] = ents[i].anchor;
+  }
+  if (items > 0x7fffffff) return KK_ERR_UNSUPPORTED;
+  A.n_entries = (int32_t)ents.size();
+  A.total_items = (int32_t)items;
+  Lc.merge_blocks = merges;
+  P.ws_floats = ws;
+  return KK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kk_row_stride_bytes(int32_t d, int32_t d_rope, int32_t bits) { return stride_of(d, d_rope, bits); }
+
+kk_status kk_validate_model(const kk_model_cfg* cfg) { return check_model(cfg); }
+
+kk_status kk_cache_bytes(const kk_model_cfg* cfg, int32_t layer, int32_t batch, int32_t t_cap, size_t* codes_bytes,
+                         size_t* scales_bytes) {
+  kk_status st = check_model(cfg);
+  if (st != KK_OK) return st;
+  if (layer < 0 || layer >= cfg->n_layers || cfg->layers[layer].anchor != layer) return KK_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || t_cap < 1 || !codes_bytes || !scales_bytes) return KK_ERR_INVALID_ARGUMENT;
+  const kk_layer_cfg& L = cfg->layers[layer];
+  *codes_bytes = (size_t)batch * (size_t)t_cap * stride_of(L.d, cfg->d_rope, L.bits);
+  *scales_bytes = (size_t)batch * (size_t)t_cap * sizeof(float);
+  return KK_OK;
+}
+
+kk_status kk_out_offsets(const kk_model_cfg* cfg, int32_t batch, int64_t* offsets) {
+  kk_status st = check_model(cfg);
+  if (st != KK_OK) return st;
+  if (batch < 1 || !offsets) return KK_ERR_INVALID_ARGUMENT;
+  int64_t off = 0;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    offsets[l] = off;
+    off += (int64_t)batch * cfg->n_heads * cfg->layers[cfg->layers[l].anchor].d;
+  }
+  offsets[cfg->n_layers] = off;
+  return KK_OK;
+}
+
+kk_status kk_quantize_write(const kk_model_cfg* cfg, int32_t layer, const void* latent, const void* rope,
+                            kk_dtype src_dtype, int64_t latent_ld, int64_t rope_ld, int64_t n_src, int32_t n_tokens,
+                            const int32_t* src_index, const int64_t* dst_slot, kk_cache dst, int32_t batch,
+                            int32_t t_cap, hipStream_t stream) {
+  kk_status st = check_model(cfg);
+  if (st != KK_OK) return st;
+  if (layer < 0 || layer >= cfg->n_layers || cfg->layers[layer].anchor != layer) return KK_ERR_INVALID_ARGUMENT;
+  if (src_dtype != KK_DTYPE_F32 && src_dtype != KK_DTYPE_BF16) return KK_ERR_INVALID_ARGUMENT;
+  if (n_tokens < 0 || n_src < 0 || batch < 1 || t_cap < 1) return KK_ERR_INVALID_ARGUMENT;
+  const kk_layer_cfg& L = cfg->layers[layer];
+  if (latent_ld < L.d || rope_ld < cfg->d_rope) return KK_ERR_INVALID_ARGUMENT;
+  if (n_tokens == 0) return KK_OK;
+  const size_t ea = src_dtype == KK_DTYPE_F32 ? 4 : 2;
+  if (!latent || !rope || !dst_slot || !dst.codes || !dst.scales) return KK_ERR_INVALID_ARGUMENT;
+  if (!aligned(latent, ea) || !aligned(rope, ea) || !aligned(dst_slot, 8) || (src_index && !aligned(src_index, 4)))
+    return KK_ERR_INVALID_ARGUMENT;
+  if (!aligned(dst.codes, 16) || !aligned(dst.scales, 16)) return KK_ERR_INVALID_ARGUMENT;
+  kk::WriteArgs a;
+  a.latent = latent;
+  a.rope = rope;
+  a.src_index = src_index;
+  a.dst_slot = dst_slot;
+  a.codes = dst.codes;
+  a.scales = dst.scales;
+  a.latent_ld = latent_ld;
+  a.rope_ld = rope_ld;
+  a.n_src = n_src;
+  a.n_slots = (int64_t)batch * t_cap;
+  a.n_tokens = n_tokens;
+  a.d = L.d;
+  a.d_rope = cfg->d_rope;
+  a.bits = L.bits;
+  a.row_stride = (int32_t)stride_of(L.d, cfg->d_rope, L.bits);
+  a.src_bf16 = src_dtype == KK_DTYPE_BF16;
+  return kk::launch_write(a, stream) == hipSuccess ? KK_OK : KK_ERR_DEVICE;
+}
+
+kk_status kk_decode_workspace_bytes(const kk_model_cfg* cfg, int32_t batch, int32_t max_seq_len,
+                                    int32_t split_tokens, size_t* bytes) {
+  kk_status st = check_model(cfg);
+  if (st != KK_OK) return st;
+  if (batch < 1 || max_seq_len < 0 || split_tokens < 0 || !bytes) return KK_ERR_INVALID_ARGUMENT;
+  if (split_tokens % kk::kTile) return KK_ERR_INVALID_ARGUMENT;
+  Plan P;
+  st = make_plan(cfg, batch, max_seq_len, split_tokens, P);
+  if (st != KK_OK) return st;
+  *bytes = (size_t)P.ws_floats * sizeof(float);
+  return KK_OK;
+}
+
+kk_status kk_decode_attn(const kk_model_cfg* cfg, const kk_cache* caches, int32_t batch, int32_t t_cap,
+                         const int32_t* seq_lens, int32_t max_seq_len, const void* q_lat, const void* q_rope,
+                         kk_dtype q_dtype, float* out, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  kk_status st = check_model(cfg);
+  if (st != KK_OK) return st;
+  if (!caches || batch < 1 || t_cap < 1 || max_seq_len < 0 || max_seq_len > t_cap) return KK_ERR_INVALID_ARGUMENT;
+  if (split_tokens < 0 || split_tokens % kk::kTile) return KK_ERR_INVALID_ARGUMENT;
+  if (q_dtype != KK_DTYPE_F32 && q_dtype != KK_DTYPE_BF16) return KK_ERR_INVALID_ARGUMENT;
+  if (!seq_lens || !q_lat || !q_rope || !out) return KK_ERR_INVALID_ARGUMENT;
+  if (!aligned(seq_lens, 4) || !aligned(q_lat, 16) || !aligned(q_rope, 16) || !aligned(out, 16))
+    return KK_ERR_INVALID_ARGUMENT;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    if (cfg->layers[l].anchor != l) continue;
+    if (!caches[l].codes || !caches[l].scales) return KK_ERR_INVALID_ARGUMENT;
+    if (!aligned(caches[l].codes, 16) || !aligned(caches[l].scales, 16)) return KK_ERR_INVALID_ARGUMENT;
+  }
+  if ((int64_t)cfg->n_layers * batch * cfg->n_heads > ((int64_t)1 << 31)) return KK_ERR_UNSUPPORTED;
+  Plan P;
+  st = make_plan(cfg, batch, max_seq_len, split_tokens, P);
+  if (st != KK_OK) return st;
+  const size_t need = (size_t)P.ws_floats * sizeof(float);
+  if (need > 0) {
+    if (!workspace || !aligned(workspace, 256)) return KK_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < need) return KK_ERR_WORKSPACE_TOO_SMALL;
+  }
+  kk::DecodeArgs& A = P.args;
+  for (int i = 0; i < A.n_entries; ++i) {
+    const int anchor = P.entry_anchor[i];
+    A.entries[i].codes = caches[anchor].codes;
+    A.entries[i].scales = caches[anchor].scales;
+  }
+  A.q_lat = q_lat;
+  A.q_rope = q_rope;
+  A.out = out;
+  A.ws = static_cast<float*>(workspace);
+  A.seq_lens = seq_lens;
+  A.batch = batch;
+  A.heads = cfg->n_heads;
+  A.r = cfg->r;
+  A.d_rope = cfg->d_rope;
+  A.t_cap = t_cap;
+  A.q_is_f32 = q_dtype == KK_DTYPE_F32;
+  return kk::launch_decode(A, P.launch, stream) == hipSuccess ? KK_OK : KK_ERR_DEVICE;
+}
+
+const char* kk_status_string(kk_status s) {
+  switch (s) {
+    case KK_OK: return "ok";
+    case KK_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case KK_ERR_UNSUPPORTED: return "unsupported by this build";
+    case KK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case KK_ERR_DEVICE: return "device error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

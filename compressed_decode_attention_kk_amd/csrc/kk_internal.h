@@ -1,0 +1,84 @@
+// Internal launch descriptors shared by the host planner and the gfx950
+// kernels of the compressed decode-attention library.  Not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kk {
+
+// ---- decode kernel geometry -------------------------------------------------
+constexpr int kWaves = 4;            // waves per workgroup (256 threads)
+constexpr int kThreads = 64 * kWaves;
+constexpr int kTile = 32;            // cached tokens per pipeline stage
+constexpr int kMaxRowBlocks = 4;     // 16-row MFMA blocks per work item (<= 64 query rows)
+constexpr int kMaxChunksPerWave = 5; // 32-wide contraction chunks per wave in Q.K (K <= 640)
+constexpr int kMaxUnitsPerWave = 4;  // 32-feature output units per wave in P.V (d <= 512)
+constexpr int kMaxEntries = 96;      // group entries per launch
+constexpr int kMaxLayers = 64;
+constexpr int kPlanCUs = 256;        // compute units assumed by the split policy
+constexpr float kLazyRescale = 8.0f; // log2 headroom before the running max is moved
+
+// One layer: softmax scale, kept width of its anchor and the float offset of
+// its block in the packed output.
+struct LayerArg {
+  float sm_scale;
+  int32_t d_eff;
+  int64_t out_off;
+};
+
+// One group entry: the query rows [row_begin, row_end) of one anchor group
+// (an anchor and the layers that inherit its cache), cut into nrc chunks of
+// at most 64 rows; every (chunk, sequence, split) triple is one work item.
+struct EntryArg {
+  const uint8_t* codes;
+  const float* scales;
+  int64_t ws_off;        // float offset of this entry's split partials
+  int32_t item_base;     // first work item (decode kernel block)
+  int32_t merge_base;    // first merge block (only when splits > 1)
+  int32_t row_stride;    // bytes per cached row
+  int32_t row_begin, row_end;
+  int16_t d, bits;
+  int16_t nrc, chunk_rows;
+  int16_t splits, lay_begin;
+};
+
+struct DecodeArgs {
+  const void* q_lat;
+  const void* q_rope;
+  float* out;
+  float* ws;
+  const int32_t* seq_lens;
+  int32_t batch, heads, r, d_rope, t_cap;
+  int32_t n_entries, total_items;
+  int32_t q_is_f32;
+  uint8_t group_layers[kMaxLayers];   // layers ordered by group
+  LayerArg layers[kMaxLayers];
+  EntryArg entries[kMaxEntries];
+};
+
+// Partial slot of one work item in the workspace: O [64][d] then m[64], l[64].
+__host__ __device__ inline int64_t partial_slot_floats(int d) { return 64 * (int64_t)d + 128; }
+
+struct WriteArgs {
+  const void* latent;
+  const void* rope;
+  const int32_t* src_index;
+  const int64_t* dst_slot;
+  uint8_t* codes;
+  float* scales;
+  int64_t latent_ld, rope_ld, n_src, n_slots;
+  int32_t n_tokens, d, d_rope, bits, row_stride, src_bf16;
+};
+
+hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
+// Per bit-width launch ranges (class c: bits 2 << c): items [item_begin, item_end).
+struct DecodeLaunch {
+  int item_begin[4], item_end[4], lds_bytes[4];
+  int merge_blocks;
+};
+
+int decode_lds_bytes(int row_stride, int K, int bits);
+hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t stream);
+
+}  // namespace kk

@@ -1,0 +1,229 @@
+"""ctypes binding of libkk.so (the C ABI declared in include/kk.h).
+
+Argument marshalling only: torch tensors supply device pointers and the
+current HIP stream; every step of the decode path runs in the library's
+kernels.  The binding fails loudly when the library is missing.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkk.so")
+
+KK_OK, KK_ERR_INVALID_ARGUMENT, KK_ERR_UNSUPPORTED, KK_ERR_WORKSPACE_TOO_SMALL, KK_ERR_DEVICE = range(5)
+KK_DTYPE_F32, KK_DTYPE_BF16 = 0, 1
+TILE = 32
+
+
+class KKError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class LayerCfg(ctypes.Structure):
+    _fields_ = [("anchor", ctypes.c_int32), ("d", ctypes.c_int32), ("bits", ctypes.c_int32),
+                ("sm_scale", ctypes.c_float)]
+
+
+class ModelCfg(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("r", ctypes.c_int32),
+                ("d_rope", ctypes.c_int32), ("layers", ctypes.POINTER(LayerCfg))]
+
+
+class Cache(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib():
+    """Load libkk.so (built by compressed_decode_attention_kk_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m compressed_decode_attention_kk_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.kk_row_stride_bytes.restype = ctypes.c_size_t
+        L.kk_row_stride_bytes.argtypes = [ctypes.c_int32] * 3
+        L.kk_validate_model.argtypes = [ctypes.POINTER(ModelCfg)]
+        L.kk_cache_bytes.argtypes = [ctypes.POINTER(ModelCfg), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+        L.kk_out_offsets.argtypes = [ctypes.POINTER(ModelCfg), ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
+        L.kk_quantize_write.argtypes = [ctypes.POINTER(ModelCfg), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_void_p, Cache, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_void_p]
+        L.kk_decode_workspace_bytes.argtypes = [ctypes.POINTER(ModelCfg), ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.kk_decode_attn.argtypes = [ctypes.POINTER(ModelCfg), ctypes.POINTER(Cache), ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                     ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                     ctypes.c_void_p]
+        L.kk_status_string.restype = ctypes.c_char_p
+        L.kk_status_string.argtypes = [ctypes.c_int]
+        for name in ("kk_validate_model", "kk_cache_bytes", "kk_out_offsets", "kk_quantize_write",
+                     "kk_decode_workspace_bytes", "kk_decode_attn"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().kk_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != KK_OK:
+        raise KKError(status, what)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(dt):
+    if dt == torch.float32:
+        return KK_DTYPE_F32
+    if dt == torch.bfloat16:
+        return KK_DTYPE_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+@dataclass
+class LayerSpec:
+    anchor: int
+    d: int
+    bits: int
+    sm_scale: float
+
+
+class Model:
+    """Per-layer table + shape (a kk_model_cfg)."""
+
+    def __init__(self, layers, n_heads: int, r: int, d_rope: int):
+        self.layers = [LayerSpec(int(l.anchor), int(l.d), int(l.bits), float(l.sm_scale)) for l in layers]
+        self.n_layers, self.n_heads, self.r, self.d_rope = len(self.layers), int(n_heads), int(r), int(d_rope)
+        self._arr = (LayerCfg * self.n_layers)(*[LayerCfg(l.anchor, l.d, l.bits, l.sm_scale) for l in self.layers])
+        self._cfg = ModelCfg(self.n_layers, self.n_heads, self.r, self.d_rope, self._arr)
+
+    @property
+    def cfg(self):
+        return ctypes.byref(self._cfg)
+
+    def anchors(self):
+        return [l for l, s in enumerate(self.layers) if s.anchor == l]
+
+    def d_eff(self, l):
+        return self.layers[self.layers[l].anchor].d
+
+    def validate(self):
+        _check(lib().kk_validate_model(self.cfg), "kk_validate_model")
+
+
+def row_stride_bytes(d: int, d_rope: int, bits: int) -> int:
+    return int(lib().kk_row_stride_bytes(d, d_rope, bits))
+
+
+def cache_bytes(model: Model, layer: int, batch: int, t_cap: int):
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().kk_cache_bytes(model.cfg, layer, batch, t_cap, ctypes.byref(cb), ctypes.byref(sb)), "kk_cache_bytes")
+    return cb.value, sb.value
+
+
+def out_offsets(model: Model, batch: int):
+    arr = (ctypes.c_int64 * (model.n_layers + 1))()
+    _check(lib().kk_out_offsets(model.cfg, batch, arr), "kk_out_offsets")
+    return list(arr)
+
+
+def alloc_cache(model: Model, layer: int, batch: int, t_cap: int, device="cuda"):
+    """Device buffers of one anchor cache: (codes uint8 [B, T_cap, stride], scales f32 [B, T_cap])."""
+    cb, _ = cache_bytes(model, layer, batch, t_cap)
+    stride = cb // (batch * t_cap)
+    codes = torch.empty((batch, t_cap, stride), dtype=torch.uint8, device=device)
+    scales = torch.empty((batch, t_cap), dtype=torch.float32, device=device)
+    return codes, scales
+
+
+def quantize_write(model: Model, layer: int, latent: torch.Tensor, rope: torch.Tensor, codes: torch.Tensor,
+                   scales: torch.Tensor, dst_slot: torch.Tensor, src_index: torch.Tensor | None = None,
+                   stream=None):
+    """Quantize source rows latent [n_src, >= d] / rope [n_src, d_R] into anchor `layer`'s cache.
+
+    dst_slot: int64 [n_tokens] (seq * t_cap + position); src_index: int32 [n_tokens] or None.
+    codes/scales: the anchor's cache buffers [B, T_cap, stride] / [B, T_cap].
+    """
+    assert latent.is_cuda and rope.is_cuda and codes.is_cuda and scales.is_cuda and dst_slot.is_cuda
+    assert latent.dim() == 2 and rope.dim() == 2 and latent.stride(1) == 1 and rope.stride(1) == 1
+    assert latent.dtype == rope.dtype and dst_slot.dtype == torch.int64 and dst_slot.is_contiguous()
+    assert codes.dtype == torch.uint8 and scales.dtype == torch.float32 and codes.is_contiguous() and scales.is_contiguous()
+    if src_index is not None:
+        assert src_index.dtype == torch.int32 and src_index.is_contiguous() and src_index.is_cuda
+        assert src_index.numel() == dst_slot.numel()
+    batch, t_cap = scales.shape
+    st = lib().kk_quantize_write(model.cfg, layer, _ptr(latent), _ptr(rope), _dtype_code(latent.dtype),
+                                 latent.stride(0), rope.stride(0), latent.shape[0], dst_slot.numel(),
+                                 _ptr(src_index), _ptr(dst_slot), Cache(codes.data_ptr(), scales.data_ptr()),
+                                 batch, t_cap, _stream(stream))
+    _check(st, "kk_quantize_write")
+
+
+def workspace_bytes(model: Model, batch: int, max_seq_len: int, split_tokens: int = 0) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().kk_decode_workspace_bytes(model.cfg, batch, max_seq_len, split_tokens, ctypes.byref(b)),
+           "kk_decode_workspace_bytes")
+    return b.value
+
+
+class Decoder:
+    """Holds the cache pointer table, output and workspace for repeated decode steps."""
+
+    def __init__(self, model: Model, caches: dict, batch: int, t_cap: int, max_seq_len: int,
+                 split_tokens: int = 0, device="cuda"):
+        self.model, self.batch, self.t_cap, self.max_seq_len = model, batch, t_cap, max_seq_len
+        self.split_tokens = split_tokens
+        self.caches = caches
+        self._ctab = (Cache * model.n_layers)()
+        for l in range(model.n_layers):
+            if model.layers[l].anchor == l:
+                c, s = caches[l]
+                self._ctab[l] = Cache(c.data_ptr(), s.data_ptr())
+        offs = out_offsets(model, batch)
+        self.offsets = offs
+        self.out = torch.empty(offs[-1], dtype=torch.float32, device=device)
+        wb = workspace_bytes(model, batch, max_seq_len, split_tokens)
+        self.workspace = torch.empty(max(wb, 256) // 4 + 64, dtype=torch.float32, device=device)
+        self.ws_bytes = wb
+
+    def __call__(self, q_lat: torch.Tensor, q_rope: torch.Tensor, seq_lens: torch.Tensor, stream=None):
+        m = self.model
+        assert q_lat.is_contiguous() and q_rope.is_contiguous() and q_lat.dtype == q_rope.dtype
+        assert tuple(q_lat.shape) == (m.n_layers, self.batch, m.n_heads, m.r)
+        assert tuple(q_rope.shape) == (m.n_layers, self.batch, m.n_heads, m.d_rope)
+        assert seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.numel() == self.batch
+        ws = self.workspace
+        wptr = (ws.data_ptr() + 255) // 256 * 256
+        st = lib().kk_decode_attn(m.cfg, self._ctab, self.batch, self.t_cap, _ptr(seq_lens), self.max_seq_len,
+                                  _ptr(q_lat), _ptr(q_rope), _dtype_code(q_lat.dtype), _ptr(self.out),
+                                  self.split_tokens, ctypes.c_void_p(wptr), self.ws_bytes, _stream(stream))
+        _check(st, "kk_decode_attn")
+        return self.out
+
+    def layer_out(self, l: int) -> torch.Tensor:
+        """View of layer l's output [B, H, d_eff]."""
+        m = self.model
+        return self.out[self.offsets[l]:self.offsets[l + 1]].view(self.batch, m.n_heads, m.d_eff(l))

@@ -1,0 +1,180 @@
+/*
+ * kk.h -- C ABI of the MI355X (gfx950) library for KV-Kaizen compressed
+ * decode attention: a per-layer compressed MLA cache (depth, rank and
+ * precision choices per layer) and one decode step of absorbed-MLA attention
+ * over it.
+ *
+ * Method source: "KV-Kaizen: Learning Context-Adaptive Cache Compression
+ * Choices" (arXiv 2609.37988), picx.dev whiteboard summary page:
+ *   - "Three Non-Eviction Compression Axes": depth (an anchor layer owns a
+ *     cache, later layers inherit it), rank (the MLA cache keeps the first
+ *     d <= r coordinates of the latent c^KV plus the decoupled RoPE key k^R),
+ *     precision (stored at b <= 16 bits, symmetric uniform quantization, one
+ *     scale per token);
+ *   - "Action Space and Cost Model": per-layer actions {inherit} U {(d, b)},
+ *     b in {2, 4, 8, 16}; cost (d + d_R) * b bits per token;
+ *   - "Selector Architecture and Training", Inference item: the per-layer
+ *     configuration is chosen once before pre-fill and fixed for every
+ *     generated token (here: an input table, constant across calls);
+ *   - "Background: The KV Cache Bottleneck": every decoded token reads the
+ *     whole cache, so decode is bound by memory bandwidth.
+ *
+ * Conventions shared by every entry point
+ *   - All device pointers are HIP device allocations owned by the caller.
+ *     The library never allocates, frees or synchronizes, and keeps no
+ *     mutable global state; calls are thread-safe.
+ *   - Every call validates its arguments on the host before enqueueing
+ *     anything; a non-KK_OK status means nothing was enqueued.
+ *   - Work is enqueued on the caller's stream and returns asynchronously;
+ *     a kernel fault surfaces at the caller's next synchronization.
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified results.
+ *
+ * Cache layout (one anchor layer)
+ *   codes  : uint8 [batch][t_cap][row_stride]; row = d + d_R fields of b bits,
+ *            field j (latent coordinate j for j < d, RoPE coordinate j - d
+ *            after) is the two's-complement code at bit offset j*b of the row,
+ *            bytes little-endian; row_stride = ceil((d + d_R)*b/8 / 16) * 16,
+ *            padding bytes are zero.  16-byte aligned.
+ *   scales : float32 [batch][t_cap], one per token.  16-byte aligned.
+ *   Quantization of one token v = [c[0:d] || k^R[0:d_R]] (fp32):
+ *     qmax = 2^(b-1) - 1; amax = max |v_j|; scale = amax / qmax (IEEE fp32
+ *     division, round to nearest even); code_j = clamp(rint(v_j / scale),
+ *     -qmax, qmax) with IEEE fp32 division and ties to even; amax = 0 gives
+ *     scale 0 and all codes 0.  Dequantized value: code * scale.
+ *
+ * Decode output layout: float32, packed per layer as [batch][n_heads][d_eff]
+ * at the float offsets returned by kk_out_offsets (layer order), where d_eff
+ * is the d of the layer's anchor.
+ */
+#ifndef KK_H_
+#define KK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KK_OK = 0,
+  KK_ERR_INVALID_ARGUMENT = 1,   /* a rule below is broken (null, misaligned, out of range) */
+  KK_ERR_UNSUPPORTED = 2,        /* valid for the method but outside this build's limits */
+  KK_ERR_WORKSPACE_TOO_SMALL = 3,
+  KK_ERR_DEVICE = 4              /* a HIP launch or query failed */
+} kk_status;
+
+typedef enum { KK_DTYPE_F32 = 0, KK_DTYPE_BF16 = 1 } kk_dtype;
+
+/* Build limits (KK_ERR_UNSUPPORTED beyond them). */
+#define KK_MAX_LAYERS 64
+#define KK_MAX_D 512           /* kept latent width d (and r >= d, any r) */
+#define KK_MAX_K 640           /* d + d_R */
+
+/* One layer's action ("Action Space and Cost Model").
+ *   anchor == own index : the layer is an anchor with action (d, bits);
+ *   anchor <  own index : the layer inherits the cache of layer `anchor`,
+ *                         which must itself be an anchor; d and bits are
+ *                         ignored (the anchor's are used).
+ * sm_scale is the layer's softmax scale (any finite value; the workloads use
+ * 1/sqrt(d_eff + d_R)).
+ * Rules: layer 0 is an anchor; 0 < d <= r, d % 16 == 0; bits in {2,4,8,16};
+ * d_R % 16 == 0; d + d_R <= KK_MAX_K; d <= KK_MAX_D. */
+typedef struct {
+  int32_t anchor;
+  int32_t d;
+  int32_t bits;
+  float sm_scale;
+} kk_layer_cfg;
+
+typedef struct {
+  int32_t n_layers;             /* 1 .. KK_MAX_LAYERS */
+  int32_t n_heads;              /* query heads per layer, >= 1 */
+  int32_t r;                    /* full latent width (q_lat row length) */
+  int32_t d_rope;               /* RoPE key width d_R, 16 .. 128, multiple of 16 */
+  const kk_layer_cfg* layers;   /* host array [n_layers] */
+} kk_model_cfg;
+
+/* Device buffers of one anchor layer's cache (see layout above). */
+typedef struct {
+  uint8_t* codes;
+  float* scales;
+} kk_cache;
+
+/* Row stride in bytes of a (d, d_rope, bits) cache; 0 if the combination is
+ * invalid (bits not in {2,4,8,16}, non-positive widths, or (d+d_rope)*bits
+ * not a multiple of 8). */
+size_t kk_row_stride_bytes(int32_t d, int32_t d_rope, int32_t bits);
+
+/* Checks the table rules above. */
+kk_status kk_validate_model(const kk_model_cfg* cfg);
+
+/* Bytes of the codes and scales buffers of anchor `layer` for [batch][t_cap].
+ * Inheriting layers own no cache: KK_ERR_INVALID_ARGUMENT. */
+kk_status kk_cache_bytes(const kk_model_cfg* cfg, int32_t layer, int32_t batch, int32_t t_cap,
+                         size_t* codes_bytes, size_t* scales_bytes);
+
+/* Float offsets of each layer's output block in the packed decode output:
+ * offsets[l] for l in [0, n_layers], offsets[n_layers] = total floats.
+ * `offsets` is a host array of n_layers + 1 entries. */
+kk_status kk_out_offsets(const kk_model_cfg* cfg, int32_t batch, int64_t* offsets);
+
+/* Quantize-and-pack cache write (pre-fill and append) for anchor `layer`.
+ *
+ * Source rows: latent [n_src][latent_ld] (first d of r coordinates used) and
+ * rope [n_src][rope_ld] (first d_rope used), both `src_dtype` (float32, or
+ * bf16 widened exactly), device, 4-byte aligned.  Token i (0 <= i < n_tokens)
+ * reads source row src_index[i] (device int32, nullable: identity) and writes
+ * cache slot dst_slot[i] (device int64: seq * t_cap + position).  A token
+ * whose source row is outside [0, n_src) or whose slot is outside
+ * [0, batch * t_cap) is skipped.  Gathering by src_index composes eviction:
+ * the kept positions of a longer context are packed densely.
+ * Two tokens writing the same slot race. */
+kk_status kk_quantize_write(const kk_model_cfg* cfg, int32_t layer,
+                            const void* latent, const void* rope, kk_dtype src_dtype,
+                            int64_t latent_ld, int64_t rope_ld, int64_t n_src, int32_t n_tokens,
+                            const int32_t* src_index, const int64_t* dst_slot,
+                            kk_cache dst, int32_t batch, int32_t t_cap, hipStream_t stream);
+
+/* Workspace bytes kk_decode_attn needs for this model, batch and
+ * max_seq_len, with the same split_tokens argument (0 = automatic).
+ * The workspace holds split partials only; it need not be zeroed. */
+kk_status kk_decode_workspace_bytes(const kk_model_cfg* cfg, int32_t batch, int32_t max_seq_len,
+                                    int32_t split_tokens, size_t* bytes);
+
+/* One decode step of absorbed-MLA attention for every layer of the table.
+ *
+ * For layer l with anchor a = cfg->layers[l].anchor, d = d_a, b = b_a, each
+ * sequence s and head h, over the cached tokens t < len_s:
+ *   z_t = sm_scale_l * (q_lat[l,s,h,0:d] . c_a[s,t,0:d] + q_rope[l,s,h,:] . kR_a[s,t,:])
+ *   out[l,s,h,i] = sum_t softmax(z)_t * c_a[s,t,i],  i < d
+ * with c_a, kR_a the dequantized anchor cache (code * scale).  Inheriting
+ * layers read their anchor's buffers (no copy); len_s = 0 gives zeros.
+ *
+ * caches     : host array [n_layers]; entries of inheriting layers are ignored.
+ * seq_lens   : device int32 [batch]; each value is clamped to [0, t_cap].
+ * max_seq_len: host bound used for planning, >= every seq_lens value
+ *              (values above it are clamped to it).
+ * q_lat      : device [n_layers][batch][n_heads][r], q_dtype.
+ * q_rope     : device [n_layers][batch][n_heads][d_rope], q_dtype.
+ * out        : device float32, packed as kk_out_offsets describes.
+ * split_tokens: tokens per split of one sequence (multiple of 32), or 0 to let
+ *              the library choose; results agree across choices within
+ *              floating-point rounding and are bitwise reproducible for a
+ *              fixed choice.
+ * workspace  : device, >= kk_decode_workspace_bytes, 256-byte aligned. */
+kk_status kk_decode_attn(const kk_model_cfg* cfg, const kk_cache* caches, int32_t batch, int32_t t_cap,
+                         const int32_t* seq_lens, int32_t max_seq_len,
+                         const void* q_lat, const void* q_rope, kk_dtype q_dtype, float* out,
+                         int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Static description of a status code. */
+const char* kk_status_string(kk_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KK_H_ */

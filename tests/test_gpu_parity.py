@@ -1,0 +1,218 @@
+"""GPU parity: the HIP library against the CPU oracle, through the C ABI.
+
+Bar: codes and scales bit-exact; decode output per layer (and here per
+sampled (layer, sequence)) within max-abs 2e-3 * max|o_oracle|.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kk_oracle as ko
+import synth
+from synth.device import build_caches
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.fixture(scope="module")
+def kk():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import compressed_decode_attention_kk_amd as kk
+    kk.lib()
+    return kk
+
+
+def oracle_layers(w):
+    return [ko.Layer(s.anchor, s.d, s.bits, s.sm_scale) for s in w.layers]
+
+
+def source_cpu(w, a, s):
+    """fp32 source rows of anchor a, sequence s, exactly as the GPU side drew them."""
+    if w.nominal_context:
+        lat, rope, pos = synth.full_context_rows(w, a, s, "cuda")
+        return lat[pos.long()].cpu().numpy(), rope[pos.long()].cpu().numpy()
+    lat, rope, _ = synth.source_rows(w, a, "cuda")
+    return lat[s].cpu().numpy(), rope[s].cpu().numpy()
+
+
+def run_gpu(kk, w, seq_lens=None, t_cap=None, split_tokens=0):
+    model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+    t_cap = t_cap or w.seq_len
+    lens = [w.seq_len] * w.batch if seq_lens is None else list(seq_lens)
+    caches = build_caches(kk, model, w, t_cap, seq_lens=[min(x, t_cap) for x in lens])
+    ql, qr = synth.queries(w, "cuda")
+    dec = kk.Decoder(model, caches, w.batch, t_cap, max(min(max(lens), t_cap), 0), split_tokens=split_tokens)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    dec(ql, qr, sl)
+    torch.cuda.synchronize()
+    return model, caches, dec, ql, qr
+
+
+def check_layer_seq(w, dec, caches, ql, qr, l, s, seq_len, src_cache=None):
+    a = w.layers[l].anchor
+    d, b = w.d_eff(l), w.bits_eff(l)
+    if src_cache is not None and a in src_cache:
+        lat, rope = src_cache[a]
+    else:
+        lat, rope = source_cpu(w, a, s)
+    packed, scales, _ = ko.write_cache(lat[:seq_len], rope[:seq_len], d, b)
+    # writer parity (bit-exact) on the rows this sequence holds
+    codes_gpu, scales_gpu = caches[a]
+    assert np.array_equal(codes_gpu[s, :seq_len].cpu().numpy(), packed), f"codes differ: anchor {a} seq {s}"
+    assert np.array_equal(scales_gpu[s, :seq_len].cpu().numpy().view(np.uint32), scales.view(np.uint32))
+    q_lat = ql[l, s].float().cpu().numpy().astype(np.float64)
+    q_rope = qr[l, s].float().cpu().numpy().astype(np.float64)
+    ref = ko.decode_layer(q_lat, q_rope, packed, scales, d, w.d_rope, b, w.layers[l].sm_scale, seq_len)
+    got = dec.layer_out(l)[s].cpu().numpy().astype(np.float64)
+    err = np.max(np.abs(got - ref)) if ref.size else 0.0
+    scale = np.max(np.abs(ref)) if ref.size else 0.0
+    if scale == 0:
+        assert err == 0
+    else:
+        assert err <= TOL * scale, f"layer {l} seq {s}: err {err:.3e} vs {TOL} * {scale:.3e} (ratio {err / scale:.2e})"
+    return err / scale if scale else 0.0
+
+
+def test_tiny_workload_full(kk):
+    w = synth.workload(0)
+    model, caches, dec, ql, qr = run_gpu(kk, w)
+    r = check_layer_seq(w, dec, caches, ql, qr, 0, 0, 256)
+    print(f"tiny: err ratio {r:.2e}")
+
+
+# A mixed table that spans every bit width, widths from 64 to 256, inheriting
+# groups of 1-3 layers (group rows 40..120 span 1-2 row chunks).
+MIXED_SMALL = [[0, 128, 8], [0, 0, 0], [2, 64, 2], [3, 256, 16], [3, 0, 0], [3, 0, 0], [6, 192, 4],
+               [7, 256, 2], [8, 64, 16], [8, 0, 0]]
+
+
+@pytest.mark.parametrize("split_tokens", [0, 64])
+def test_mixed_small_ragged_full(kk, split_tokens):
+    w = synth.small_workload(10, len(MIXED_SMALL), 40, 4, 1000, 256, 32, MIXED_SMALL)
+    lens = [1000, 517, 33, 1]
+    model, caches, dec, ql, qr = run_gpu(kk, w, seq_lens=lens, t_cap=1024, split_tokens=split_tokens)
+    worst = 0.0
+    for s in range(w.batch):
+        src = {a: source_cpu(w, a, s) for a in w.anchors()}
+        for l in range(w.n_layers):
+            worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, lens[s], src))
+    print(f"mixed small split={split_tokens}: worst err ratio {worst:.2e}")
+
+
+def test_edge_lengths_and_empty(kk):
+    table = [[0, 64, 4], [1, 32, 8], [1, 0, 0]]
+    w = synth.small_workload(11, 3, 24, 6, 70, 64, 16, table)
+    lens = [0, 1, 31, 32, 33, 70]
+    model, caches, dec, ql, qr = run_gpu(kk, w, seq_lens=lens, t_cap=72)
+    for s in range(w.batch):
+        src = {a: source_cpu(w, a, s) for a in w.anchors()}
+        for l in range(3):
+            if lens[s] == 0:
+                assert torch.all(dec.layer_out(l)[s] == 0)
+            else:
+                check_layer_seq(w, dec, caches, ql, qr, l, s, lens[s], src)
+
+
+def test_deterministic_and_split_invariant(kk):
+    w = synth.small_workload(12, len(MIXED_SMALL), 40, 2, 700, 256, 32, MIXED_SMALL)
+    model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+    caches = build_caches(kk, model, w)
+    ql, qr = synth.queries(w, "cuda")
+    sl = torch.full((w.batch,), 700, dtype=torch.int32, device="cuda")
+    outs = []
+    for st in (0, 0, 96, 32):
+        dec = kk.Decoder(model, caches, w.batch, 700, 700, split_tokens=st)
+        dec(ql, qr, sl)
+        outs.append(dec.out.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    # different split choices round P' differently (per-split maxima and scale
+    # exponents); each is within the bar of the oracle, so they agree within it
+    for o in outs[2:]:
+        rel = (o - outs[0]).abs().max() / outs[0].abs().max()
+        assert rel < TOL
+
+
+def test_inheritor_equals_one_layer_call_on_anchor_cache(kk):
+    w = synth.small_workload(13, len(MIXED_SMALL), 40, 2, 300, 256, 32, MIXED_SMALL)
+    model, caches, dec, ql, qr = run_gpu(kk, w, split_tokens=64)
+    sl = torch.full((w.batch,), 300, dtype=torch.int32, device="cuda")
+    for l in (1, 4, 5, 9):
+        a = w.layers[l].anchor
+        spec = w.layers[a]
+        one = kk.Model([kk.LayerSpec(0, spec.d, spec.bits, w.layers[l].sm_scale)], w.n_heads, w.r, w.d_rope)
+        d1 = kk.Decoder(one, {0: caches[a]}, w.batch, 300, 300, split_tokens=64)
+        d1(ql[l:l + 1].contiguous(), qr[l:l + 1].contiguous(), sl)
+        torch.cuda.synchronize()
+        assert torch.equal(d1.layer_out(0), dec.layer_out(l)), f"inheritor {l}"
+
+
+def test_outliers_and_zero_tokens(kk):
+    table = [[0, 128, 2], [1, 128, 4], [2, 128, 8], [3, 128, 16]]
+    w = synth.small_workload(14, 4, 16, 1, 200, 128, 32, table)
+    model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+    caches = {}
+    src = {}
+    g = torch.Generator(device="cuda")
+    g.manual_seed(99)
+    for a in w.anchors():
+        lat = torch.randn(200, 128, generator=g, device="cuda")
+        rope = torch.randn(200, 32, generator=g, device="cuda")
+        mask = torch.rand(200, 128, generator=g, device="cuda") < 1e-3
+        lat = torch.where(mask, lat * 20, lat)
+        lat[5] = 0
+        rope[5] = 0                                    # an all-zero token: scale 0, codes 0
+        lat[7] *= 1e-20                                # a tiny-magnitude token
+        codes, scales = kk.alloc_cache(model, a, 1, 200)
+        kk.quantize_write(model, a, lat, rope, codes, scales, torch.arange(200, device="cuda"))
+        caches[a] = (codes, scales)
+        src[a] = (lat.cpu().numpy(), rope.cpu().numpy())
+    ql, qr = synth.queries(w, "cuda")
+    ql[2, 0, 3] = 0
+    qr[2, 0, 3] = 0                                    # a head with q = 0: uniform weights
+    dec = kk.Decoder(model, caches, 1, 200, 200)
+    dec(ql, qr, torch.tensor([200], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    for l in range(4):
+        check_layer_seq(w, dec, caches, ql, qr, l, 0, 200, src)
+
+
+def test_b16_full_rank_matches_unquantized_attention(kk):
+    table = [[0, 256, 16]]
+    w = synth.small_workload(15, 1, 28, 2, 2048, 256, 64, table)
+    model, caches, dec, ql, qr = run_gpu(kk, w)
+    for s in range(2):
+        lat, rope = source_cpu(w, 0, s)
+        src = np.concatenate([lat, rope], 1).astype(np.float64)
+        q = np.concatenate([ql[0, s].float().cpu().numpy(), qr[0, s].float().cpu().numpy()], 1).astype(np.float64)
+        ref = ko.attend(q, src, 256, w.layers[0].sm_scale)
+        got = dec.layer_out(0)[s].cpu().numpy()
+        assert np.max(np.abs(got - ref)) <= TOL * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("wid,samples", [(1, [(0, 0), (27, 31), (13, 7)]),
+                                         (2, [(0, 0), (27, 31), (11, 5)]),
+                                         (3, None),
+                                         (4, None)])
+def test_full_size_workloads_sampled(kk, wid, samples):
+    w = synth.workload(wid)
+    model, caches, dec, ql, qr = run_gpu(kk, w)
+    if samples is None:
+        # one layer of every bit width, an inheritor of the largest group, first and last sequence
+        picks = []
+        for b in (2, 4, 8, 16):
+            l = next(l for l in range(w.n_layers) if w.bits_eff(l) == b)
+            picks.append(l)
+        grp = max(w.anchors(), key=lambda a: sum(1 for s in w.layers if s.anchor == a))
+        picks.append(max(l for l in range(w.n_layers) if w.layers[l].anchor == grp))
+        samples = [(l, s) for i, l in enumerate(picks) for s in ((0, w.batch - 1) if i % 2 == 0 else (w.batch // 2,))]
+    worst = 0.0
+    for (l, s) in samples:
+        worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, w.seq_len))
+    print(f"workload {wid}: worst err ratio {worst:.2e} over {len(samples)} (layer, seq) samples")
