@@ -1,0 +1,203 @@
+"""Benchmark one decode step of compressed MLA attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload 3]
+
+A step is one kk_decode_attn call over every layer of the workload (by
+default the Qwen2.5-14B-shaped mixed 4x table: 48 layers, 40 heads, r = 512,
+d_R = 64, batch 32, 8192 cached tokens per sequence) with the caches, queries
+and sequence lengths already resident in HBM.  Prints one JSON line.
+
+roofline.achieved = algorithmic bytes of one step / mean device time of one
+step (HIP events on the launch stream).  Algorithmic bytes U = anchor caches
+once (rows + scales) + the d_eff + d_R query values read per layer + the fp32
+outputs written.
+"""
+
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+
+
+def algorithmic_bytes(kk, w, model):
+    """U = sum_anchors B*T*(row_stride + 4) + sum_l B*H*(d_eff + d_R)*sizeof(q) + sum_l B*H*d_eff*4."""
+    qsize = 4 if str(w.q_dtype) == "torch.float32" else 2
+    cache = sum(w.batch * w.seq_len * (kk.row_stride_bytes(w.layers[a].d, w.d_rope, w.layers[a].bits) + 4)
+                for a in w.anchors())
+    q = sum(w.batch * w.n_heads * (w.d_eff(l) + w.d_rope) * qsize for l in range(w.n_layers))
+    out = sum(w.batch * w.n_heads * w.d_eff(l) * 4 for l in range(w.n_layers))
+    return cache + q + out, cache
+
+
+def useful_flops(w):
+    """Q.K and P.V multiply-adds per step: B*T*(2H(d+d_R) + 2Hd) per layer."""
+    return sum(w.batch * w.seq_len * (2 * w.n_heads * (w.d_eff(l) + w.d_rope) + 2 * w.n_heads * w.d_eff(l))
+               for l in range(w.n_layers))
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "compressed_decode_attention_kk_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload_name):
+    """HBM bytes per step from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload_name}_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_step")
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle (unchanged) on the host cores: decode of whole (layer, sequence)
+    pairs of the same workload until the time budget is used."""
+    import numpy as np
+    import torch
+    from oracle import kk_oracle as ko
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:                                    # pragma: no cover
+        cores = os.cpu_count() or 1
+    ql, qr = synth.queries(w, "cuda")
+    done, spent = 0, 0.0
+    pairs = [(l, s) for s in range(w.batch) for l in range(w.n_layers)]
+    cache = {}
+    for (l, s) in pairs:
+        a = w.layers[l].anchor
+        if (a, s) not in cache:
+            cache.clear()
+            lat, rope, _ = synth.source_rows(w, a, "cuda", seqs=[s])
+            packed, scales, _ = ko.write_cache(lat[0].cpu().numpy(), rope[0].cpu().numpy(), w.d_eff(l), w.bits_eff(l))
+            cache[(a, s)] = (packed, scales)
+            del lat, rope
+        packed, scales = cache[(a, s)]
+        q_lat = ql[l, s].float().cpu().numpy().astype(np.float64)
+        q_rope = qr[l, s].float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        ko.decode_layer(q_lat, q_rope, packed, scales, w.d_eff(l), w.d_rope, w.bits_eff(l), w.layers[l].sm_scale,
+                        w.seq_len)
+        spent += time.perf_counter() - t0
+        done += 1
+        if spent >= budget_s:
+            break
+    return {"value": done / spent, "unit": "layer*tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{done} (layer, sequence) decodes of the same workload (unpack, dequantize, fp64 attention "
+                      f"over {w.seq_len} tokens, {w.n_heads} heads), {spent:.1f} s of CPU time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (the decode path has no multi-GPU mode); got --gpus {args.gpus}",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import compressed_decode_attention_kk_amd as kk
+    import synth
+    from synth.device import build_caches
+
+    kk.lib()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = synth.workload(args.workload)
+    model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+    t_setup = time.perf_counter()
+    caches = build_caches(kk, model, w)
+    ql, qr = synth.queries(w, "cuda")
+    seq_lens = torch.full((w.batch,), w.seq_len, dtype=torch.int32, device="cuda")
+    dec = kk.Decoder(model, caches, w.batch, w.seq_len, w.seq_len, split_tokens=args.split_tokens)
+    torch.cuda.synchronize()
+    print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        dec(ql, qr, seq_lens)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        dec(ql, qr, seq_lens)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    dev_ms = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    mean_dev_ms = sum(dev_ms) / len(dev_ms)
+    ms_per_step = wall * 1000.0 / args.steps
+
+    U, cache_bytes = algorithmic_bytes(kk, w, model)
+    flops = useful_flops(w)
+    achieved = U / (mean_dev_ms * 1e-3) / 1e9
+    traffic = stored_traffic(w.name)
+    print(f"[bench] device ms/step mean {mean_dev_ms:.4f} p10 {dev_ms[len(dev_ms) // 10]:.4f} "
+          f"p90 {dev_ms[(9 * len(dev_ms)) // 10]:.4f}; wall ms/step {ms_per_step:.4f}; U {U / 1e9:.3f} GB; "
+          f"{achieved:.0f} GB/s; MFMA-useful {flops / (mean_dev_ms * 1e-3) / 1e12:.1f} TFLOP/s",
+          file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_budget)
+
+    anchors = w.anchors()
+    bits_tok = sum((w.layers[a].d + w.d_rope) * w.layers[a].bits + 32 for a in anchors)
+    line = {
+        "metric": "compressed decode-attn layer*tokens/s",
+        "value": w.n_layers * w.batch / (ms_per_step * 1e-3),
+        "unit": "layer*tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.n_layers, "heads": w.n_heads, "batch": w.batch,
+                   "cached_tokens": w.seq_len, "r": w.r, "d_rope": w.d_rope, "anchors": len(anchors),
+                   "bits_per_token": bits_tok, "q_dtype": str(w.q_dtype).replace("torch.", ""),
+                   "split_tokens": args.split_tokens or "auto", "parallelism": "none (one GPU)"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_step": U, "device_ms_per_step": mean_dev_ms,
+                     "useful_tflops": flops / (mean_dev_ms * 1e-3) / 1e12},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,28 +9,25 @@
 // Decode reads the whole cache for every token ("Background: The KV Cache
 // Bottleneck"), so the kernel is built around streaming the packed codes once.
 //
-// Work item = (anchor-group chunk of <= 64 query rows, sequence, token split).
-// A workgroup of 4 waves processes one item in 32-token tiles:
+// Work item = (chunk of <= 16*RB query rows of one anchor group, sequence,
+// token split).  A workgroup of 4 waves processes one item in 32-token tiles:
 //   1. the tile's packed rows and scales are copied HBM -> LDS with direct
-//      loads (global_load_lds_dwordx4), double-buffered one tile ahead;
-//   2. Q.K: the 32-wide contraction chunks are split over the 4 waves; each
-//      wave dequantizes its chunks of the codes to exact fp16 integers
-//      (magic-number conversion) and runs v_mfma_f32_16x16x32_f16 against its
-//      q fragments held in registers; partial scores go through LDS;
-//   3. online softmax: the wave owning a 16-row block sums the partials,
-//      applies sm_scale * per-token scale, keeps a lazily moved running max
-//      (log2 domain), and writes P' = exp2(z - m) * scale_t * 2^-E as fp16;
-//   4. P.V: the output features are split over the waves in 32-wide units;
-//      codes are read transposed with ds_read_b64_tr_b{4,8,16}, dequantized
-//      and multiplied by P' with MFMA into fp32 accumulators.
-// Inheriting layers of a group add query rows to the same item, so one read
-// of the anchor cache serves the whole group.  Items that were split write
-// (m, l, O) partials; a second small kernel merges them in a fixed order.
-//
-// Exactness: codes are exact fp16 integers (|c| <= 127; b = 16 codes are split
-// as hi*256 + lo with both halves exact), bf16 queries are exact in fp16 after
-// a power-of-two row prescale, products are exact in the fp32 accumulators.
-// The only rounding besides fp32 accumulation is P' to fp16 (2^-11 relative).
+//      loads (global_load_lds), double-buffered one tile ahead;
+//   2. Q.K on the integer MFMA: wave w < RB owns query rows 16w..16w+15.  The
+//      codes are used as int8 operands directly (b = 8), after a shift/mask
+//      nibble or 2-bit expansion (b = 4, 2; offset-binary with an exact bias
+//      correction), or as a signed high byte and biased low byte (b = 16).
+//      The query is a per-row fixed-point number (power-of-two prescale,
+//      14 bits) held as two int8 limbs, so scores accumulate exactly in int32;
+//   3. online softmax in the same wave (no exchange): per-token scale and
+//      sm_scale applied in fp32, running max in the log2 domain moved lazily,
+//      P' = exp2(z - m) * scale_t * 2^-E written to LDS as fp16, with E a
+//      lazily raised power-of-two bound of the scales seen;
+//   4. P.V on the fp16 MFMA, output features split over the 4 waves in
+//      32-wide units; codes are read transposed with ds_read_b64_tr_b{4,8,16}
+//      and converted to exact fp16 integers (magic-number conversion).
+// Inheriting layers of a group are extra query rows of the same items.  Items
+// that were split write (m, l, O) partials; a small kernel merges them.
 #include <hip/hip_runtime.h>
 
 #include "kk_internal.h"
@@ -41,6 +38,7 @@ namespace {
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef int i4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef int i2 __attribute__((ext_vector_type(2)));
@@ -54,27 +52,27 @@ typedef __attribute__((address_space(4))) const DecodeArgs KArgs;
 typedef __attribute__((address_space(4))) const EntryArg KEntry;
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kQFrac = 13;           // query fixed point: |q'| < 1 -> |q'| * 2^13 <= 8192
+constexpr int kScaleHeadroom = 6;    // scales may exceed 2^E by 2^6 before E is raised
+constexpr int kMaxChunks64 = (kMaxK + 63) / 64;
 
 // ---- LDS map (bytes, dynamic shared memory) ----------------------------------
-//  [0, 2*buf)            two tile buffers: codes of token block 0 | block 1 | scales | slack
-//  sbuf                  Q.K partials   [wave][row block][token block][64 lanes] f4
-//  pbuf                  P' fragments   [row block][64 lanes] h8
-//  alpha / flags / rowmax / final (m, l)
-constexpr int kSbufBytes = kWaves * kMaxRowBlocks * 2 * 64 * 16;
+//  [0, 2*buf)   two tile buffers: codes of token block 0 | block 1 | slack | 128 B scales
+//  pbuf         P' fragments [row block][64 lanes] h8
+//  alpha[64] flags[4] ml[64][2] misc[16]
 constexpr int kPbufBytes = kMaxRowBlocks * 64 * 16;
-constexpr int kMiscBytes = 64 * 4 /*alpha*/ + 16 /*flags*/ + kWaves * 64 * 4 /*rowmax*/ +
-                           64 * 8 /*m,l*/ + 64 /*reduce*/;
+constexpr int kMiscBytes = 64 * 4 + 16 + 64 * 8 + 64;
 
 __host__ __device__ inline int nseg_of(int row_stride) { return row_stride >> 4; }
-__host__ __device__ inline int chunks_of(int K) { return (K + 31) >> 5; }
-__host__ __device__ inline int nsegpad_of(int K, int bits) { return (chunks_of(K) * bits + 3) >> 2; }
-// one tile buffer: two token blocks of nseg segments, over-read slack, then 128 B of scales
+__host__ __device__ inline int chunks64_of(int K) { return (K + 63) >> 6; }
+// 16-byte segments read by the Q.K chunks (whole 64-feature chunks)
+__host__ __device__ inline int nsegpad_of(int K, int bits) { return (chunks64_of(K) * bits + 1) >> 1; }
 __host__ __device__ inline int tilebuf_bytes(int row_stride, int K, int bits) {
-  int nseg = nseg_of(row_stride), pad = nsegpad_of(K, bits);
+  const int nseg = nseg_of(row_stride), pad = nsegpad_of(K, bits);
   return (nseg + (pad > nseg ? pad : nseg)) * 256 + 256;
 }
 
-// ---- dequantization to exact fp16 integers ------------------------------------
+// ---- operand conversions ------------------------------------------------------
 __device__ inline h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
 __device__ inline uint32_t perm(uint32_t a, uint32_t b, uint32_t sel) { return __builtin_amdgcn_perm(a, b, sel); }
 
@@ -85,15 +83,14 @@ __device__ inline h8 pack8(h2 a, h2 b, h2 c, h2 d) {
   return r;
 }
 
+// fp16 exact integers for the P.V operand.  fp16 0x64XX = 1024 + XX.
 // 8 signed bytes (x0: elements 0..3, x1: 4..7) -> fp16 in element order.
-// fp16 0x64XX = 1024 + XX; the byte is offset by 128 first (xor of its sign bit).
 __device__ inline h8 cvt_b8(uint32_t x0, uint32_t x1) {
   const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
   x0 ^= 0x80808080u; x1 ^= 0x80808080u;
   return pack8(as_h2(perm(0x64646464u, x0, 0x04010400u)) + bias, as_h2(perm(0x64646464u, x0, 0x04030402u)) + bias,
                as_h2(perm(0x64646464u, x1, 0x04010400u)) + bias, as_h2(perm(0x64646464u, x1, 0x04030402u)) + bias);
 }
-
 // 8 signed nibbles of x (element k at bits 4k) -> fp16 in order (0,4,1,5,2,6,3,7).
 __device__ inline h8 cvt_b4(uint32_t x) {
   const h2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
@@ -101,45 +98,65 @@ __device__ inline h8 cvt_b4(uint32_t x) {
   return pack8(as_h2((x & 0x000F000Fu) | 0x64006400u) + bias, as_h2(((x >> 4) & 0x000F000Fu) | 0x64006400u) + bias,
                as_h2(((x >> 8) & 0x000F000Fu) | 0x64006400u) + bias, as_h2(((x >> 12) & 0x000F000Fu) | 0x64006400u) + bias);
 }
-
-// 8 signed 2-bit fields of the low 16 bits of x (element k at bits 2k) -> fp16
-// in order (0,4,1,5,2,6,3,7).
-__device__ inline h8 cvt_b2(uint32_t x) {
-  const h2 bias = {(_Float16)-1026.0f, (_Float16)-1026.0f};
-  uint32_t y = (x ^ 0xAAAAu) & 0xFFFFu;
-  y |= (y >> 8) << 16;
-  return pack8(as_h2((y & 0x00030003u) | 0x64006400u) + bias, as_h2(((y >> 2) & 0x00030003u) | 0x64006400u) + bias,
-               as_h2(((y >> 4) & 0x00030003u) | 0x64006400u) + bias, as_h2(((y >> 6) & 0x00030003u) | 0x64006400u) + bias);
-}
-
 // 2-bit fields of nibble-packed data from a 4-bit transpose read: element e at
 // bits 4e (even field) or 4e + 2 (odd field); result order (0,4,1,5,2,6,3,7).
 __device__ inline h8 cvt_b2_nib(uint32_t x, int odd) {
   const h2 bias = {(_Float16)-1026.0f, (_Float16)-1026.0f};
-  uint32_t y = (x ^ 0xAAAAAAAAu) >> (odd ? 2 : 0);
+  const uint32_t y = (x ^ 0xAAAAAAAAu) >> (odd ? 2 : 0);
   return pack8(as_h2((y & 0x00030003u) | 0x64006400u) + bias, as_h2(((y >> 4) & 0x00030003u) | 0x64006400u) + bias,
                as_h2(((y >> 8) & 0x00030003u) | 0x64006400u) + bias, as_h2(((y >> 12) & 0x00030003u) | 0x64006400u) + bias);
 }
-
 // 8 int16 codes (w0..w3 little-endian) -> hi (signed high byte) and lo/256
 // (unsigned low byte scaled by 2^-8, exact: fp16 0x44XX = 4 + XX/256).
 __device__ inline void cvt_b16(u4 w, h8& hi, h8& lo) {
   const h2 bh = {(_Float16)-1152.0f, (_Float16)-1152.0f};
   const h2 bl = {(_Float16)-4.0f, (_Float16)-4.0f};
-  u4 x = w ^ 0x80008000u;
+  const u4 x = w ^ 0x80008000u;
   hi = pack8(as_h2(perm(0x64646464u, x[0], 0x04030401u)) + bh, as_h2(perm(0x64646464u, x[1], 0x04030401u)) + bh,
              as_h2(perm(0x64646464u, x[2], 0x04030401u)) + bh, as_h2(perm(0x64646464u, x[3], 0x04030401u)) + bh);
   lo = pack8(as_h2(perm(0x44444444u, w[0], 0x04020400u)) + bl, as_h2(perm(0x44444444u, w[1], 0x04020400u)) + bl,
              as_h2(perm(0x44444444u, w[2], 0x04020400u)) + bl, as_h2(perm(0x44444444u, w[3], 0x04020400u)) + bl);
 }
 
-__device__ inline f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+// int8 operands for the Q.K MFMA (16 features per lane).
+// b = 4: 16 nibbles (x0: 0..7, x1: 8..15) -> offset-binary bytes (code + 8),
+//        slot order 0,2,4,6 | 1,3,5,7 | 8,10,12,14 | 9,11,13,15.
+__device__ inline i4 qk_b4(uint32_t x0, uint32_t x1) {
+  x0 ^= 0x88888888u; x1 ^= 0x88888888u;
+  return i4{(int)(x0 & 0x0F0F0F0Fu), (int)((x0 >> 4) & 0x0F0F0F0Fu), (int)(x1 & 0x0F0F0F0Fu), (int)((x1 >> 4) & 0x0F0F0F0Fu)};
+}
+// b = 2: 16 fields of x -> offset-binary bytes (code + 2); slot 4j + k holds field 4k + j.
+__device__ inline i4 qk_b2(uint32_t x) {
+  x ^= 0xAAAAAAAAu;
+  return i4{(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u), (int)((x >> 6) & 0x03030303u)};
+}
+// b = 16: 16 int16 (w0..w7) -> signed high bytes and low bytes minus 128.
+__device__ inline void qk_b16(u4 a, u4 b, i4& hi, i4& lo) {
+  hi = i4{(int)perm(a[1], a[0], 0x07050301u), (int)perm(a[3], a[2], 0x07050301u),
+          (int)perm(b[1], b[0], 0x07050301u), (int)perm(b[3], b[2], 0x07050301u)};
+  lo = i4{(int)(perm(a[1], a[0], 0x06040200u) ^ 0x80808080u), (int)(perm(a[3], a[2], 0x06040200u) ^ 0x80808080u),
+          (int)(perm(b[1], b[0], 0x06040200u) ^ 0x80808080u), (int)(perm(b[3], b[2], 0x06040200u) ^ 0x80808080u)};
+}
+// feature (within a lane's 16) held by operand slot i
+template <int BITS>
+__device__ constexpr int qk_slot_feature(int i) {
+  return BITS == 4 ? ((i >> 3) << 3) + ((i & 3) << 1) + ((i >> 2) & 1)
+       : BITS == 2 ? ((i & 3) << 2) + (i >> 2)
+       : i;
+}
 
-__device__ inline float wave_max_xor_16_32(float v) {
+__device__ inline f4 mfma_f16(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+__device__ inline i4 mfma_i8(i4 a, i4 b, i4 c) { return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0); }
+
+__device__ inline float max_xor_16_32(float v) {
   v = fmaxf(v, __shfl_xor(v, 16));
   return fmaxf(v, __shfl_xor(v, 32));
 }
-__device__ inline float wave_sum_xor_16_32(float v) {
+__device__ inline float sum_xor_16_32(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+__device__ inline int isum_xor_16_32(int v) {
   v += __shfl_xor(v, 16);
   return v + __shfl_xor(v, 32);
 }
@@ -149,26 +166,34 @@ __device__ inline float wave_sum_xor_16_32(float v) {
 // P.V reads of tokens {4g..4g+3} of both blocks land in different LDS banks.
 __device__ inline int tile_off(int pitch, int tb, int seg, int t) { return tb * pitch + seg * 256 + ((t ^ (tb << 2)) << 4); }
 
-// ---- per-item decode, specialised on the bit width ------------------------------
-template <int BITS>
+// ---- per-item decode ----------------------------------------------------------
+// BITS: the anchor's bit width; RB: 16-row MFMA blocks per item (uniform for a
+// launch, it follows from the head count).
+template <int BITS, int RB>
 __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char* lds) {
+  constexpr int NUW = kMaxUnitsPerWave;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, n = lane & 15;
-  const int d = E.d, K = d + A.d_rope, KC = chunks_of(K);
+  const int d = E.d, K = d + A.d_rope, KC = chunks64_of(K);
   const int NSEG = nseg_of(E.row_stride), PITCH = NSEG * 256;
   const int bufbytes = tilebuf_bytes(E.row_stride, K, BITS);
-  char* sbuf = lds + 2 * bufbytes;
-  char* pbuf = sbuf + kSbufBytes;
+  char* pbuf = lds + 2 * bufbytes;
   float* alpha_lds = (float*)(pbuf + kPbufBytes);
   int* flag_lds = (int*)(alpha_lds + 64);
-  float* rowmax_lds = (float*)(flag_lds + 4);
-  float* ml_lds = rowmax_lds + kWaves * 64;
-  float* red_lds = ml_lds + 128;
+  float* ml_lds = (float*)(flag_lds + 4);
+  int* misc_lds = (int*)(ml_lds + 128);
 
-  // rows of this chunk
+  // rows of this chunk (at most 16 * RB); wave < RB owns rows 16*wave + n
   const int r0 = E.row_begin + chunk * E.chunk_rows;
   const int nrows = min(E.chunk_rows, E.row_end - r0);
-  const int RB = (nrows + 15) >> 4;
+  const bool qk_wave = wave < RB;
+  const int my_row = 16 * wave + n;
+  int my_layer = -1, my_head = 0;
+  if (qk_wave && my_row < nrows) {
+    const int gr = r0 + my_row;
+    my_layer = A.group_layers[E.lay_begin + gr / A.heads];
+    my_head = gr % A.heads;
+  }
 
   // token range of this split
   int len = A.seq_lens[s];
@@ -180,107 +205,20 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
   const int ntiles = (ntok + kTile - 1) / kTile;
   const int64_t row0 = (int64_t)s * A.t_cap + t0;    // first cache row of this item
 
-  // ---- scale exponent E: s_t * 2^-E <= 1 for every token of the item -------------
-  float smax = 0.0f;
-  for (int t = tid; t < ntok; t += kThreads) smax = fmaxf(smax, E.scales[row0 + t]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) smax = fmaxf(smax, __shfl_xor(smax, o));
-  if (lane == 0) red_lds[wave] = smax;
-
-  // ---- q fragments (registers), with a power-of-two prescale per row ---------------
-  // fragment (ci, rb): chunk c = wave + 4*ci, lane (g, n): row 16*rb + n, features
-  // 32c + 8g + slot order (identity for b >= 8, (0,4,1,5,2,6,3,7) for b <= 4).
-  float qv[kMaxChunksPerWave][kMaxRowBlocks][8];
-  float rmax[kMaxRowBlocks];
-  int row_layer[kMaxRowBlocks], row_head[kMaxRowBlocks];
-#pragma unroll
-  for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
-    rmax[rb] = 0.0f;
-    const int rl = 16 * rb + n;
-    row_layer[rb] = -1;
-    row_head[rb] = 0;
-    if (rl < nrows) {
-      const int gr = r0 + rl;
-      row_layer[rb] = A.group_layers[E.lay_begin + gr / A.heads];
-      row_head[rb] = gr % A.heads;
-    }
-  }
-#pragma unroll
-  for (int ci = 0; ci < kMaxChunksPerWave; ++ci) {
-    const int c = wave + kWaves * ci;
-    const int f0 = 32 * c + 8 * g;
-#pragma unroll
-    for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
-      float x[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = 0.0f;
-      if (c < KC && row_layer[rb] >= 0 && f0 < K) {
-        const int64_t qrow = ((int64_t)row_layer[rb] * A.batch + s) * A.heads + row_head[rb];
-        const bool lat = f0 < d;
-        const int64_t off = lat ? qrow * A.r + f0 : qrow * A.d_rope + (f0 - d);
-        const void* base = lat ? A.q_lat : A.q_rope;
-        if (A.q_is_f32) {
-          const f4* p = (const f4*)((const float*)base + off);
-          f4 a = p[0], b = p[1];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
-        } else {
-          u4 w = *(const u4*)((const uint16_t*)base + off);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[2 * i] = __uint_as_float(w[i] << 16);
-            x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int src = BITS <= 4 ? ((i & 1) ? 4 + (i >> 1) : (i >> 1)) : i;
-        qv[ci][rb][i] = x[src];
-        rmax[rb] = fmaxf(rmax[rb], fabsf(x[i]));
-      }
-    }
-  }
-#pragma unroll
-  for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
-    rmax[rb] = wave_max_xor_16_32(rmax[rb]);
-    if (g == 0) rowmax_lds[wave * 64 + 16 * rb + n] = rmax[rb];
-  }
-  __syncthreads();
-  float item_smax = fmaxf(fmaxf(red_lds[0], red_lds[1]), fmaxf(red_lds[2], red_lds[3]));
-  int Eexp = 0;
-  if (item_smax > 0.0f) (void)frexpf(item_smax, &Eexp);     // item_smax * 2^-Eexp in [0.5, 1)
-  h8 qf[kMaxChunksPerWave][kMaxRowBlocks];
-  float rowf[kMaxRowBlocks];                                  // used by the softmax wave
-  constexpr float kBitScale = BITS == 16 ? 256.0f : 1.0f;
-#pragma unroll
-  for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
-    float m = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) m = fmaxf(m, rowmax_lds[w * 64 + 16 * rb + n]);
-    int e = 0;
-    if (m > 0.0f) (void)frexpf(m, &e);
-    const float pre = ldexpf(1.0f, -e);
-#pragma unroll
-    for (int ci = 0; ci < kMaxChunksPerWave; ++ci)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qf[ci][rb][i] = (_Float16)(qv[ci][rb][i] * pre);
-    rowf[rb] = row_layer[rb] >= 0 ? A.layers[row_layer[rb]].sm_scale * kLog2e * ldexpf(kBitScale, e) : 0.0f;
-  }
-
   // ---- tile loader: direct HBM -> LDS copies ---------------------------------------
   const uint8_t* codes = E.codes;
   const float* scales = E.scales;
+  const int block_pieces = NSEG * 16;
   auto issue_tile = [&](int it) {
     char* buf = lds + (it & 1) * bufbytes;
     const int tok0 = it * kTile;
     const int tvalid = min(kTile, ntok - tok0);
-    const int npos = 32 * NSEG;                  // 16-byte pieces of codes in the tile
+    const int npos = 2 * block_pieces;           // 16-byte pieces of codes in the tile
     const int ninst = (npos + 63) >> 6;
     for (int i = wave; i < ninst; i += kWaves) {
       const int p = i * 64 + lane;
-      const int tb = p / (NSEG * 16);
-      const int rem = p - tb * NSEG * 16;
+      const int tb = p >= block_pieces ? 1 : 0;
+      const int rem = p - tb * block_pieces;
       const int seg = rem >> 4, slot = rem & 15;
       const int t = 16 * tb + (slot ^ (tb << 2));
       if (p < npos && t < tvalid) {
@@ -288,25 +226,95 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
         __builtin_amdgcn_global_load_lds(gp, LDS_PTR(void, buf + i * 1024), 16, 0, 0);
       }
     }
-    if (wave == kWaves - 1 && lane < kTile && lane < tvalid) {
+    if (wave == kWaves - 1 && lane < tvalid) {
       __builtin_amdgcn_global_load_lds(scales + row0 + tok0 + lane, LDS_PTR(void, buf + 2 * PITCH), 4, 0, 0);
     }
   };
+  if (ntiles > 0) issue_tile(0);
 
-  // ---- accumulators -------------------------------------------------------------
-  f4 oacc[kMaxUnitsPerWave][2][kMaxRowBlocks];
+  // ---- q as two int8 limbs of a 14-bit fixed-point number per row ------------------
+  // chunk c, lane (g, n): row 16*wave + n, features 64c + 16g + qk_slot_feature(i).
+  i4 qh[kMaxChunks64], ql[kMaxChunks64];
+  int qsum = 0;                                 // sum of the fixed-point q of this row
+  float rowf = 0.0f;
+  {
+    float qv[kMaxChunks64][16];
+    float mx = 0.0f;
 #pragma unroll
-  for (int u = 0; u < kMaxUnitsPerWave; ++u)
+    for (int c = 0; c < kMaxChunks64; ++c) {
+      const int f0 = 64 * c + 16 * g;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) qv[c][i] = 0.0f;
+      if (my_layer >= 0 && f0 < K) {
+        const int64_t qrow = ((int64_t)my_layer * A.batch + s) * A.heads + my_head;
+        const bool lat = f0 < d;
+        const int64_t off = lat ? qrow * A.r + f0 : qrow * A.d_rope + (f0 - d);
+        const void* base = lat ? A.q_lat : A.q_rope;
+        float x[16];
+        if (A.q_is_f32) {
+          const f4* p = (const f4*)((const float*)base + off);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const f4 a = p[v];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[4 * v + i] = a[i];
+          }
+        } else {
+          const u4* p = (const u4*)((const uint16_t*)base + off);
+#pragma unroll
+          for (int v = 0; v < 2; ++v) {
+            const u4 w = p[v];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[8 * v + 2 * i] = __uint_as_float(w[i] << 16);
+              x[8 * v + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          qv[c][i] = x[qk_slot_feature<BITS>(i)];
+          mx = fmaxf(mx, fabsf(x[i]));
+        }
+      }
+    }
+    mx = max_xor_16_32(mx);
+    int e = 0;
+    if (mx > 0.0f) (void)frexpf(mx, &e);          // mx * 2^-e in [0.5, 1)
+    const float pre = ldexpf(1.0f, kQFrac - e);
+#pragma unroll
+    for (int c = 0; c < kMaxChunks64; ++c) {
+      uint32_t hw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qi = (int)rintf(qv[c][i] * pre);    // |qi| <= 8192
+        const int hi = (qi + 64) >> 7;                // floor division, in [-64, 64]
+        const int lo = qi - (hi << 7);                // in [-64, 63]
+        qsum += qi;
+        hw[i >> 2] |= ((uint32_t)hi & 0xFFu) << (8 * (i & 3));
+        lw[i >> 2] |= ((uint32_t)lo & 0xFFu) << (8 * (i & 3));
+      }
+      qh[c] = i4{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3]};
+      ql[c] = i4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
+    }
+    qsum = isum_xor_16_32(qsum);
+    if (my_layer >= 0) rowf = A.layers[my_layer].sm_scale * kLog2e * ldexpf(1.0f, e - kQFrac);
+  }
+  // offset-binary bias of the Q.K operand (exact integer correction)
+  const int qbias = BITS == 4 ? 8 * qsum : BITS == 2 ? 2 * qsum : BITS == 16 ? 128 * qsum : 0;
+
+  // ---- accumulators and softmax state -----------------------------------------------
+  f4 oacc[NUW][2][RB];
+#pragma unroll
+  for (int u = 0; u < NUW; ++u)
 #pragma unroll
     for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int rb = 0; rb < kMaxRowBlocks; ++rb) oacc[u][f][rb] = f4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_lane = 0.0f;     // softmax state of row 16*wave + n (wave < RB)
-  const float sprime = ldexpf(1.0f, -Eexp);
+      for (int rb = 0; rb < RB; ++rb) oacc[u][f][rb] = f4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_lane = 0.0f;     // softmax state of row 16*wave + n
+  int Ecur = -1000;                            // scales of the item so far are <= 2^(Ecur + headroom)
   const int NU = (d + 31) >> 5;               // 32-feature output units
-  const int nqk = min(kWaves, KC);             // waves holding Q.K chunks
 
-  if (ntiles > 0) issue_tile(0);
   for (int it = 0; it < ntiles; ++it) {
     __builtin_amdgcn_s_waitcnt(0x3f70);        // vmcnt(0): this tile's copies have landed
     __syncthreads();                            // (A) tile visible; previous P.V finished
@@ -315,122 +323,125 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
     const float* sc = (const float*)(buf + 2 * PITCH);
     const int tvalid = min(kTile, ntok - it * kTile);
 
-    // ---- Q.K partial over this wave's chunks ----
-    f4 sacc[kMaxRowBlocks][2];
+    if (qk_wave) {
+      // ---- Q.K for this wave's 16 rows, all features, both token blocks ----
+      constexpr int NACC = BITS == 16 ? 4 : 2;   // code x q_hi, code x q_lo (b = 16: high and low byte each)
+      i4 acc[2][NACC];
 #pragma unroll
-    for (int rb = 0; rb < kMaxRowBlocks; ++rb) sacc[rb][0] = sacc[rb][1] = f4{0.f, 0.f, 0.f, 0.f};
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-    for (int tb = 0; tb < 2; ++tb) {
+        for (int k = 0; k < NACC; ++k) acc[tb][k] = i4{0, 0, 0, 0};
 #pragma unroll
-      for (int ci = 0; ci < kMaxChunksPerWave; ++ci) {
-        const int c = wave + kWaves * ci;
+      for (int c = 0; c < kMaxChunks64; ++c) {
         if (c < KC) {
-        const int piece = 4 * c + g;                 // 8 fields of BITS bits = BITS bytes
-        const int byte = piece * BITS;
-        const char* p = buf + tile_off(PITCH, tb, byte >> 4, n) + (byte & 15);
-        if constexpr (BITS == 16) {
-          h8 hi, lo;
-          cvt_b16(*(const u4*)p, hi, lo);
+          const int fbyte = (64 * c + 16 * g) * BITS / 8;     // first byte of this lane's 16 features
 #pragma unroll
-          for (int rb = 0; rb < kMaxRowBlocks; ++rb)
-            if (rb < RB) {
-              sacc[rb][tb] = mfma(hi, qf[ci][rb], sacc[rb][tb]);
-              sacc[rb][tb] = mfma(lo, qf[ci][rb], sacc[rb][tb]);
+          for (int tb = 0; tb < 2; ++tb) {
+            const char* p = buf + tile_off(PITCH, tb, fbyte >> 4, n) + (fbyte & 15);
+            if constexpr (BITS == 8) {
+              const i4 a = *(const i4*)p;
+              acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
+              acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
+            } else if constexpr (BITS == 4) {
+              const u2 x = *(const u2*)p;
+              const i4 a = qk_b4(x[0], x[1]);
+              acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
+              acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
+            } else if constexpr (BITS == 2) {
+              const i4 a = qk_b2(*(const uint32_t*)p);
+              acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
+              acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
+            } else {
+              const u4 x0 = *(const u4*)p;
+              const u4 x1 = *(const u4*)(p + 256);           // next segment of the same token
+              i4 hi, lo;
+              qk_b16(x0, x1, hi, lo);
+              acc[tb][0] = mfma_i8(hi, qh[c], acc[tb][0]);
+              acc[tb][1] = mfma_i8(hi, ql[c], acc[tb][1]);
+              acc[tb][2] = mfma_i8(lo, qh[c], acc[tb][2]);
+              acc[tb][3] = mfma_i8(lo, ql[c], acc[tb][3]);
             }
-        } else {
-          h8 a;
-          if constexpr (BITS == 8) { u2 x = *(const u2*)p; a = cvt_b8(x[0], x[1]); }
-          if constexpr (BITS == 4) { a = cvt_b4(*(const uint32_t*)p); }
-          if constexpr (BITS == 2) { a = cvt_b2(*(const uint16_t*)p); }
-#pragma unroll
-          for (int rb = 0; rb < kMaxRowBlocks; ++rb)
-            if (rb < RB) sacc[rb][tb] = mfma(a, qf[ci][rb], sacc[rb][tb]);
-        }
+          }
         }
       }
-    }
-    if (wave < nqk) {
-#pragma unroll
-      for (int rb = 0; rb < kMaxRowBlocks; ++rb)
-        if (rb < RB)
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-            ((f4*)sbuf)[((wave * kMaxRowBlocks + rb) * 2 + tb) * 64 + lane] = sacc[rb][tb];
-    }
-    __syncthreads();                            // (B) partial scores visible
 
-    // ---- online softmax for row block `wave` ----
-    if (wave < RB) {
-      const int rb = wave;
-      float rf = 0.0f;
+      // ---- online softmax for these rows ----
+      f4 scv[2];
+      scv[0] = *(const f4*)(sc + 4 * g);
+      scv[1] = *(const f4*)(sc + 16 + 4 * g);
+      float z[2][4], smax = 0.0f, tmax = -INFINITY;
 #pragma unroll
-      for (int q = 0; q < kMaxRowBlocks; ++q) if (q == rb) rf = rowf[q];
-      float z[2][4];
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb) {
-        f4 acc = ((const f4*)sbuf)[((0 * kMaxRowBlocks + rb) * 2 + tb) * 64 + lane];
-        for (int w = 1; w < nqk; ++w) acc += ((const f4*)sbuf)[((w * kMaxRowBlocks + rb) * 2 + tb) * 64 + lane];
+      for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int t = 16 * tb + 4 * g + j;
-          z[tb][j] = t < tvalid ? acc[j] * rf * sc[t] : -INFINITY;
+          const bool valid = 16 * tb + 4 * g + j < tvalid;
+          float sq;
+          if constexpr (BITS == 16)
+            sq = 256.0f * (float)(128 * acc[tb][0][j] + acc[tb][1][j]) + (float)(128 * acc[tb][2][j] + acc[tb][3][j] + qbias);
+          else
+            sq = (float)(128 * acc[tb][0][j] + acc[tb][1][j] - qbias);
+          const float st = valid ? scv[tb][j] : 0.0f;
+          scv[tb][j] = st;
+          smax = fmaxf(smax, st);
+          z[tb][j] = valid ? sq * rowf * st : -INFINITY;
           tmax = fmaxf(tmax, z[tb][j]);
         }
-      }
-      tmax = wave_max_xor_16_32(tmax);
-      const bool need = tmax > m_run + kLazyRescale;
+      smax = max_xor_16_32(smax);
+      tmax = max_xor_16_32(tmax);
+      const bool raise_e = smax > ldexpf(1.0f, Ecur + kScaleHeadroom);
+      const bool move_m = tmax > m_run + kLazyRescale;
       int flag = 0;
-      if (__any(need)) {
+      if (__any(move_m) || raise_e) {
         const float mnew = fmaxf(m_run, tmax);
-        const float alpha = exp2f(m_run - mnew);
-        l_lane *= alpha;
+        int enew = Ecur;
+        if (raise_e) (void)frexpf(smax, &enew);
+        const float am = exp2f(m_run - mnew);
+        l_lane *= am;
+        const float alpha = am * ldexpf(1.0f, Ecur - enew);
         m_run = mnew;
-        if (g == 0) alpha_lds[16 * rb + n] = alpha;
+        Ecur = enew;
+        if (g == 0) alpha_lds[my_row] = alpha;
         flag = 1;
       }
-      if (lane == 0) flag_lds[rb] = flag;
+      if (lane == 0) flag_lds[wave] = flag;
+      const float sprime = ldexpf(1.0f, -Ecur);
       h8 pf;
 #pragma unroll
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int t = 16 * tb + 4 * g + j;
-          const float e = exp2f(z[tb][j] - m_run);
+          const float e = __builtin_amdgcn_exp2f(z[tb][j] - m_run);
           l_lane += e;
-          pf[4 * tb + j] = (_Float16)(t < tvalid ? e * (sc[t] * sprime) : 0.0f);
+          pf[4 * tb + j] = (_Float16)(e * (scv[tb][j] * sprime));
         }
-      ((h8*)pbuf)[rb * 64 + lane] = pf;
+      ((h8*)pbuf)[wave * 64 + lane] = pf;
     }
     __syncthreads();                            // (C) P' and rescale factors visible
 
     // ---- P.V over this wave's output units ----
-    h8 pfr[kMaxRowBlocks];
+    h8 pfr[RB];
 #pragma unroll
-    for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
-      if (rb < RB) {
-        pfr[rb] = ((const h8*)pbuf)[rb * 64 + lane];
-        if (flag_lds[rb]) {
-          const float al = alpha_lds[16 * rb + n];
+    for (int rb = 0; rb < RB; ++rb) {
+      pfr[rb] = ((const h8*)pbuf)[rb * 64 + lane];
+      if (flag_lds[rb]) {
+        const float al = alpha_lds[16 * rb + n];
 #pragma unroll
-          for (int u = 0; u < kMaxUnitsPerWave; ++u)
+        for (int u = 0; u < NUW; ++u)
 #pragma unroll
-            for (int f = 0; f < 2; ++f) oacc[u][f][rb] *= al;
-        }
+          for (int f = 0; f < 2; ++f) oacc[u][f][rb] *= al;
       }
     }
+    // transposed operand reads of all units first (units past NU re-read unit NU-1)
+    u2 rv[NUW][BITS == 16 ? 4 : BITS == 8 ? 2 : 1];
 #pragma unroll
-    for (int ui = 0; ui < kMaxUnitsPerWave; ++ui) {
-      const int u = wave + kWaves * ui;
-      if (u < NU) {
-      h8 a[2], alo[2];
+    for (int ui = 0; ui < NUW; ++ui) {
+      const int u = min(wave + kWaves * ui, NU - 1);
       if constexpr (BITS == 8) {
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           const int e = n >> 1, h = n & 1, tb = e >> 2;
           const char* p = buf + tile_off(PITCH, tb, 2 * u + f, 4 * g + (e & 3)) + 8 * h;
-          i2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i2, p));
-          a[f] = cvt_b8((uint32_t)x[0], (uint32_t)x[1]);
+          rv[ui][f] = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i2, p)));
         }
       }
       if constexpr (BITS == 4 || BITS == 2) {
@@ -438,65 +449,81 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
         const int tb = (e >> 1) & 1, t = 4 * g + 2 * (e & 1) + (e >> 2);
         const char* p = BITS == 4 ? buf + tile_off(PITCH, tb, u, t) + 8 * half
                                   : buf + tile_off(PITCH, tb, u >> 1, t) + 8 * (u & 1);
-        i2 x = __builtin_amdgcn_ds_read_tr4_b64_v2i32(LDS_PTR(i2, p));
-        if constexpr (BITS == 4) { a[0] = cvt_b4((uint32_t)x[0]); a[1] = cvt_b4((uint32_t)x[1]); }
-        else { a[0] = cvt_b2_nib((uint32_t)x[0], 0); a[1] = cvt_b2_nib((uint32_t)x[0], 1); }
+        rv[ui][0] = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr4_b64_v2i32(LDS_PTR(i2, p)));
       }
       if constexpr (BITS == 16) {
 #pragma unroll
         for (int f = 0; f < 2; ++f) {
           const int fb = 2 * u + f, e = n >> 2, q = n & 3;
           const int seg = 2 * fb + (q >> 1), off = 8 * (q & 1);
-          s4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s4, buf + tile_off(PITCH, 0, seg, 4 * g + e) + off));
-          s4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s4, buf + tile_off(PITCH, 1, seg, 4 * g + e) + off));
-          u2 y0 = __builtin_bit_cast(u2, x0), y1 = __builtin_bit_cast(u2, x1);
-          cvt_b16(u4{y0[0], y0[1], y1[0], y1[1]}, a[f], alo[f]);
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb)
+            rv[ui][2 * f + tb] = __builtin_bit_cast(
+                u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s4, buf + tile_off(PITCH, tb, seg, 4 * g + e) + off)));
         }
       }
+    }
 #pragma unroll
-      for (int f = 0; f < 2; ++f)
+    for (int ui = 0; ui < NUW; ++ui) {
+      if (wave + kWaves * ui < NU) {
+        h8 a[2], alo[2];
+        if constexpr (BITS == 8) {
+          a[0] = cvt_b8(rv[ui][0][0], rv[ui][0][1]);
+          a[1] = cvt_b8(rv[ui][1][0], rv[ui][1][1]);
+        }
+        if constexpr (BITS == 4) { a[0] = cvt_b4(rv[ui][0][0]); a[1] = cvt_b4(rv[ui][0][1]); }
+        if constexpr (BITS == 2) { a[0] = cvt_b2_nib(rv[ui][0][0], 0); a[1] = cvt_b2_nib(rv[ui][0][0], 1); }
+        if constexpr (BITS == 16) {
 #pragma unroll
-        for (int rb = 0; rb < kMaxRowBlocks; ++rb)
-          if (rb < RB) {
-            oacc[ui][f][rb] = mfma(a[f], pfr[rb], oacc[ui][f][rb]);
-            if constexpr (BITS == 16) oacc[ui][f][rb] = mfma(alo[f], pfr[rb], oacc[ui][f][rb]);
+          for (int f = 0; f < 2; ++f)
+            cvt_b16(u4{rv[ui][2 * f][0], rv[ui][2 * f][1], rv[ui][2 * f + 1][0], rv[ui][2 * f + 1][1]}, a[f], alo[f]);
+        }
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            oacc[ui][f][rb] = mfma_f16(a[f], pfr[rb], oacc[ui][f][rb]);
+            if constexpr (BITS == 16) oacc[ui][f][rb] = mfma_f16(alo[f], pfr[rb], oacc[ui][f][rb]);
           }
       }
     }
   }
 
   // ---- finish: row sums, then normalized output or split partial -----------------
-  if (wave < RB) {
-    const float lrow = wave_sum_xor_16_32(l_lane);
-    if (g == 0) { ml_lds[2 * (16 * wave + n)] = m_run; ml_lds[2 * (16 * wave + n) + 1] = lrow; }
+  if (qk_wave) {
+    const float lrow = sum_xor_16_32(l_lane);
+    if (g == 0) { ml_lds[2 * my_row] = m_run; ml_lds[2 * my_row + 1] = lrow; }
+    if (wave == 0 && lane == 0) misc_lds[0] = Ecur;
   }
   __syncthreads();
-  const float outscale = ldexpf(kBitScale, Eexp);
+  constexpr float kBitScale = BITS == 16 ? 256.0f : 1.0f;
+  const float outscale = ntiles > 0 ? ldexpf(kBitScale, misc_lds[0]) : 0.0f;
   const bool split = E.splits > 1;
   float* part = nullptr;
   if (split) {
     const int64_t slot = ((int64_t)(s * E.splits + ksplit) * E.nrc + chunk);
     part = A.ws + E.ws_off + slot * partial_slot_floats(d);
-    if (tid < 64) {
+    if (tid < 16 * RB) {
       part[64 * (int64_t)d + tid] = ml_lds[2 * tid];
       part[64 * (int64_t)d + 64 + tid] = ml_lds[2 * tid + 1];
     }
   }
 #pragma unroll
-  for (int rb = 0; rb < kMaxRowBlocks; ++rb) {
+  for (int rb = 0; rb < RB; ++rb) {
     const int rl = 16 * rb + n;
-    if (rb < RB && rl < nrows) {
+    if (rl < nrows) {
+      const int gr = r0 + rl;
+      const int layer = A.group_layers[E.lay_begin + gr / A.heads], head = gr % A.heads;
       const float lrow = ml_lds[2 * rl + 1];
       const float fac = split ? outscale : (lrow > 0.0f ? outscale / lrow : 0.0f);
-      float* dst = split ? part + (int64_t)rl * d
-                         : A.out + A.layers[row_layer[rb]].out_off + ((int64_t)s * A.heads + row_head[rb]) * d;
+      float* dst = split ? part + (int64_t)rl * d : A.out + A.layers[layer].out_off + ((int64_t)s * A.heads + head) * d;
 #pragma unroll
-      for (int ui = 0; ui < kMaxUnitsPerWave; ++ui) {
+      for (int ui = 0; ui < NUW; ++ui) {
         const int u = wave + kWaves * ui;
         if constexpr (BITS == 2) {
           const int fbase = 32 * u + 8 * g;
           if (u < NU && fbase < d) {
-            f4 e0 = oacc[ui][0][rb] * fac, e1 = oacc[ui][1][rb] * fac;
+            const f4 e0 = oacc[ui][0][rb] * fac, e1 = oacc[ui][1][rb] * fac;
             *(f4*)(dst + fbase) = f4{e0[0], e1[0], e0[1], e1[1]};
             *(f4*)(dst + fbase + 4) = f4{e0[2], e1[2], e0[3], e1[3]};
           }
@@ -527,11 +554,11 @@ __device__ inline KArgs& kernel_args() {
   return *(KArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
 }
 
-// One kernel per bit width (entries are ordered by bit width on the host, so
-// each launch covers a contiguous item range): each specialisation is
-// register-allocated on its own.
-template <int BITS>
-__global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs, int item_begin) {
+// One kernel per (bit width, row blocks): entries are ordered by bit width on
+// the host, so each launch covers a contiguous item range, and each
+// specialisation is register-allocated on its own.
+template <int BITS, int RB>
+__global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs, int item_begin) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   KArgs& A = kernel_args();
   const int item = item_begin + blockIdx.x;
@@ -553,11 +580,12 @@ __global__ void __launch_bounds__(kThreads, 1) decode_kernel(DecodeArgs, int ite
     j = 8 * q8 + rem % r8;
   }
   const int s = j / E.splits, ks = j - s * E.splits;
-  run_item<BITS>(A, E, s, ks, chunk, lds);
+  run_item<BITS, RB>(A, E, s, ks, chunk, lds);
 }
 
-// Merge split partials of one (entry, sequence, chunk): fixed split order.
+// Merge the split partials of one (entry, sequence, chunk) in a fixed order.
 __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs) {
+  __shared__ float wgt[kMaxMergeSplits][64];
   KArgs& A = kernel_args();
   const int blk = blockIdx.x;
   int ei = -1;
@@ -568,39 +596,62 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs) {
   const int local = blk - E.merge_base;
   if (local >= A.batch * E.nrc) return;
   const int s = local / E.nrc, chunk = local - s * E.nrc;
-  const int d = E.d;
+  const int d = E.d, S = E.splits;
   const int r0 = E.row_begin + chunk * E.chunk_rows;
   const int nrows = min(E.chunk_rows, E.row_end - r0);
   const int64_t slotf = partial_slot_floats(d);
-  const float* base = A.ws + E.ws_off + (int64_t)(s * E.splits) * E.nrc * slotf + chunk * slotf;
+  const float* base = A.ws + E.ws_off + (int64_t)(s * S) * E.nrc * slotf + chunk * slotf;
   const int64_t kstride = E.nrc * slotf;
-  for (int idx = threadIdx.x; idx < nrows * d; idx += 256) {
-    const int rl = idx / d, f = idx - rl * d;
+  for (int rl = threadIdx.x; rl < nrows; rl += 256) {
     float M = -INFINITY;
-    for (int k = 0; k < E.splits; ++k) {
-      const float* p = base + k * kstride;
-      if (p[64 * (int64_t)d + 64 + rl] > 0.0f) M = fmaxf(M, p[64 * (int64_t)d + rl]);
+    for (int k = 0; k < S; ++k) {
+      const float* p = base + k * kstride + 64 * (int64_t)d;
+      if (p[64 + rl] > 0.0f) M = fmaxf(M, p[rl]);
     }
-    float L = 0.0f, acc = 0.0f;
-    for (int k = 0; k < E.splits; ++k) {
-      const float* p = base + k * kstride;
-      const float l = p[64 * (int64_t)d + 64 + rl];
-      if (l > 0.0f) {
-        const float w = exp2f(p[64 * (int64_t)d + rl] - M);
-        L += l * w;
-        acc += p[(int64_t)rl * d + f] * w;
-      }
+    float L = 0.0f;
+    for (int k = 0; k < S; ++k) {
+      const float* p = base + k * kstride + 64 * (int64_t)d;
+      L += p[64 + rl] > 0.0f ? p[64 + rl] * exp2f(p[rl] - M) : 0.0f;
     }
+    for (int k = 0; k < S; ++k) {
+      const float* p = base + k * kstride + 64 * (int64_t)d;
+      wgt[k][rl] = (L > 0.0f && p[64 + rl] > 0.0f) ? exp2f(p[rl] - M) / L : 0.0f;
+    }
+  }
+  __syncthreads();
+  const int d4 = d >> 2;
+  for (int idx = threadIdx.x; idx < nrows * d4; idx += 256) {
+    const int rl = idx / d4, f = (idx - rl * d4) * 4;
+    f4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < S; ++k) acc += *(const f4*)(base + k * kstride + (int64_t)rl * d + f) * wgt[k][rl];
     const int gr = r0 + rl;
     const int layer = A.group_layers[E.lay_begin + gr / A.heads], head = gr % A.heads;
-    A.out[A.layers[layer].out_off + ((int64_t)s * A.heads + head) * d + f] = L > 0.0f ? acc / L : 0.0f;
+    *(f4*)(A.out + A.layers[layer].out_off + ((int64_t)s * A.heads + head) * d + f) = acc;
+  }
+}
+
+template <int BITS, int RB>
+hipError_t launch_one(const DecodeArgs& a, int begin, int n, int lds, hipStream_t stream) {
+  hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<BITS, RB>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_kernel<BITS, RB>), dim3(n), dim3(kThreads), lds, stream, a, begin);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_bits(const DecodeArgs& a, int rb, int begin, int n, int lds, hipStream_t stream) {
+  switch (rb) {
+    case 1: return launch_one<BITS, 1>(a, begin, n, lds, stream);
+    case 2: return launch_one<BITS, 2>(a, begin, n, lds, stream);
+    case 3: return launch_one<BITS, 3>(a, begin, n, lds, stream);
+    default: return launch_one<BITS, 4>(a, begin, n, lds, stream);
   }
 }
 
 }  // namespace
 
 int decode_lds_bytes(int row_stride, int K, int bits) {
-  return 2 * tilebuf_bytes(row_stride, K, bits) + kSbufBytes + kPbufBytes + kMiscBytes;
+  return 2 * tilebuf_bytes(row_stride, K, bits) + kPbufBytes + kMiscBytes;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t stream) {
@@ -608,17 +659,13 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t
   for (int c = 0; c < 4; ++c) {
     const int n = L.item_end[c] - L.item_begin[c];
     if (n <= 0) continue;
-    const void* fn = c == 0 ? (const void*)decode_kernel<2> : c == 1 ? (const void*)decode_kernel<4>
-                   : c == 2 ? (const void*)decode_kernel<8> : (const void*)decode_kernel<16>;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, L.lds_bytes[c]);
-    if (e != hipSuccess) return e;
+    hipError_t e;
     switch (c) {
-      case 0: hipLaunchKernelGGL(decode_kernel<2>, dim3(n), dim3(kThreads), L.lds_bytes[c], stream, a, L.item_begin[c]); break;
-      case 1: hipLaunchKernelGGL(decode_kernel<4>, dim3(n), dim3(kThreads), L.lds_bytes[c], stream, a, L.item_begin[c]); break;
-      case 2: hipLaunchKernelGGL(decode_kernel<8>, dim3(n), dim3(kThreads), L.lds_bytes[c], stream, a, L.item_begin[c]); break;
-      default: hipLaunchKernelGGL(decode_kernel<16>, dim3(n), dim3(kThreads), L.lds_bytes[c], stream, a, L.item_begin[c]); break;
+      case 0: e = launch_bits<2>(a, L.row_blocks, L.item_begin[c], n, L.lds_bytes[c], stream); break;
+      case 1: e = launch_bits<4>(a, L.row_blocks, L.item_begin[c], n, L.lds_bytes[c], stream); break;
+      case 2: e = launch_bits<8>(a, L.row_blocks, L.item_begin[c], n, L.lds_bytes[c], stream); break;
+      default: e = launch_bits<16>(a, L.row_blocks, L.item_begin[c], n, L.lds_bytes[c], stream); break;
     }
-    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (L.merge_blocks > 0) {

@@ -16,6 +16,8 @@
 #include "kk.h"
 #include "kk_internal.h"
 
+static_assert(kk::kMaxK == KK_MAX_K && kk::kMaxLayers == KK_MAX_LAYERS, "ABI limits and kernel limits differ");
+
 namespace {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -92,7 +94,12 @@ kk_status make_plan(const kk_model_cfg* c, int batch, int max_len, int split_tok
     int64_t bytes_item;
   };
   std::vector<Ent> ents;
-  const int kEntryRows = 64 * 8;
+  // Row chunks: RB blocks of 16 rows per item, RB fixed by the head count; when
+  // a layer's heads fit in one item, chunks hold whole layers (least padding).
+  const int RB = std::min(4, (std::min(H, 64) + 15) / 16);
+  const int chunk_rows = H <= 64 ? H * ((16 * RB) / H) : 64;
+  const int kEntryRows = 8 * chunk_rows;
+  P.launch.row_blocks = RB;
   for (size_t gi = 0; gi < groups.size(); ++gi) {
     const int a = groups[gi].first, begin = groups[gi].second;
     const int end = gi + 1 < groups.size() ? groups[gi + 1].second : L;
@@ -106,9 +113,8 @@ kk_status make_plan(const kk_model_cfg* c, int batch, int max_len, int split_tok
       E.e.row_begin = rb;
       E.e.row_end = std::min(rows, rb + kEntryRows);
       const int n = E.e.row_end - E.e.row_begin;
-      const int nrc = (n + 63) / 64;
-      E.e.nrc = (int16_t)nrc;
-      E.e.chunk_rows = (int16_t)(((n + nrc - 1) / nrc + 15) / 16 * 16);
+      E.e.nrc = (int16_t)((n + chunk_rows - 1) / chunk_rows);
+      E.e.chunk_rows = (int16_t)chunk_rows;
       E.e.lay_begin = (int16_t)begin;
       E.anchor = a;
       E.bytes_item = (int64_t)max_len * (E.e.row_stride + 4);
@@ -117,16 +123,19 @@ kk_status make_plan(const kk_model_cfg* c, int batch, int max_len, int split_tok
   }
   if ((int)ents.size() > kk::kMaxEntries) return KK_ERR_UNSUPPORTED;
 
-  int64_t total = 0;
-  for (auto& E : ents) total += E.bytes_item * E.e.nrc * batch;
-  const int64_t target = std::max<int64_t>(total / (4 * kk::kPlanCUs), 256 * 1024);
+  // Splits: each bit width runs as its own launch, so items are sized per bit
+  // width to give every launch about two waves of items over the resident
+  // workgroup slots (at least 256 KB of cache per item).
+  int64_t class_bytes[4] = {0, 0, 0, 0};
+  for (auto& E : ents) class_bytes[bits_class(E.e.bits)] += E.bytes_item * E.e.nrc * batch;
   const int max_tiles = std::max(1, (max_len + kk::kTile - 1) / kk::kTile);
   for (auto& E : ents) {
+    const int64_t target = std::max<int64_t>(class_bytes[bits_class(E.e.bits)] / (2 * kk::kPlanSlots), 256 * 1024);
     int64_t sp;
     if (split_tokens > 0) sp = (max_len + split_tokens - 1) / split_tokens;
     else sp = (E.bytes_item + target - 1) / target;
     sp = std::max<int64_t>(1, std::min<int64_t>(sp, max_tiles));
-    sp = std::min<int64_t>(sp, 1024);
+    sp = std::min<int64_t>(sp, kk::kMaxMergeSplits);
     E.e.splits = (int16_t)sp;
   }
   std::stable_sort(ents.begin(), ents.end(), [](const Ent& x, const Ent& y) {

@@ -12,11 +12,12 @@ constexpr int kWaves = 4;            // waves per workgroup (256 threads)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;            // cached tokens per pipeline stage
 constexpr int kMaxRowBlocks = 4;     // 16-row MFMA blocks per work item (<= 64 query rows)
-constexpr int kMaxChunksPerWave = 5; // 32-wide contraction chunks per wave in Q.K (K <= 640)
 constexpr int kMaxUnitsPerWave = 4;  // 32-feature output units per wave in P.V (d <= 512)
+constexpr int kMaxMergeSplits = 64;  // token splits of one sequence
+constexpr int kMaxK = 640;           // d + d_R (the ABI limit)
 constexpr int kMaxEntries = 96;      // group entries per launch
 constexpr int kMaxLayers = 64;
-constexpr int kPlanCUs = 256;        // compute units assumed by the split policy
+constexpr int kPlanSlots = 2 * 256;  // workgroups resident at once on 256 CUs (split policy)
 constexpr float kLazyRescale = 8.0f; // log2 headroom before the running max is moved
 
 // One layer: softmax scale, kept width of its anchor and the float offset of
@@ -75,6 +76,7 @@ hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
 // Per bit-width launch ranges (class c: bits 2 << c): items [item_begin, item_end).
 struct DecodeLaunch {
   int item_begin[4], item_end[4], lds_bytes[4];
+  int row_blocks;        // 16-row MFMA blocks per item (1..4), uniform for the step
   int merge_blocks;
 };
 
