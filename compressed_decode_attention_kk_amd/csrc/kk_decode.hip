@@ -30,6 +30,8 @@
 // that were split write (m, l, O) partials; a small kernel merges them.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "kk_internal.h"
 
 namespace kk {
@@ -314,6 +316,7 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
   float m_run = -INFINITY, l_lane = 0.0f;     // softmax state of row 16*wave + n
   int Ecur = -1000;                            // scales of the item so far are <= 2^(Ecur + headroom)
   const int NU = (d + 31) >> 5;               // 32-feature output units
+  const int my_units = NU > wave ? (NU - wave + kWaves - 1) / kWaves : 0;
 
   for (int it = 0; it < ntiles; ++it) {
     __builtin_amdgcn_s_waitcnt(0x3f70);        // vmcnt(0): this tile's copies have landed
@@ -331,9 +334,13 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
       for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
         for (int k = 0; k < NACC; ++k) acc[tb][k] = i4{0, 0, 0, 0};
+      // The chunk count is a compile-time constant in each case below, so every
+      // LDS read of the tile is straight-line code the scheduler can hoist
+      // ahead of the MFMAs that consume it.
+      auto qk_chunks = [&](auto nc) {
+        constexpr int NC = decltype(nc)::value;
 #pragma unroll
-      for (int c = 0; c < kMaxChunks64; ++c) {
-        if (c < KC) {
+        for (int c = 0; c < NC; ++c) {
           const int fbyte = (64 * c + 16 * g) * BITS / 8;     // first byte of this lane's 16 features
 #pragma unroll
           for (int tb = 0; tb < 2; ++tb) {
@@ -363,6 +370,18 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
             }
           }
         }
+      };
+      switch (KC) {
+        case 1: qk_chunks(std::integral_constant<int, 1>{}); break;
+        case 2: qk_chunks(std::integral_constant<int, 2>{}); break;
+        case 3: qk_chunks(std::integral_constant<int, 3>{}); break;
+        case 4: qk_chunks(std::integral_constant<int, 4>{}); break;
+        case 5: qk_chunks(std::integral_constant<int, 5>{}); break;
+        case 6: qk_chunks(std::integral_constant<int, 6>{}); break;
+        case 7: qk_chunks(std::integral_constant<int, 7>{}); break;
+        case 8: qk_chunks(std::integral_constant<int, 8>{}); break;
+        case 9: qk_chunks(std::integral_constant<int, 9>{}); break;
+        default: qk_chunks(std::integral_constant<int, kMaxChunks64>{}); break;
       }
 
       // ---- online softmax for these rows ----
@@ -431,41 +450,42 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
           for (int f = 0; f < 2; ++f) oacc[u][f][rb] *= al;
       }
     }
-    // transposed operand reads of all units first (units past NU re-read unit NU-1)
-    u2 rv[NUW][BITS == 16 ? 4 : BITS == 8 ? 2 : 1];
+    // units of this wave: u = wave + 4*ui for ui < UW; all operand reads first
+    auto pv_units = [&](auto uw) {
+      constexpr int UW = decltype(uw)::value;
+      u2 rv[UW > 0 ? UW : 1][BITS == 16 ? 4 : BITS == 8 ? 2 : 1];
 #pragma unroll
-    for (int ui = 0; ui < NUW; ++ui) {
-      const int u = min(wave + kWaves * ui, NU - 1);
-      if constexpr (BITS == 8) {
+      for (int ui = 0; ui < UW; ++ui) {
+        const int u = wave + kWaves * ui;
+        if constexpr (BITS == 8) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int e = n >> 1, h = n & 1, tb = e >> 2;
-          const char* p = buf + tile_off(PITCH, tb, 2 * u + f, 4 * g + (e & 3)) + 8 * h;
-          rv[ui][f] = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i2, p)));
+          for (int f = 0; f < 2; ++f) {
+            const int e = n >> 1, h = n & 1, tb = e >> 2;
+            const char* p = buf + tile_off(PITCH, tb, 2 * u + f, 4 * g + (e & 3)) + 8 * h;
+            rv[ui][f] = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i2, p)));
+          }
+        }
+        if constexpr (BITS == 4 || BITS == 2) {
+          const int e = n & 7, half = n >> 3;
+          const int tb = (e >> 1) & 1, t = 4 * g + 2 * (e & 1) + (e >> 2);
+          const char* p = BITS == 4 ? buf + tile_off(PITCH, tb, u, t) + 8 * half
+                                    : buf + tile_off(PITCH, tb, u >> 1, t) + 8 * (u & 1);
+          rv[ui][0] = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr4_b64_v2i32(LDS_PTR(i2, p)));
+        }
+        if constexpr (BITS == 16) {
+#pragma unroll
+          for (int f = 0; f < 2; ++f) {
+            const int fb = 2 * u + f, e = n >> 2, q = n & 3;
+            const int seg = 2 * fb + (q >> 1), off = 8 * (q & 1);
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb)
+              rv[ui][2 * f + tb] = __builtin_bit_cast(
+                  u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s4, buf + tile_off(PITCH, tb, seg, 4 * g + e) + off)));
+          }
         }
       }
-      if constexpr (BITS == 4 || BITS == 2) {
-        const int e = n & 7, half = n >> 3;
-        const int tb = (e >> 1) & 1, t = 4 * g + 2 * (e & 1) + (e >> 2);
-        const char* p = BITS == 4 ? buf + tile_off(PITCH, tb, u, t) + 8 * half
-                                  : buf + tile_off(PITCH, tb, u >> 1, t) + 8 * (u & 1);
-        rv[ui][0] = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr4_b64_v2i32(LDS_PTR(i2, p)));
-      }
-      if constexpr (BITS == 16) {
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
-          const int fb = 2 * u + f, e = n >> 2, q = n & 3;
-          const int seg = 2 * fb + (q >> 1), off = 8 * (q & 1);
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb)
-            rv[ui][2 * f + tb] = __builtin_bit_cast(
-                u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s4, buf + tile_off(PITCH, tb, seg, 4 * g + e) + off)));
-        }
-      }
-    }
-#pragma unroll
-    for (int ui = 0; ui < NUW; ++ui) {
-      if (wave + kWaves * ui < NU) {
+      for (int ui = 0; ui < UW; ++ui) {
         h8 a[2], alo[2];
         if constexpr (BITS == 8) {
           a[0] = cvt_b8(rv[ui][0][0], rv[ui][0][1]);
@@ -486,6 +506,13 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
             if constexpr (BITS == 16) oacc[ui][f][rb] = mfma_f16(alo[f], pfr[rb], oacc[ui][f][rb]);
           }
       }
+    };
+    switch (my_units) {
+      case 0: break;
+      case 1: pv_units(std::integral_constant<int, 1>{}); break;
+      case 2: pv_units(std::integral_constant<int, 2>{}); break;
+      case 3: pv_units(std::integral_constant<int, 3>{}); break;
+      default: pv_units(std::integral_constant<int, NUW>{}); break;
     }
   }
 

@@ -154,8 +154,10 @@ kk_status kk_decode_workspace_bytes(const kk_model_cfg* cfg, int32_t batch, int3
  *
  * caches     : host array [n_layers]; entries of inheriting layers are ignored.
  * seq_lens   : device int32 [batch]; each value is clamped to [0, t_cap].
- * max_seq_len: host bound used for planning, >= every seq_lens value
- *              (values above it are clamped to it).
+ * max_seq_len: host planning hint in [0, t_cap]: the expected longest
+ *              sequence, which sets how many splits each sequence's tokens
+ *              are cut into.  It never truncates: every sequence is attended
+ *              over all of its (clamped) seq_lens tokens, also above it.
  * q_lat      : device [n_layers][batch][n_heads][r], q_dtype.
  * q_rope     : device [n_layers][batch][n_heads][d_rope], q_dtype.
  * out        : device float32, packed as kk_out_offsets describes.

@@ -1,0 +1,208 @@
+"""The C ABI on the host: the library loads, exports every function that
+include/kk.h declares, and its host-only calls (sizes, offsets, table
+validation, argument checks that reject a call before anything is enqueued)
+behave as documented.  No call here reaches a kernel launch, so no GPU is
+needed."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from oracle import kk_oracle as ko
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kk.h")
+
+
+@pytest.fixture(scope="module")
+def kk():
+    import compressed_decode_attention_kk_amd as kk
+    kk.lib()
+    return kk
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(kk_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("kk_quantize_write", "kk_decode_attn", "kk_decode_workspace_bytes", "kk_cache_bytes",
+              "kk_out_offsets", "kk_validate_model", "kk_row_stride_bytes", "kk_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_function(kk):
+    L = ctypes.CDLL(kk.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, f"declared in kk.h but not exported: {missing}"
+
+
+def test_missing_library_fails_loudly(kk, monkeypatch):
+    monkeypatch.setattr(kk.kk, "_lib", None)
+    monkeypatch.setattr(kk.kk, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libkk.so"))
+    with pytest.raises(ImportError):
+        kk.kk.lib()
+
+
+@pytest.mark.parametrize("d,dr,bits", [(512, 64, 2), (512, 64, 4), (512, 64, 8), (512, 64, 16), (256, 64, 4),
+                                       (32, 16, 8), (64, 16, 2), (96, 32, 2), (160, 64, 4), (16, 16, 2)])
+def test_row_stride_matches_oracle_layout(kk, d, dr, bits):
+    assert kk.row_stride_bytes(d, dr, bits) == ko.row_stride(d + dr, bits)
+
+
+def test_row_stride_rejects_invalid(kk):
+    assert kk.row_stride_bytes(64, 16, 3) == 0
+    assert kk.row_stride_bytes(0, 16, 4) == 0
+    assert kk.row_stride_bytes(3, 0, 2) == 0          # 6 bits: not whole bytes
+
+
+def table(rows, r=512, dr=64, heads=8, kk=None):
+    layers = [kk.LayerSpec(a, d, b, 1.0 / math.sqrt(max(d, 1) + dr)) for a, d, b in rows]
+    return kk.Model(layers, heads, r, dr)
+
+
+def status(kk, model):
+    return kk.lib().kk_validate_model(model.cfg)
+
+
+def test_validate_model_rules(kk):
+    ok = [[0, 512, 4], [0, 0, 0], [2, 256, 16], [2, 0, 0]]
+    assert status(kk, table(ok, kk=kk)) == kk.KK_OK
+    cases = {
+        kk.KK_ERR_INVALID_ARGUMENT: [
+            [[0, 0, 0]] * 1 + [[0, 0, 0]],            # layer 0 inherits (anchor 0 has d = 0)
+            [[1, 64, 4], [1, 64, 4]],                 # layer 0 points forward
+            [[0, 64, 4], [0, 0, 0], [1, 0, 0]],       # inherits an inheritor
+            [[0, 64, 3]],                             # bits outside {2,4,8,16}
+            [[0, 528, 4]],                            # d > r
+            [[0, 64, 4], [2, 0, 0]],                  # anchor index beyond own index
+        ],
+        kk.KK_ERR_UNSUPPORTED: [
+            [[0, 72, 4]],                             # d not a multiple of 16
+        ],
+    }
+    for want, tables in cases.items():
+        for t in tables:
+            assert status(kk, table(t, kk=kk)) == want, t
+    assert status(kk, table([[0, 64, 4]] + [[0, 0, 0]] * 64, kk=kk)) == kk.KK_ERR_UNSUPPORTED   # 65 layers
+    assert status(kk, table([[0, 576, 4]], r=640, dr=64, kk=kk)) == kk.KK_ERR_UNSUPPORTED      # d > 512
+    assert status(kk, table([[0, 64, 4]], dr=144, kk=kk)) == kk.KK_ERR_UNSUPPORTED             # d_R > 128
+    assert status(kk, table([[0, 64, 4]], dr=24, kk=kk)) == kk.KK_ERR_UNSUPPORTED              # d_R % 16
+    m = table([[0, 64, 4]], kk=kk)
+    m._arr[0].sm_scale = float("nan")
+    assert status(kk, m) == kk.KK_ERR_INVALID_ARGUMENT
+
+
+def test_cache_bytes_and_offsets(kk):
+    rows = [[0, 512, 4], [0, 0, 0], [2, 256, 16], [2, 0, 0], [2, 0, 0], [5, 128, 2]]
+    m = table(rows, heads=40, kk=kk)
+    B, T = 32, 8192
+    for a, d, b in [(0, 512, 4), (2, 256, 16), (5, 128, 2)]:
+        cb, sb = kk.cache_bytes(m, a, B, T)
+        assert cb == B * T * ko.row_stride(d + 64, b)
+        assert sb == B * T * 4
+    with pytest.raises(kk.KKError) as e:
+        kk.cache_bytes(m, 1, B, T)
+    assert e.value.status == kk.KK_ERR_INVALID_ARGUMENT
+    offs = kk.out_offsets(m, B)
+    d_eff = [512, 512, 256, 256, 256, 128]
+    want = [0]
+    for d in d_eff:
+        want.append(want[-1] + B * 40 * d)
+    assert offs == want
+
+
+def test_workspace_sizes(kk):
+    rows = [[0, 512, 4], [0, 0, 0], [2, 256, 16]]
+    m = table(rows, heads=40, kk=kk)
+    # one split per sequence needs no partials
+    assert kk.workspace_bytes(m, 4, 1024, 1024) == 0
+    small = kk.workspace_bytes(m, 4, 1024, 512)
+    smaller = kk.workspace_bytes(m, 4, 1024, 64)
+    assert 0 < small < smaller
+    assert kk.workspace_bytes(m, 4, 0, 0) == 0
+    with pytest.raises(kk.KKError) as e:
+        kk.workspace_bytes(m, 4, 1024, 48)                 # not a multiple of the 32-token tile
+    assert e.value.status == kk.KK_ERR_INVALID_ARGUMENT
+
+
+class _Fake:
+    """Distinct, 256-byte aligned, never dereferenced host addresses for
+    argument-check calls that must return before any launch."""
+
+    def __init__(self):
+        self.buf = ctypes.create_string_buffer(1 << 16)
+        self.base = (ctypes.addressof(self.buf) + 255) // 256 * 256
+
+    def __call__(self, i, misalign=0):
+        return ctypes.c_void_p(self.base + 1024 * i + misalign)
+
+
+def test_decode_attn_rejects_bad_arguments_before_launch(kk):
+    L = kk.lib()
+    rows = [[0, 128, 4], [0, 0, 0], [2, 64, 8]]
+    m = table(rows, r=128, dr=32, heads=16, kk=kk)
+    fake = _Fake()
+    caches = (kk.Cache * 3)()
+    caches[0] = kk.Cache(fake(1).value, fake(2).value)
+    caches[2] = kk.Cache(fake(3).value, fake(4).value)
+    B, T = 4, 1024
+    need = kk.workspace_bytes(m, B, T, 64)
+    assert need > 0
+
+    def call(**kw):
+        a = dict(caches=caches, batch=B, t_cap=T, seq_lens=fake(5), max_len=T, q_lat=fake(6), q_rope=fake(7),
+                 q_dtype=kk.KK_DTYPE_F32, out=fake(8), split=64, ws=fake(9), ws_bytes=need)
+        a.update(kw)
+        return L.kk_decode_attn(m.cfg, a["caches"], a["batch"], a["t_cap"], a["seq_lens"], a["max_len"],
+                                a["q_lat"], a["q_rope"], a["q_dtype"], a["out"], a["split"], a["ws"],
+                                a["ws_bytes"], None)
+
+    assert call(ws_bytes=need - 1) == kk.KK_ERR_WORKSPACE_TOO_SMALL
+    assert call(ws=fake(9, 16)) == kk.KK_ERR_INVALID_ARGUMENT          # workspace not 256-byte aligned
+    assert call(ws=None) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(q_lat=fake(6, 4)) == kk.KK_ERR_INVALID_ARGUMENT        # query not 16-byte aligned
+    assert call(out=None) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(max_len=T + 1) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(split=33) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(batch=0) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(q_dtype=7) == kk.KK_ERR_INVALID_ARGUMENT
+    bad = (kk.Cache * 3)()
+    bad[0] = caches[0]                                                 # anchor 2 has no buffers
+    assert call(caches=bad) == kk.KK_ERR_INVALID_ARGUMENT
+    bad[2] = kk.Cache(fake(3, 8).value, fake(4).value)                 # codes not 16-byte aligned
+    assert call(caches=bad) == kk.KK_ERR_INVALID_ARGUMENT
+
+
+def test_quantize_write_rejects_bad_arguments_before_launch(kk):
+    L = kk.lib()
+    rows = [[0, 128, 4], [0, 0, 0]]
+    m = table(rows, r=128, dr=32, heads=16, kk=kk)
+    fake = _Fake()
+
+    def call(layer=0, dtype=kk.KK_DTYPE_F32, lat_ld=128, rope_ld=32, n_src=10, n_tok=10, codes=None, latent=None):
+        c = kk.Cache(codes if codes is not None else fake(1).value, fake(2).value)
+        return L.kk_quantize_write(m.cfg, layer, latent if latent is not None else fake(3), fake(4), dtype,
+                                   lat_ld, rope_ld, n_src, n_tok, None, fake(5), c, 2, 16, None)
+
+    assert call(layer=1) == kk.KK_ERR_INVALID_ARGUMENT                 # an inheriting layer owns no cache
+    assert call(layer=2) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(dtype=5) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(lat_ld=64) == kk.KK_ERR_INVALID_ARGUMENT               # row shorter than d
+    assert call(rope_ld=16) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(n_tok=-1) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(codes=fake(1, 8).value) == kk.KK_ERR_INVALID_ARGUMENT  # codes not 16-byte aligned
+    assert call(latent=fake(3, 2)) == kk.KK_ERR_INVALID_ARGUMENT       # f32 rows not 4-byte aligned
+    assert call(n_tok=0) == kk.KK_OK                                   # nothing to write: no launch
+
+
+def test_status_strings(kk):
+    seen = {kk.status_string(s) for s in range(5)}
+    assert len(seen) == 5 and kk.status_string(0) == "ok"
+    assert kk.status_string(99) == "unknown status"
