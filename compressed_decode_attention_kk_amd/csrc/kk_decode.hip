@@ -150,17 +150,73 @@ __device__ constexpr int qk_slot_feature(int i) {
 __device__ inline f4 mfma_f16(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 __device__ inline i4 mfma_i8(i4 a, i4 b, i4 c) { return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0); }
 
+// Reductions over the four 16-lane rows of a wave (lanes n, n+16, n+32, n+48)
+// with the gfx950 row-swap instructions: v_permlane16_swap exchanges odd and
+// even 16-lane rows, v_permlane32_swap the two 32-lane halves.  Called with
+// both operands equal, they return (row 0, row 0, row 2, row 2) and
+// (row 1, row 1, row 3, row 3) (resp. (half 0, half 0), (half 1, half 1)), so
+// op(r[0], r[1]) is the pairwise result, in the same operand order on every lane.
 __device__ inline float max_xor_16_32(float v) {
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  const uint32_t x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const uint32_t y = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ inline float sum_xor_16_32(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  const uint32_t x = __float_as_uint(v);
+  const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const uint32_t y = __float_as_uint(v);
+  const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// Workgroup barrier for LDS hand-offs.  __syncthreads() also fences memory,
+// which drains every outstanding HBM -> LDS copy (they count as LDS stores) and
+// so would serialize the tile pipeline; here only the LDS operations of the
+// calling wave are waited for, and copies are waited for explicitly (vm_wait).
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// HBM -> LDS copies (global_load_lds): lane i writes LDS at lds_base + i*16
+// (dwordx4) or lds_base + i*4 (dword).  Written as asm so that the compiler's
+// wait insertion does not see them: it cannot tell that they never alias the
+// LDS reads of the tile being computed and would drain every copy in flight
+// before each such read.  All waits for them are explicit (vm_wait).  M0 holds
+// the LDS base; the nop covers the M0-write hazard.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void copy16_to_lds(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base) : "memory", "m0");
+}
+__device__ inline void copy4_to_lds(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ inline uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LDS_PTR(const void, p));
+}
+
+// Wait until at most n vector-memory operations of this wave are outstanding
+// (n is clamped to 31; a smaller count only waits longer).
+__device__ inline void vm_wait(int n) {
+  // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt at their maxima
+#define KK_VM(k) case k: __builtin_amdgcn_s_waitcnt(0x3f70 | ((k) & 15) | (((k) >> 4) << 14)); break;
+  switch (n) {
+    KK_VM(0) KK_VM(1) KK_VM(2) KK_VM(3) KK_VM(4) KK_VM(5) KK_VM(6) KK_VM(7)
+    KK_VM(8) KK_VM(9) KK_VM(10) KK_VM(11) KK_VM(12) KK_VM(13) KK_VM(14) KK_VM(15)
+    KK_VM(16) KK_VM(17) KK_VM(18) KK_VM(19) KK_VM(20) KK_VM(21) KK_VM(22) KK_VM(23)
+    KK_VM(24) KK_VM(25) KK_VM(26) KK_VM(27) KK_VM(28) KK_VM(29) KK_VM(30) KK_VM(31)
+    default: __builtin_amdgcn_s_waitcnt(0x3f70 | 15 | (1 << 14)); break;
+  }
+#undef KK_VM
+}
+
 __device__ inline int isum_xor_16_32(int v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = (int)a[0] + (int)a[1];
+  const auto b = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  return (int)b[0] + (int)b[1];
 }
 
 // Byte offset of (token block tb, segment seg, token-in-block t) inside a tile
@@ -179,7 +235,8 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
   const int d = E.d, K = d + A.d_rope, KC = chunks64_of(K);
   const int NSEG = nseg_of(E.row_stride), PITCH = NSEG * 256;
   const int bufbytes = tilebuf_bytes(E.row_stride, K, BITS);
-  char* pbuf = lds + 2 * bufbytes;
+  const int nbuf = E.nbuf;                    // tile buffers; nbuf - 1 tiles are in flight
+  char* pbuf = lds + nbuf * bufbytes;
   float* alpha_lds = (float*)(pbuf + kPbufBytes);
   int* flag_lds = (int*)(alpha_lds + 64);
   float* ml_lds = (float*)(flag_lds + 4);
@@ -208,31 +265,38 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
   const int64_t row0 = (int64_t)s * A.t_cap + t0;    // first cache row of this item
 
   // ---- tile loader: direct HBM -> LDS copies ---------------------------------------
+  // Every wave issues the same number of copy instructions for every tile
+  // (rows past the valid tokens re-read the last valid row), so "tile `it` has
+  // landed" is a fixed count of this wave's outstanding copies.
   const uint8_t* codes = E.codes;
   const float* scales = E.scales;
   const int block_pieces = NSEG * 16;
-  auto issue_tile = [&](int it) {
-    char* buf = lds + (it & 1) * bufbytes;
+  const int npos = 2 * block_pieces;             // 16-byte pieces of codes in a tile
+  const int ninst = (npos + 63) >> 6;            // 64-lane copy instructions per tile
+  // this wave's copy instructions per tile (wave-uniform, so the waits below are scalar code)
+  const int copies = __builtin_amdgcn_readfirstlane((ninst > wave ? (ninst - wave + kWaves - 1) / kWaves : 0) +
+                                                    (wave == kWaves - 1 ? 1 : 0));
+  auto issue_tile = [&](int it, int slotb) {
+    char* buf = lds + slotb * bufbytes;
     const int tok0 = it * kTile;
-    const int tvalid = min(kTile, ntok - tok0);
-    const int npos = 2 * block_pieces;           // 16-byte pieces of codes in the tile
-    const int ninst = (npos + 63) >> 6;
+    const int tlast = min(kTile, ntok - tok0) - 1;
     for (int i = wave; i < ninst; i += kWaves) {
       const int p = i * 64 + lane;
       const int tb = p >= block_pieces ? 1 : 0;
       const int rem = p - tb * block_pieces;
       const int seg = rem >> 4, slot = rem & 15;
-      const int t = 16 * tb + (slot ^ (tb << 2));
-      if (p < npos && t < tvalid) {
+      const int t = min(16 * tb + (slot ^ (tb << 2)), tlast);
+      if (p < npos) {                            // lane 0 always copies: the instruction is issued
         const uint8_t* gp = codes + (row0 + tok0 + t) * (int64_t)E.row_stride + seg * 16;
-        __builtin_amdgcn_global_load_lds(gp, LDS_PTR(void, buf + i * 1024), 16, 0, 0);
+        copy16_to_lds(gp, lds_addr(buf + i * 1024));
       }
     }
-    if (wave == kWaves - 1 && lane < tvalid) {
-      __builtin_amdgcn_global_load_lds(scales + row0 + tok0 + lane, LDS_PTR(void, buf + 2 * PITCH), 4, 0, 0);
+    if (wave == kWaves - 1 && lane < kTile) {
+      copy4_to_lds(scales + row0 + tok0 + min(lane, tlast), lds_addr(buf + 2 * PITCH));
     }
   };
-  if (ntiles > 0) issue_tile(0);
+  const int depth = nbuf - 1;
+  for (int it = 0; it < depth && it < ntiles; ++it) issue_tile(it, it);
 
   // ---- q as two int8 limbs of a 14-bit fixed-point number per row ------------------
   // chunk c, lane (g, n): row 16*wave + n, features 64c + 16g + qk_slot_feature(i).
@@ -318,32 +382,36 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
   const int NU = (d + 31) >> 5;               // 32-feature output units
   const int my_units = NU > wave ? (NU - wave + kWaves - 1) / kWaves : 0;
 
+  int cur = 0;                                  // buffer of tile `it`
   for (int it = 0; it < ntiles; ++it) {
-    __builtin_amdgcn_s_waitcnt(0x3f70);        // vmcnt(0): this tile's copies have landed
-    __syncthreads();                            // (A) tile visible; previous P.V finished
-    if (it + 1 < ntiles) issue_tile(it + 1);
-    const char* buf = lds + (it & 1) * bufbytes;
+    vm_wait(min(depth - 1, ntiles - 1 - it) * copies);   // this wave's copies of tile `it` have landed
+    lds_barrier();                              // (A) tile visible to all; previous P.V finished
+    if (it + depth < ntiles) issue_tile(it + depth, cur == 0 ? nbuf - 1 : cur - 1);
+    const char* buf = lds + cur * bufbytes;
+    cur = cur + 1 == nbuf ? 0 : cur + 1;
     const float* sc = (const float*)(buf + 2 * PITCH);
     const int tvalid = min(kTile, ntok - it * kTile);
 
     if (qk_wave) {
       // ---- Q.K for this wave's 16 rows, all features, both token blocks ----
-      constexpr int NACC = BITS == 16 ? 4 : 2;   // code x q_hi, code x q_lo (b = 16: high and low byte each)
-      i4 acc[2][NACC];
-#pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int k = 0; k < NACC; ++k) acc[tb][k] = i4{0, 0, 0, 0};
+      // code x q_hi, code x q_lo; b = 16: high byte x (q_hi, q_lo) and low byte x q_hi.
+      // The low byte x q_lo product is left out: its weight is 2^-15 of the
+      // leading term, below the 14-bit rounding of q itself.
+      constexpr int NACC = BITS == 16 ? 3 : 2;
+      float sqv[2][4];                            // integer scores (exact in fp32 for b < 16)
       // The chunk count is a compile-time constant in each case below, so every
       // LDS read of the tile is straight-line code the scheduler can hoist
-      // ahead of the MFMAs that consume it.
+      // ahead of the MFMAs that consume it.  b = 16 finishes one token block
+      // before starting the other (its operands and accumulators are larger).
       auto qk_chunks = [&](auto nc) {
         constexpr int NC = decltype(nc)::value;
+        i4 acc[2][NACC];
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int fbyte = (64 * c + 16 * g) * BITS / 8;     // first byte of this lane's 16 features
+        for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {
+          for (int k = 0; k < NACC; ++k) acc[tb][k] = i4{0, 0, 0, 0};
+        auto step = [&](int c, int tb) {
+            const int fbyte = (64 * c + 16 * g) * BITS / 8;   // first byte of this lane's 16 features
             const char* p = buf + tile_off(PITCH, tb, fbyte >> 4, n) + (fbyte & 15);
             if constexpr (BITS == 8) {
               const i4 a = *(const i4*)p;
@@ -366,9 +434,32 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
               acc[tb][0] = mfma_i8(hi, qh[c], acc[tb][0]);
               acc[tb][1] = mfma_i8(hi, ql[c], acc[tb][1]);
               acc[tb][2] = mfma_i8(lo, qh[c], acc[tb][2]);
-              acc[tb][3] = mfma_i8(lo, ql[c], acc[tb][3]);
             }
+        };
+        auto finish = [&](int tb) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            if constexpr (BITS == 16)
+              sqv[tb][j] = 256.0f * (float)(128 * acc[tb][0][j] + acc[tb][1][j]) + (float)(128 * acc[tb][2][j] + qbias);
+            else
+              sqv[tb][j] = (float)(128 * acc[tb][0][j] + acc[tb][1][j] - qbias);
           }
+        };
+        if constexpr (BITS == 16) {
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) step(c, tb);
+            finish(tb);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int tb = 0; tb < 2; ++tb) step(c, tb);
+          }
+          finish(0);
+          finish(1);
         }
       };
       switch (KC) {
@@ -394,11 +485,7 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const bool valid = 16 * tb + 4 * g + j < tvalid;
-          float sq;
-          if constexpr (BITS == 16)
-            sq = 256.0f * (float)(128 * acc[tb][0][j] + acc[tb][1][j]) + (float)(128 * acc[tb][2][j] + acc[tb][3][j] + qbias);
-          else
-            sq = (float)(128 * acc[tb][0][j] + acc[tb][1][j] - qbias);
+          const float sq = sqv[tb][j];
           const float st = valid ? scv[tb][j] : 0.0f;
           scv[tb][j] = st;
           smax = fmaxf(smax, st);
@@ -435,7 +522,7 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
         }
       ((h8*)pbuf)[wave * 64 + lane] = pf;
     }
-    __syncthreads();                            // (C) P' and rescale factors visible
+    lds_barrier();                              // (C) P' and rescale factors visible
 
     // ---- P.V over this wave's output units ----
     h8 pfr[RB];
@@ -456,6 +543,9 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
       u2 rv[UW > 0 ? UW : 1][BITS == 16 ? 4 : BITS == 8 ? 2 : 1];
 #pragma unroll
       for (int ui = 0; ui < UW; ++ui) {
+        if constexpr (BITS == 16) {
+          if (ui > 0) __builtin_amdgcn_sched_barrier(0);
+        }
         const int u = wave + kWaves * ui;
         if constexpr (BITS == 8) {
 #pragma unroll
@@ -486,6 +576,10 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
       }
 #pragma unroll
       for (int ui = 0; ui < UW; ++ui) {
+        // b = 16 holds twice the operands per unit: one unit at a time
+        if constexpr (BITS == 16) {
+          if (ui > 0) __builtin_amdgcn_sched_barrier(0);
+        }
         h8 a[2], alo[2];
         if constexpr (BITS == 8) {
           a[0] = cvt_b8(rv[ui][0][0], rv[ui][0][1]);
@@ -522,7 +616,7 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
     if (g == 0) { ml_lds[2 * my_row] = m_run; ml_lds[2 * my_row + 1] = lrow; }
     if (wave == 0 && lane == 0) misc_lds[0] = Ecur;
   }
-  __syncthreads();
+  lds_barrier();
   constexpr float kBitScale = BITS == 16 ? 256.0f : 1.0f;
   const float outscale = ntiles > 0 ? ldexpf(kBitScale, misc_lds[0]) : 0.0f;
   const bool split = E.splits > 1;
@@ -581,14 +675,14 @@ __device__ inline KArgs& kernel_args() {
   return *(KArgs*)(__builtin_amdgcn_kernarg_segment_ptr());
 }
 
-// One kernel per (bit width, row blocks): entries are ordered by bit width on
-// the host, so each launch covers a contiguous item range, and each
-// specialisation is register-allocated on its own.
-template <int BITS, int RB>
-__global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs, int item_begin) {
+// One launch covers the items of every bit width, interleaved by the host so
+// that each CU runs a mix of bandwidth-bound (wide codes) and arithmetic-bound
+// (narrow codes) items; the bit width is uniform per workgroup.
+template <int RB>
+__global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   KArgs& A = kernel_args();
-  const int item = item_begin + blockIdx.x;
+  const int item = blockIdx.x;
   const int ei = find_entry(A, item);
   KEntry& E = A.entries[ei];
   // item numbering: chunks of one (sequence, split) pair sit 8 blocks apart, so
@@ -607,7 +701,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs, int ite
     j = 8 * q8 + rem % r8;
   }
   const int s = j / E.splits, ks = j - s * E.splits;
-  run_item<BITS, RB>(A, E, s, ks, chunk, lds);
+  switch (E.bits) {
+    case 2: run_item<2, RB>(A, E, s, ks, chunk, lds); break;
+    case 4: run_item<4, RB>(A, E, s, ks, chunk, lds); break;
+    case 8: run_item<8, RB>(A, E, s, ks, chunk, lds); break;
+    default: run_item<16, RB>(A, E, s, ks, chunk, lds); break;
+  }
 }
 
 // Merge the split partials of one (entry, sequence, chunk) in a fixed order.
@@ -657,41 +756,37 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs) {
   }
 }
 
-template <int BITS, int RB>
-hipError_t launch_one(const DecodeArgs& a, int begin, int n, int lds, hipStream_t stream) {
-  hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<BITS, RB>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+template <int RB>
+hipError_t launch_one(const DecodeArgs& a, int n, int lds, hipStream_t stream) {
+  hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<RB>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_kernel<BITS, RB>), dim3(n), dim3(kThreads), lds, stream, a, begin);
+  hipLaunchKernelGGL((decode_kernel<RB>), dim3(n), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
-}
-
-template <int BITS>
-hipError_t launch_bits(const DecodeArgs& a, int rb, int begin, int n, int lds, hipStream_t stream) {
-  switch (rb) {
-    case 1: return launch_one<BITS, 1>(a, begin, n, lds, stream);
-    case 2: return launch_one<BITS, 2>(a, begin, n, lds, stream);
-    case 3: return launch_one<BITS, 3>(a, begin, n, lds, stream);
-    default: return launch_one<BITS, 4>(a, begin, n, lds, stream);
-  }
 }
 
 }  // namespace
 
+// Tile buffers per workgroup: as many as fit in the workgroup's share of the
+// 160 KB LDS, 2 to 8.
+int decode_nbuf(int row_stride, int K, int bits) {
+  const int budget = 160 * 1024 / decode_wg_per_cu(bits) - kPbufBytes - kMiscBytes;
+  const int n = budget / tilebuf_bytes(row_stride, K, bits);
+  return n < 2 ? 2 : (n > 8 ? 8 : n);
+}
+
 int decode_lds_bytes(int row_stride, int K, int bits) {
-  return 2 * tilebuf_bytes(row_stride, K, bits) + kPbufBytes + kMiscBytes;
+  return decode_nbuf(row_stride, K, bits) * tilebuf_bytes(row_stride, K, bits) + kPbufBytes + kMiscBytes;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t stream) {
   static_assert(sizeof(DecodeArgs) < 7600, "kernel argument block too large");
-  for (int c = 0; c < 4; ++c) {
-    const int n = L.item_end[c] - L.item_begin[c];
-    if (n <= 0) continue;
+  if (L.items > 0) {
     hipError_t e;
-    switch (c) {
-      case 0: e = launch_bits<2>(a, L.row_blocks, L.item_begin[c], n, L.lds_bytes[c], stream); break;
-      case 1: e = launch_bits<4>(a, L.row_blocks, L.item_begin[c], n, L.lds_bytes[c], stream); break;
-      case 2: e = launch_bits<8>(a, L.row_blocks, L.item_begin[c], n, L.lds_bytes[c], stream); break;
-      default: e = launch_bits<16>(a, L.row_blocks, L.item_begin[c], n, L.lds_bytes[c], stream); break;
+    switch (L.row_blocks) {
+      case 1: e = launch_one<1>(a, L.items, L.lds_bytes, stream); break;
+      case 2: e = launch_one<2>(a, L.items, L.lds_bytes, stream); break;
+      case 3: e = launch_one<3>(a, L.items, L.lds_bytes, stream); break;
+      default: e = launch_one<4>(a, L.items, L.lds_bytes, stream); break;
     }
     if (e != hipSuccess) return e;
   }

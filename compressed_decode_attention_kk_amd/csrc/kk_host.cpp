@@ -61,6 +61,13 @@ struct Plan {
 
 int bits_class(int bits) { return bits == 2 ? 0 : bits == 4 ? 1 : bits == 8 ? 2 : 3; }
 
+// Relative time of one 32-token tile of one work item: about equal for 2-, 4-
+// and 8-bit codes (fixed per-tile work dominates), up to 1.7x for 16-bit codes,
+// which stream 2-8x the bytes (measured on MI355X).
+int64_t tile_cost(int bits, int d) { return 10 + (bits == 16 ? (7 * d + 511) / 512 : 0); }
+constexpr int kItemWaves = 3;       // waves of items over the resident slots
+constexpr int kMinSplitTiles = 8;   // no split shorter than 8 tiles (256 tokens)
+
 // Work plan of one decode step.  Groups: an anchor and the layers inheriting
 // its cache.  Each group's query rows (layer-major, head-minor) form entries of
 // <= 512 rows cut into chunks of <= 64 rows; an item is (chunk, seq, split).
@@ -91,7 +98,8 @@ kk_status make_plan(const kk_model_cfg* c, int batch, int max_len, int split_tok
   struct Ent {
     kk::EntryArg e;
     int anchor;
-    int64_t bytes_item;
+    int64_t cost_tile;     // relative time of one 32-token tile of one item
+    int key_num, key_den;  // position of the entry in its bit width's order
   };
   std::vector<Ent> ents;
   // Row chunks: RB blocks of 16 rows per item, RB fixed by the head count; when
@@ -117,59 +125,76 @@ kk_status make_plan(const kk_model_cfg* c, int batch, int max_len, int split_tok
       E.e.chunk_rows = (int16_t)chunk_rows;
       E.e.lay_begin = (int16_t)begin;
       E.anchor = a;
-      E.bytes_item = (int64_t)max_len * (E.e.row_stride + 4);
+      E.cost_tile = tile_cost(E.e.bits, E.e.d);
       ents.push_back(E);
     }
   }
   if ((int)ents.size() > kk::kMaxEntries) return KK_ERR_UNSUPPORTED;
 
-  // Splits: each bit width runs as its own launch, so items are sized per bit
-  // width to give every launch about two waves of items over the resident
-  // workgroup slots (at least 256 KB of cache per item).
-  int64_t class_bytes[4] = {0, 0, 0, 0};
-  for (auto& E : ents) class_bytes[bits_class(E.e.bits)] += E.bytes_item * E.e.nrc * batch;
+  // Splits: one launch runs every item, so items are sized by estimated time:
+  // about kItemWaves waves of items over the resident workgroup slots, each at
+  // least kMinSplitTiles tiles long.  Unsplit items need no merge pass.
   const int max_tiles = std::max(1, (max_len + kk::kTile - 1) / kk::kTile);
+  int64_t total_cost = 0;
+  for (auto& E : ents) total_cost += E.cost_tile * max_tiles * E.e.nrc * batch;
+  const int64_t slots = (int64_t)kk::kCUs * kk::decode_wg_per_cu(0);
+  const int64_t target = std::max<int64_t>(1, total_cost / (kItemWaves * slots));
   for (auto& E : ents) {
-    const int64_t target = std::max<int64_t>(class_bytes[bits_class(E.e.bits)] / (2 * kk::kPlanSlots), 256 * 1024);
     int64_t sp;
     if (split_tokens > 0) sp = (max_len + split_tokens - 1) / split_tokens;
-    else sp = (E.bytes_item + target - 1) / target;
+    else sp = (E.cost_tile * max_tiles + target - 1) / target;
+    if (split_tokens <= 0) sp = std::min<int64_t>(sp, std::max(1, max_tiles / kMinSplitTiles));
     sp = std::max<int64_t>(1, std::min<int64_t>(sp, max_tiles));
     sp = std::min<int64_t>(sp, kk::kMaxMergeSplits);
     E.e.splits = (int16_t)sp;
   }
+  // Order: within a bit width, longest items first; the widths are interleaved
+  // in proportion to their entry counts, so that the workgroups resident at
+  // any time mix bandwidth-bound and arithmetic-bound items.
   std::stable_sort(ents.begin(), ents.end(), [](const Ent& x, const Ent& y) {
     if (x.e.bits != y.e.bits) return x.e.bits < y.e.bits;
-    return x.bytes_item / x.e.splits > y.bytes_item / y.e.splits;
+    return x.cost_tile * y.e.splits > y.cost_tile * x.e.splits;
   });
+  {
+    int count[4] = {0, 0, 0, 0}, seen[4] = {0, 0, 0, 0};
+    for (auto& E : ents) ++count[bits_class(E.e.bits)];
+    for (auto& E : ents) {
+      const int cl = bits_class(E.e.bits);
+      E.key_num = 2 * seen[cl]++ + 1;
+      E.key_den = 2 * count[cl];
+    }
+    std::stable_sort(ents.begin(), ents.end(), [](const Ent& x, const Ent& y) {
+      return (int64_t)x.key_num * y.key_den < (int64_t)y.key_num * x.key_den;
+    });
+  }
   int64_t items = 0, ws = 0;
   int merges = 0;
   kk::DecodeLaunch& Lc = P.launch;
-  for (int c = 0; c < 4; ++c) Lc.item_begin[c] = Lc.item_end[c] = Lc.lds_bytes[c] = 0;
+  Lc.items = 0;
+  Lc.lds_bytes = 0;
   for (size_t i = 0; i < ents.size(); ++i) {
     kk::EntryArg& e = ents[i].e;
     e.merge_base = 0;
     e.codes = nullptr;
     e.scales = nullptr;
-    e.item_base = (int32_t)items;
-    const int cls = bits_class(e.bits);
-    if (Lc.item_end[cls] == Lc.item_begin[cls]) Lc.item_begin[cls] = (int)items;
+    e.item_base = (int32_t)std::min<int64_t>(items, 0x7fffffff);
     items += (int64_t)e.nrc * batch * e.splits;
-    Lc.item_end[cls] = (int)std::min<int64_t>(items, 0x7fffffff);
     if (e.splits > 1) {
       e.ws_off = ws;
       ws += (int64_t)e.nrc * batch * e.splits * kk::partial_slot_floats(e.d);
       e.merge_base = merges;
       merges += e.nrc * batch;
     }
-    Lc.lds_bytes[cls] = std::max(Lc.lds_bytes[cls], kk::decode_lds_bytes(e.row_stride, e.d + c->d_rope, e.bits));
-    if (Lc.lds_bytes[cls] > 160 * 1024) return KK_ERR_UNSUPPORTED;
+    e.nbuf = (int16_t)kk::decode_nbuf(e.row_stride, e.d + c->d_rope, e.bits);
+    Lc.lds_bytes = std::max(Lc.lds_bytes, kk::decode_lds_bytes(e.row_stride, e.d + c->d_rope, e.bits));
+    if (Lc.lds_bytes > 160 * 1024 / kk::decode_wg_per_cu(0)) return KK_ERR_UNSUPPORTED;
     A.entries[i] = e;
     P.entry_anchor[i] = ents[i].anchor;
   }
   if (items > 0x7fffffff) return KK_ERR_UNSUPPORTED;
   A.n_entries = (int32_t)ents.size();
   A.total_items = (int32_t)items;
+  Lc.items = (int)items;
   Lc.merge_blocks = merges;
   P.ws_floats = ws;
   return KK_OK;

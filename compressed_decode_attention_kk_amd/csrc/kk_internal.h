@@ -14,10 +14,13 @@ constexpr int kTile = 32;            // cached tokens per pipeline stage
 constexpr int kMaxRowBlocks = 4;     // 16-row MFMA blocks per work item (<= 64 query rows)
 constexpr int kMaxUnitsPerWave = 4;  // 32-feature output units per wave in P.V (d <= 512)
 constexpr int kMaxMergeSplits = 64;  // token splits of one sequence
-constexpr int kMaxK = 640;           // d + d_R (the ABI limit)
+constexpr int kMaxK = 576;           // d + d_R (the ABI limit)
 constexpr int kMaxEntries = 96;      // group entries per launch
 constexpr int kMaxLayers = 64;
-constexpr int kPlanSlots = 2 * 256;  // workgroups resident at once on 256 CUs (split policy)
+constexpr int kCUs = 256;
+// Decode workgroups per CU (the same for every bit width: a second workgroup
+// hides the per-item and per-tile fixed latencies of the first).
+constexpr int decode_wg_per_cu(int) { return 2; }
 constexpr float kLazyRescale = 8.0f; // log2 headroom before the running max is moved
 
 // One layer: softmax scale, kept width of its anchor and the float offset of
@@ -42,6 +45,7 @@ struct EntryArg {
   int16_t d, bits;
   int16_t nrc, chunk_rows;
   int16_t splits, lay_begin;
+  int16_t nbuf, pad_;    // LDS tile buffers of this entry (nbuf - 1 tiles in flight)
 };
 
 struct DecodeArgs {
@@ -73,13 +77,15 @@ struct WriteArgs {
 };
 
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
-// Per bit-width launch ranges (class c: bits 2 << c): items [item_begin, item_end).
+// One decode launch covers every work item of the step (all bit widths).
 struct DecodeLaunch {
-  int item_begin[4], item_end[4], lds_bytes[4];
+  int items;
+  int lds_bytes;         // dynamic LDS per workgroup: the largest entry's need
   int row_blocks;        // 16-row MFMA blocks per item (1..4), uniform for the step
   int merge_blocks;
 };
 
+int decode_nbuf(int row_stride, int K, int bits);
 int decode_lds_bytes(int row_stride, int K, int bits);
 hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t stream);
 

@@ -70,7 +70,7 @@ typedef enum { KK_DTYPE_F32 = 0, KK_DTYPE_BF16 = 1 } kk_dtype;
 /* Build limits (KK_ERR_UNSUPPORTED beyond them). */
 #define KK_MAX_LAYERS 64
 #define KK_MAX_D 512           /* kept latent width d (and r >= d, any r) */
-#define KK_MAX_K 640           /* d + d_R */
+#define KK_MAX_K 576           /* d + d_R (512 + 64, the MLA shape) */
 
 /* One layer's action ("Action Space and Cost Model").
  *   anchor == own index : the layer is an anchor with action (d, bits);

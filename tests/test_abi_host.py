@@ -94,6 +94,8 @@ def test_validate_model_rules(kk):
     assert status(kk, table([[0, 576, 4]], r=640, dr=64, kk=kk)) == kk.KK_ERR_UNSUPPORTED      # d > 512
     assert status(kk, table([[0, 64, 4]], dr=144, kk=kk)) == kk.KK_ERR_UNSUPPORTED             # d_R > 128
     assert status(kk, table([[0, 64, 4]], dr=24, kk=kk)) == kk.KK_ERR_UNSUPPORTED              # d_R % 16
+    assert status(kk, table([[0, 512, 4]], dr=80, kk=kk)) == kk.KK_ERR_UNSUPPORTED             # d + d_R > 576
+    assert status(kk, table([[0, 448, 4]], dr=128, kk=kk)) == kk.KK_OK                         # d + d_R = 576
     m = table([[0, 64, 4]], kk=kk)
     m._arr[0].sm_scale = float("nan")
     assert status(kk, m) == kk.KK_ERR_INVALID_ARGUMENT
