@@ -8,9 +8,20 @@ d_R = 64, batch 32, 8192 cached tokens per sequence) with the caches, queries
 and sequence lengths already resident in HBM.  Prints one JSON line.
 
 roofline.achieved = algorithmic bytes of one step / mean device time of one
-step (HIP events on the launch stream).  Algorithmic bytes U = anchor caches
-once (rows + scales) + the d_eff + d_R query values read per layer + the fp32
-outputs written.
+step (HIP events on the launch stream; a step is the decode launch plus the
+small split-merge launch).  Algorithmic bytes U = anchor caches once (rows +
+scales) + the d_eff + d_R query values read per layer + the fp32 outputs
+written.
+
+roofline.traffic (HBM bytes per step) comes from two rocprofv3 counter passes
+over this same command with --calibration-copy-mib: FETCH_SIZE, then
+WRITE_SIZE.  Each counter is scaled by what it reads for a device-to-device
+copy of known size, and the result is stored with a digest of the kernel
+sources by
+
+    python bench.py --traffic-from FETCH.csv WRITE.csv
+
+It is reported as null when the kernel sources have changed since.
 """
 
 from __future__ import annotations
@@ -67,6 +78,48 @@ def stored_traffic(workload_name):
     return rec.get("hbm_bytes_per_step")
 
 
+DECODE_KERNELS = ("decode_kernel", "merge_kernel")
+COPY_KERNEL = "copyBuffer"
+
+
+def _counter_rows(path, counter):
+    import csv
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            key = r["Dispatch_Id"]
+            rows.setdefault(key, [r["Kernel_Name"], 0.0])
+            rows[key][1] += float(r["Counter_Value"])
+    return list(rows.values())
+
+
+def traffic_from(fetch_csv, write_csv, copy_mib, workload_name):
+    """HBM bytes per step from rocprofv3 FETCH_SIZE / WRITE_SIZE passes (KiB per
+    dispatch), each calibrated on the copies of known size in the same run."""
+    out = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, name)
+        copies = [v for k, v in rows if COPY_KERNEL in k and v * 1024 > 0.5 * copy_mib * 2 ** 20]
+        if not copies:
+            raise SystemExit(f"no calibration copy dispatch found in {path}")
+        factor = copy_mib * 2 ** 20 / (sum(copies) / len(copies) * 1024)
+        dec = [(k, v) for k, v in rows if any(n in k for n in DECODE_KERNELS)]
+        n_steps = sum(1 for k, _ in dec if DECODE_KERNELS[0] in k)      # one decode launch per step
+        per_step = sum(v for _, v in dec) * 1024 / max(n_steps, 1)
+        out[name] = {"raw_bytes_per_step": per_step, "copy_factor": factor, "bytes_per_step": per_step * factor,
+                     "steps": n_steps, "decode_and_merge_dispatches": len(dec), "copy_dispatches": len(copies)}
+    rec = {"workload": workload_name, "kernel_source_sha256": kernel_source_digest(),
+           "hbm_bytes_per_step": out["FETCH_SIZE"]["bytes_per_step"] + out["WRITE_SIZE"]["bytes_per_step"],
+           "counters": out, "calibration_copy_mib": copy_mib,
+           "method": "rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE, over bench.py --steps 3 --warmup 1 "
+                     "--no-cpu-baseline --calibration-copy-mib M; sum over the decode_kernel and merge_kernel "
+                     "dispatches / number of decode_kernel dispatches, each counter scaled by the copy bytes / "
+                     "the counter bytes of the copies"}
+    return rec
+
+
 def cpu_baseline(w, budget_s: float):
     """The oracle (unchanged) on the host cores: decode of whole (layer, sequence)
     pairs of the same workload until the time budget is used."""
@@ -115,7 +168,21 @@ def main():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="after timing, run 3 device-to-device copies of this size (counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic record from two rocprofv3 counter CSVs and exit")
     args = ap.parse_args()
+    if args.traffic_from:
+        import synth
+        w = synth.workload(args.workload)
+        rec = traffic_from(args.traffic_from[0], args.traffic_from[1], args.calibration_copy_mib or 1024, w.name)
+        path = os.path.join(ROOT, "profiles", f"decode_{w.name}_hbm_traffic.json")
+        os.makedirs(os.path.dirname(path), exist_ok=True)
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        print(json.dumps(rec))
+        return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (the decode path has no multi-GPU mode); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -158,6 +225,16 @@ def main():
     mean_dev_ms = sum(dev_ms) / len(dev_ms)
     ms_per_step = wall * 1000.0 / args.steps
 
+    if args.calibration_copy_mib > 0:
+        n = args.calibration_copy_mib * 2 ** 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     U, cache_bytes = algorithmic_bytes(kk, w, model)
     flops = useful_flops(w)
     achieved = U / (mean_dev_ms * 1e-3) / 1e9
@@ -190,7 +267,8 @@ def main():
                    "cached_tokens": w.seq_len, "r": w.r, "d_rope": w.d_rope, "anchors": len(anchors),
                    "bits_per_token": bits_tok, "q_dtype": str(w.q_dtype).replace("torch.", ""),
                    "split_tokens": args.split_tokens or "auto", "parallelism": "none (one GPU)"},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+        "roofline": {"bound": "hbm", "kernel": "decode step: decode_kernel + merge_kernel",
+                     "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_step": U, "device_ms_per_step": mean_dev_ms,
                      "useful_tflops": flops / (mean_dev_ms * 1e-3) / 1e12},
