@@ -39,6 +39,7 @@ namespace {
 
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef int i4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
@@ -59,19 +60,23 @@ constexpr int kScaleHeadroom = 6;    // scales may exceed 2^E by 2^6 before E is
 constexpr int kMaxChunks64 = (kMaxK + 63) / 64;
 
 // ---- LDS map (bytes, dynamic shared memory) ----------------------------------
-//  [0, 2*buf)   two tile buffers: codes of token block 0 | block 1 | slack | 128 B scales
-//  pbuf         P' fragments [row block][64 lanes] h8
-//  alpha[64] flags[4] ml[64][2] misc[16]
-constexpr int kPbufBytes = kMaxRowBlocks * 64 * 16;
-constexpr int kMiscBytes = 64 * 4 + 16 + 64 * 8 + 64;
+//  [0, nbuf*buf)  tile buffers: codes of token block 0 [| block 1] | slack | scales
+//  pbuf           P' fragments [tile parity][row block][64 lanes] 16 B
+//  alpha[2][64] flags[2][4] ml[64][2] misc[16]
+constexpr int kPbufBytes = 2 * kMaxRowBlocks * 64 * 16;
+constexpr int kMiscBytes = 2 * 64 * 4 + 2 * 4 * 4 + 64 * 8 + 64;
 
 __host__ __device__ inline int nseg_of(int row_stride) { return row_stride >> 4; }
 __host__ __device__ inline int chunks64_of(int K) { return (K + 63) >> 6; }
 // 16-byte segments read by the Q.K chunks (whole 64-feature chunks)
 __host__ __device__ inline int nsegpad_of(int K, int bits) { return (chunks64_of(K) * bits + 1) >> 1; }
+// 16-token blocks per tile (see tile_blocks below)
+__host__ __device__ inline int tile_blocks_of(int bits) { return bits == 16 ? 1 : 2; }
+// Tile buffer: all but the last token block at full pitch, the last one padded
+// for whole-chunk Q.K reads, then 256 bytes for the scales.
 __host__ __device__ inline int tilebuf_bytes(int row_stride, int K, int bits) {
   const int nseg = nseg_of(row_stride), pad = nsegpad_of(K, bits);
-  return (nseg + (pad > nseg ? pad : nseg)) * 256 + 256;
+  return ((tile_blocks_of(bits) - 1) * nseg + (pad > nseg ? pad : nseg)) * 256 + 256;
 }
 
 // ---- operand conversions ------------------------------------------------------
@@ -225,34 +230,58 @@ __device__ inline int isum_xor_16_32(int v) {
 __device__ inline int tile_off(int pitch, int tb, int seg, int t) { return tb * pitch + seg * 256 + ((t ^ (tb << 2)) << 4); }
 
 // ---- per-item decode ----------------------------------------------------------
-// BITS: the anchor's bit width; RB: 16-row MFMA blocks per item (uniform for a
-// launch, it follows from the head count).
+// Tiles hold 2 token blocks of 16 (32 tokens) for b <= 8 and 1 block (16
+// tokens) for b = 16, whose rows are up to 8x longer, so that every entry keeps
+// three or more tiles in LDS (two in use, the rest in flight).
+template <int BITS>
+constexpr int tile_blocks() { return BITS == 16 ? 1 : 2; }
+static_assert(tile_blocks<16>() == 1 && tile_blocks<8>() == 2, "tile_blocks and tile_blocks_of differ");
+
+// P.V output units (32 features) per wave.  Q.K waves take a few units; the
+// waves without Q.K rows take the rest, so that no wave idles while Q.K runs.
+template <int RB>
+constexpr int qk_units_max() { return RB >= kWaves ? 4 : 3; }
+template <int RB>
+constexpr int pv_units_max() { return RB == 3 ? 7 : 5; }
+
+__device__ inline f4 mfma_f16_k16(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
+
+// 4 int16 codes (w0, w1 little-endian) -> signed high bytes and low bytes / 256 as fp16.
+__device__ inline void cvt_b16_4(u2 w, h4& hi, h4& lo) {
+  const h2 bh = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  const h2 bl = {(_Float16)-4.0f, (_Float16)-4.0f};
+  const uint32_t x0 = w[0] ^ 0x80008000u, x1 = w[1] ^ 0x80008000u;
+  const h2 a0 = as_h2(perm(0x64646464u, x0, 0x04030401u)) + bh, a1 = as_h2(perm(0x64646464u, x1, 0x04030401u)) + bh;
+  const h2 b0 = as_h2(perm(0x44444444u, w[0], 0x04020400u)) + bl, b1 = as_h2(perm(0x44444444u, w[1], 0x04020400u)) + bl;
+  hi = h4{a0[0], a0[1], a1[0], a1[1]};
+  lo = h4{b0[0], b0[1], b1[0], b1[1]};
+}
+
+// One work item: a chunk of <= 16*RB query rows of one anchor group, one
+// sequence, one token split.  Stage st (st = -1 .. ntiles-1) runs Q.K and the
+// softmax of tile st+1 on the Q.K waves and P.V of tile st on every wave, with
+// one barrier per stage (P.V first, so that after its rescale branch the two
+// halves form one region the compiler can interleave); P', the rescale factors
+// and the flags are double buffered by tile parity.
 template <int BITS, int RB>
-__device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char* lds) {
-  constexpr int NUW = kMaxUnitsPerWave;
+__device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char* lds) {
+  constexpr int TB = tile_blocks<BITS>();
+  constexpr int TILE = 16 * TB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, n = lane & 15;
   const int d = E.d, K = d + A.d_rope, KC = chunks64_of(K);
   const int NSEG = nseg_of(E.row_stride), PITCH = NSEG * 256;
   const int bufbytes = tilebuf_bytes(E.row_stride, K, BITS);
-  const int nbuf = E.nbuf;                    // tile buffers; nbuf - 1 tiles are in flight
-  char* pbuf = lds + nbuf * bufbytes;
-  float* alpha_lds = (float*)(pbuf + kPbufBytes);
-  int* flag_lds = (int*)(alpha_lds + 64);
-  float* ml_lds = (float*)(flag_lds + 4);
+  const int nbuf = E.nbuf;                    // >= 3 tile buffers
+  char* pbuf = lds + nbuf * bufbytes;         // [2][kMaxRowBlocks][64 lanes] 16 B
+  float* alpha_lds = (float*)(pbuf + kPbufBytes);   // [2][64]
+  int* flag_lds = (int*)(alpha_lds + 128);          // [2][4]
+  float* ml_lds = (float*)(flag_lds + 8);           // [64][2]
   int* misc_lds = (int*)(ml_lds + 128);
 
   // rows of this chunk (at most 16 * RB); wave < RB owns rows 16*wave + n
   const int r0 = E.row_begin + chunk * E.chunk_rows;
   const int nrows = min(E.chunk_rows, E.row_end - r0);
-  const bool qk_wave = wave < RB;
-  const int my_row = 16 * wave + n;
-  int my_layer = -1, my_head = 0;
-  if (qk_wave && my_row < nrows) {
-    const int gr = r0 + my_row;
-    my_layer = A.group_layers[E.lay_begin + gr / A.heads];
-    my_head = gr % A.heads;
-  }
 
   // token range of this split
   int len = A.seq_lens[s];
@@ -261,28 +290,28 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
   const int t0 = ksplit * tps;
   const int t1 = min(len, t0 + tps);
   const int ntok = t1 > t0 ? t1 - t0 : 0;
-  const int ntiles = (ntok + kTile - 1) / kTile;
+  const int ntiles = (ntok + TILE - 1) / TILE;
   const int64_t row0 = (int64_t)s * A.t_cap + t0;    // first cache row of this item
 
   // ---- tile loader: direct HBM -> LDS copies ---------------------------------------
   // Every wave issues the same number of copy instructions for every tile
-  // (rows past the valid tokens re-read the last valid row), so "tile `it` has
+  // (rows past the valid tokens re-read the last valid row), so "tile t has
   // landed" is a fixed count of this wave's outstanding copies.
   const uint8_t* codes = E.codes;
   const float* scales = E.scales;
   const int block_pieces = NSEG * 16;
-  const int npos = 2 * block_pieces;             // 16-byte pieces of codes in a tile
+  const int npos = TB * block_pieces;            // 16-byte pieces of codes in a tile
   const int ninst = (npos + 63) >> 6;            // 64-lane copy instructions per tile
   // this wave's copy instructions per tile (wave-uniform, so the waits below are scalar code)
   const int copies = __builtin_amdgcn_readfirstlane((ninst > wave ? (ninst - wave + kWaves - 1) / kWaves : 0) +
                                                     (wave == kWaves - 1 ? 1 : 0));
   auto issue_tile = [&](int it, int slotb) {
     char* buf = lds + slotb * bufbytes;
-    const int tok0 = it * kTile;
-    const int tlast = min(kTile, ntok - tok0) - 1;
+    const int tok0 = it * TILE;
+    const int tlast = min(TILE, ntok - tok0) - 1;
     for (int i = wave; i < ninst; i += kWaves) {
       const int p = i * 64 + lane;
-      const int tb = p >= block_pieces ? 1 : 0;
+      const int tb = (TB == 2 && p >= block_pieces) ? 1 : 0;
       const int rem = p - tb * block_pieces;
       const int seg = rem >> 4, slot = rem & 15;
       const int t = min(16 * tb + (slot ^ (tb << 2)), tlast);
@@ -291,373 +320,425 @@ __device__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char
         copy16_to_lds(gp, lds_addr(buf + i * 1024));
       }
     }
-    if (wave == kWaves - 1 && lane < kTile) {
-      copy4_to_lds(scales + row0 + tok0 + min(lane, tlast), lds_addr(buf + 2 * PITCH));
+    if (wave == kWaves - 1 && lane < TILE) {
+      copy4_to_lds(scales + row0 + tok0 + min(lane, tlast), lds_addr(buf + TB * PITCH));
     }
   };
-  const int depth = nbuf - 1;
-  for (int it = 0; it < depth && it < ntiles; ++it) issue_tile(it, it);
+  // prologue: tiles 0 .. nbuf-3; stage st issues tile st + nbuf - 1
+  for (int it = 0; it < nbuf - 2 && it < ntiles; ++it) issue_tile(it, it);
 
-  // ---- q as two int8 limbs of a 14-bit fixed-point number per row ------------------
-  // chunk c, lane (g, n): row 16*wave + n, features 64c + 16g + qk_slot_feature(i).
-  i4 qh[kMaxChunks64], ql[kMaxChunks64];
-  int qsum = 0;                                 // sum of the fixed-point q of this row
-  float rowf = 0.0f;
-  {
-    float qv[kMaxChunks64][16];
-    float mx = 0.0f;
+  // ---- P.V output units of this wave ---------------------------------------------
+  const int NU = (d + 31) >> 5;
+  int ubase, ucount;
+  if (RB >= kWaves) {
+    const int per = (NU + kWaves - 1) / kWaves;
+    ubase = wave * per;
+    ucount = max(0, min(per, NU - ubase));
+  } else {
+    const int npv = kWaves - RB;
+    int uq = max((NU * 3) / 16, (NU - npv * pv_units_max<RB>() + RB - 1) / RB);
+    uq = min(max(uq, 0), qk_units_max<RB>());
+    const int rest = NU - RB * uq;
+    const int per = (rest + npv - 1) / npv;
+    if (wave < RB) {
+      ubase = wave * uq;
+      ucount = uq;
+    } else {
+      ubase = RB * uq + (wave - RB) * per;
+      ucount = max(0, min(per, rest - (wave - RB) * per));
+    }
+  }
+
+  float m_run = -INFINITY, l_lane = 0.0f;     // softmax state of row 16*wave + n (Q.K waves)
+  int Ecur = -1000;                            // scales so far are <= 2^(Ecur + headroom)
+
+  // The stage loop of one wave role.  QKW: this wave owns Q.K rows; UMAX: its
+  // largest unit count (each role is register-allocated for its own arrays).
+  auto pipeline = [&](auto qkw_tag, auto umax_tag) {
+    constexpr bool QKW = decltype(qkw_tag)::value;
+    constexpr int UMAX = decltype(umax_tag)::value;
+    const int my_row = 16 * wave + n;
+
+    // ---- q as two int8 limbs of a 14-bit fixed-point number per row ------------------
+    // chunk c, lane (g, n): row 16*wave + n, features 64c + 16g + qk_slot_feature(i).
+    i4 qh[QKW ? kMaxChunks64 : 1], ql[QKW ? kMaxChunks64 : 1];
+    float rowf = 0.0f;
+    int qbias = 0;
+    if constexpr (QKW) {
+      int my_layer = -1, my_head = 0;
+      if (my_row < nrows) {
+        const int gr = r0 + my_row;
+        my_layer = A.group_layers[E.lay_begin + gr / A.heads];
+        my_head = gr % A.heads;
+      }
+      int qsum = 0;                               // sum of the fixed-point q of this row
+      float qv[kMaxChunks64][16];
+      float mx = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks64; ++c) {
-      const int f0 = 64 * c + 16 * g;
+      for (int c = 0; c < kMaxChunks64; ++c) {
+        const int f0 = 64 * c + 16 * g;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) qv[c][i] = 0.0f;
-      if (my_layer >= 0 && f0 < K) {
-        const int64_t qrow = ((int64_t)my_layer * A.batch + s) * A.heads + my_head;
-        const bool lat = f0 < d;
-        const int64_t off = lat ? qrow * A.r + f0 : qrow * A.d_rope + (f0 - d);
-        const void* base = lat ? A.q_lat : A.q_rope;
-        float x[16];
-        if (A.q_is_f32) {
-          const f4* p = (const f4*)((const float*)base + off);
+        for (int i = 0; i < 16; ++i) qv[c][i] = 0.0f;
+        if (my_layer >= 0 && f0 < K) {
+          const int64_t qrow = ((int64_t)my_layer * A.batch + s) * A.heads + my_head;
+          const bool lat = f0 < d;
+          const int64_t off = lat ? qrow * A.r + f0 : qrow * A.d_rope + (f0 - d);
+          const void* base = lat ? A.q_lat : A.q_rope;
+          float x[16];
+          if (A.q_is_f32) {
+            const f4* p = (const f4*)((const float*)base + off);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const f4 a = p[v];
+            for (int v = 0; v < 4; ++v) {
+              const f4 a = p[v];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x[4 * v + i] = a[i];
-          }
-        } else {
-          const u4* p = (const u4*)((const uint16_t*)base + off);
+              for (int i = 0; i < 4; ++i) x[4 * v + i] = a[i];
+            }
+          } else {
+            const u4* p = (const u4*)((const uint16_t*)base + off);
 #pragma unroll
-          for (int v = 0; v < 2; ++v) {
-            const u4 w = p[v];
+            for (int v = 0; v < 2; ++v) {
+              const u4 w = p[v];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              x[8 * v + 2 * i] = __uint_as_float(w[i] << 16);
-              x[8 * v + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+              for (int i = 0; i < 4; ++i) {
+                x[8 * v + 2 * i] = __uint_as_float(w[i] << 16);
+                x[8 * v + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+              }
             }
           }
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            qv[c][i] = x[qk_slot_feature<BITS>(i)];
+            mx = fmaxf(mx, fabsf(x[i]));
+          }
         }
+      }
+      mx = max_xor_16_32(mx);
+      int e = 0;
+      if (mx > 0.0f) (void)frexpf(mx, &e);          // mx * 2^-e in [0.5, 1)
+      const float pre = ldexpf(1.0f, kQFrac - e);
+#pragma unroll
+      for (int c = 0; c < kMaxChunks64; ++c) {
+        uint32_t hw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          qv[c][i] = x[qk_slot_feature<BITS>(i)];
-          mx = fmaxf(mx, fabsf(x[i]));
+          const int qi = (int)rintf(qv[c][i] * pre);    // |qi| <= 8192
+          const int hi = (qi + 64) >> 7;                // floor division, in [-64, 64]
+          const int lo = qi - (hi << 7);                // in [-64, 63]
+          qsum += qi;
+          hw[i >> 2] |= ((uint32_t)hi & 0xFFu) << (8 * (i & 3));
+          lw[i >> 2] |= ((uint32_t)lo & 0xFFu) << (8 * (i & 3));
         }
+        qh[c] = i4{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3]};
+        ql[c] = i4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
       }
+      qsum = isum_xor_16_32(qsum);
+      if (my_layer >= 0) rowf = A.layers[my_layer].sm_scale * kLog2e * ldexpf(1.0f, e - kQFrac);
+      // offset-binary bias of the Q.K operand (exact integer correction)
+      qbias = BITS == 4 ? 8 * qsum : BITS == 2 ? 2 * qsum : BITS == 16 ? 128 * qsum : 0;
     }
-    mx = max_xor_16_32(mx);
-    int e = 0;
-    if (mx > 0.0f) (void)frexpf(mx, &e);          // mx * 2^-e in [0.5, 1)
-    const float pre = ldexpf(1.0f, kQFrac - e);
-#pragma unroll
-    for (int c = 0; c < kMaxChunks64; ++c) {
-      uint32_t hw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qi = (int)rintf(qv[c][i] * pre);    // |qi| <= 8192
-        const int hi = (qi + 64) >> 7;                // floor division, in [-64, 64]
-        const int lo = qi - (hi << 7);                // in [-64, 63]
-        qsum += qi;
-        hw[i >> 2] |= ((uint32_t)hi & 0xFFu) << (8 * (i & 3));
-        lw[i >> 2] |= ((uint32_t)lo & 0xFFu) << (8 * (i & 3));
-      }
-      qh[c] = i4{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3]};
-      ql[c] = i4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
-    }
-    qsum = isum_xor_16_32(qsum);
-    if (my_layer >= 0) rowf = A.layers[my_layer].sm_scale * kLog2e * ldexpf(1.0f, e - kQFrac);
-  }
-  // offset-binary bias of the Q.K operand (exact integer correction)
-  const int qbias = BITS == 4 ? 8 * qsum : BITS == 2 ? 2 * qsum : BITS == 16 ? 128 * qsum : 0;
 
-  // ---- accumulators and softmax state -----------------------------------------------
-  f4 oacc[NUW][2][RB];
+    f4 oacc[UMAX][2][RB];
 #pragma unroll
-  for (int u = 0; u < NUW; ++u)
+    for (int u = 0; u < UMAX; ++u)
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+      for (int f = 0; f < 2; ++f)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) oacc[u][f][rb] = f4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_lane = 0.0f;     // softmax state of row 16*wave + n
-  int Ecur = -1000;                            // scales of the item so far are <= 2^(Ecur + headroom)
-  const int NU = (d + 31) >> 5;               // 32-feature output units
-  const int my_units = NU > wave ? (NU - wave + kWaves - 1) / kWaves : 0;
+        for (int rb = 0; rb < RB; ++rb) oacc[u][f][rb] = f4{0.f, 0.f, 0.f, 0.f};
 
-  int cur = 0;                                  // buffer of tile `it`
-  for (int it = 0; it < ntiles; ++it) {
-    vm_wait(min(depth - 1, ntiles - 1 - it) * copies);   // this wave's copies of tile `it` have landed
-    lds_barrier();                              // (A) tile visible to all; previous P.V finished
-    if (it + depth < ntiles) issue_tile(it + depth, cur == 0 ? nbuf - 1 : cur - 1);
-    const char* buf = lds + cur * bufbytes;
-    cur = cur + 1 == nbuf ? 0 : cur + 1;
-    const float* sc = (const float*)(buf + 2 * PITCH);
-    const int tvalid = min(kTile, ntok - it * kTile);
+    int slot_qk = 0, slot_pv = nbuf - 1, slot_issue = nbuf - 2;   // buffers of tiles st+1, st, st+nbuf-1
+    for (int st = -1; st < ntiles; ++st) {
+      if (st + 1 < ntiles) vm_wait(min(nbuf - 3, ntiles - 2 - st) * copies);  // tile st+1 has landed
+      lds_barrier();                  // tile st+1 visible; P'(st) written; P.V(st-1) done everywhere
+      if (st + nbuf - 1 < ntiles) issue_tile(st + nbuf - 1, slot_issue);
+      slot_issue = slot_issue + 1 == nbuf ? 0 : slot_issue + 1;
 
-    if (qk_wave) {
-      // ---- Q.K for this wave's 16 rows, all features, both token blocks ----
-      // code x q_hi, code x q_lo; b = 16: high byte x (q_hi, q_lo) and low byte x q_hi.
-      // The low byte x q_lo product is left out: its weight is 2^-15 of the
-      // leading term, below the 14-bit rounding of q itself.
-      constexpr int NACC = BITS == 16 ? 3 : 2;
-      float sqv[2][4];                            // integer scores (exact in fp32 for b < 16)
-      // The chunk count is a compile-time constant in each case below, so every
-      // LDS read of the tile is straight-line code the scheduler can hoist
-      // ahead of the MFMAs that consume it.  b = 16 finishes one token block
-      // before starting the other (its operands and accumulators are larger).
-      auto qk_chunks = [&](auto nc) {
-        constexpr int NC = decltype(nc)::value;
-        i4 acc[2][NACC];
+      // ---- P.V of tile st (every wave, its own output units) ----
+      if (st >= 0) {
+        const char* buf = lds + slot_pv * bufbytes;
+        const int par = st & 1;
+        const char* psrc = pbuf + par * (kPbufBytes / 2);
 #pragma unroll
-        for (int tb = 0; tb < 2; ++tb)
+        for (int rb = 0; rb < RB; ++rb) {
+          if (flag_lds[4 * par + rb]) {
+            const float al = alpha_lds[64 * par + 16 * rb + n];
 #pragma unroll
-          for (int k = 0; k < NACC; ++k) acc[tb][k] = i4{0, 0, 0, 0};
-        auto step = [&](int c, int tb) {
-            const int fbyte = (64 * c + 16 * g) * BITS / 8;   // first byte of this lane's 16 features
-            const char* p = buf + tile_off(PITCH, tb, fbyte >> 4, n) + (fbyte & 15);
-            if constexpr (BITS == 8) {
-              const i4 a = *(const i4*)p;
-              acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
-              acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
-            } else if constexpr (BITS == 4) {
-              const u2 x = *(const u2*)p;
-              const i4 a = qk_b4(x[0], x[1]);
-              acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
-              acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
-            } else if constexpr (BITS == 2) {
-              const i4 a = qk_b2(*(const uint32_t*)p);
-              acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
-              acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
-            } else {
-              const u4 x0 = *(const u4*)p;
-              const u4 x1 = *(const u4*)(p + 256);           // next segment of the same token
-              i4 hi, lo;
-              qk_b16(x0, x1, hi, lo);
-              acc[tb][0] = mfma_i8(hi, qh[c], acc[tb][0]);
-              acc[tb][1] = mfma_i8(hi, ql[c], acc[tb][1]);
-              acc[tb][2] = mfma_i8(lo, qh[c], acc[tb][2]);
+            for (int u = 0; u < UMAX; ++u)
+#pragma unroll
+              for (int f = 0; f < 2; ++f) oacc[u][f][rb] *= al;
+          }
+        }
+        auto pv_units = [&](auto uw) {
+          constexpr int UW = decltype(uw)::value;
+          if constexpr (TB == 2) {
+            h8 pfr[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) pfr[rb] = *(const h8*)(psrc + (rb * 64 + lane) * 16);
+            u2 rv[UW][BITS == 16 ? 4 : BITS == 8 ? 2 : 1];
+#pragma unroll
+            for (int ui = 0; ui < UW; ++ui) {
+              const int u = ubase + ui;
+              if constexpr (BITS == 8) {
+#pragma unroll
+                for (int f = 0; f < 2; ++f) {
+                  const int e = n >> 1, h = n & 1, tb = e >> 2;
+                  const char* p = buf + tile_off(PITCH, tb, 2 * u + f, 4 * g + (e & 3)) + 8 * h;
+                  rv[ui][f] = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i2, p)));
+                }
+              }
+              if constexpr (BITS == 4 || BITS == 2) {
+                const int e = n & 7, half = n >> 3;
+                const int tb = (e >> 1) & 1, t = 4 * g + 2 * (e & 1) + (e >> 2);
+                const char* p = BITS == 4 ? buf + tile_off(PITCH, tb, u, t) + 8 * half
+                                          : buf + tile_off(PITCH, tb, u >> 1, t) + 8 * (u & 1);
+                rv[ui][0] = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr4_b64_v2i32(LDS_PTR(i2, p)));
+              }
             }
-        };
-        auto finish = [&](int tb) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            if constexpr (BITS == 16)
-              sqv[tb][j] = 256.0f * (float)(128 * acc[tb][0][j] + acc[tb][1][j]) + (float)(128 * acc[tb][2][j] + qbias);
-            else
-              sqv[tb][j] = (float)(128 * acc[tb][0][j] + acc[tb][1][j] - qbias);
+            for (int ui = 0; ui < UW; ++ui) {
+              h8 a[2];
+              if constexpr (BITS == 8) {
+                a[0] = cvt_b8(rv[ui][0][0], rv[ui][0][1]);
+                a[1] = cvt_b8(rv[ui][1][0], rv[ui][1][1]);
+              }
+              if constexpr (BITS == 4) { a[0] = cvt_b4(rv[ui][0][0]); a[1] = cvt_b4(rv[ui][0][1]); }
+              if constexpr (BITS == 2) { a[0] = cvt_b2_nib(rv[ui][0][0], 0); a[1] = cvt_b2_nib(rv[ui][0][0], 1); }
+#pragma unroll
+              for (int f = 0; f < 2; ++f)
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) oacc[ui][f][rb] = mfma_f16(a[f], pfr[rb], oacc[ui][f][rb]);
+            }
+          } else {
+            // b = 16, 16-token tiles: k = 16 MFMAs on the high byte and the low byte / 256
+            h4 pfr[RB];
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) pfr[rb] = *(const h4*)(psrc + (rb * 64 + lane) * 16);
+#pragma unroll
+            for (int ui = 0; ui < UW; ++ui) {
+              const int u = ubase + ui;
+              u2 rv[2];
+#pragma unroll
+              for (int f = 0; f < 2; ++f) {
+                const int fb = 2 * u + f, e = n >> 2, q = n & 3;
+                const int seg = 2 * fb + (q >> 1), off = 8 * (q & 1);
+                rv[f] = __builtin_bit_cast(
+                    u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s4, buf + tile_off(PITCH, 0, seg, 4 * g + e) + off)));
+              }
+#pragma unroll
+              for (int f = 0; f < 2; ++f) {
+                h4 hi, lo;
+                cvt_b16_4(rv[f], hi, lo);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                  oacc[ui][f][rb] = mfma_f16_k16(hi, pfr[rb], oacc[ui][f][rb]);
+                  oacc[ui][f][rb] = mfma_f16_k16(lo, pfr[rb], oacc[ui][f][rb]);
+                }
+              }
+            }
           }
         };
-        if constexpr (BITS == 16) {
-#pragma unroll
-          for (int tb = 0; tb < 2; ++tb) {
-#pragma unroll
-            for (int c = 0; c < NC; ++c) step(c, tb);
-            finish(tb);
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < NC; ++c) {
-#pragma unroll
-            for (int tb = 0; tb < 2; ++tb) step(c, tb);
-          }
-          finish(0);
-          finish(1);
+        switch (ucount) {
+          case 0: break;
+          case 1: pv_units(std::integral_constant<int, 1>{}); break;
+          case 2: if constexpr (UMAX >= 2) pv_units(std::integral_constant<int, 2>{}); break;
+          case 3: if constexpr (UMAX >= 3) pv_units(std::integral_constant<int, 3>{}); break;
+          case 4: if constexpr (UMAX >= 4) pv_units(std::integral_constant<int, 4>{}); break;
+          case 5: if constexpr (UMAX >= 5) pv_units(std::integral_constant<int, 5>{}); break;
+          case 6: if constexpr (UMAX >= 6) pv_units(std::integral_constant<int, 6>{}); break;
+          default: if constexpr (UMAX >= 7) pv_units(std::integral_constant<int, 7>{}); break;
         }
-      };
-      switch (KC) {
-        case 1: qk_chunks(std::integral_constant<int, 1>{}); break;
-        case 2: qk_chunks(std::integral_constant<int, 2>{}); break;
-        case 3: qk_chunks(std::integral_constant<int, 3>{}); break;
-        case 4: qk_chunks(std::integral_constant<int, 4>{}); break;
-        case 5: qk_chunks(std::integral_constant<int, 5>{}); break;
-        case 6: qk_chunks(std::integral_constant<int, 6>{}); break;
-        case 7: qk_chunks(std::integral_constant<int, 7>{}); break;
-        case 8: qk_chunks(std::integral_constant<int, 8>{}); break;
-        case 9: qk_chunks(std::integral_constant<int, 9>{}); break;
-        default: qk_chunks(std::integral_constant<int, kMaxChunks64>{}); break;
       }
+      // ---- Q.K and softmax of tile st+1 (Q.K waves) ----
+      if constexpr (QKW) {
+        if (st + 1 < ntiles) {
+          const int tq = st + 1;
+          const char* buf = lds + slot_qk * bufbytes;
+          const float* sc = (const float*)(buf + TB * PITCH);
+          const int tvalid = min(TILE, ntok - tq * TILE);
+          // code x q_hi, code x q_lo; b = 16: high byte x (q_hi, q_lo) and low byte x q_hi.
+          // The low byte x q_lo product is left out: its weight is 2^-15 of the
+          // leading term, below the 14-bit rounding of q itself.
+          constexpr int NACC = BITS == 16 ? 3 : 2;
+          float sqv[TB][4];                         // integer scores (exact in fp32 for b < 16)
+          // The chunk count is a compile-time constant in each case below, so every
+          // LDS read of the tile is straight-line code the scheduler can hoist
+          // ahead of the MFMAs that consume it.
+          auto qk_chunks = [&](auto nc) {
+            constexpr int NC = decltype(nc)::value;
+            i4 acc[TB][NACC];
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+              for (int k = 0; k < NACC; ++k) acc[tb][k] = i4{0, 0, 0, 0};
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+              const int fbyte = (64 * c + 16 * g) * BITS / 8;   // first byte of this lane's 16 features
+#pragma unroll
+              for (int tb = 0; tb < TB; ++tb) {
+                const char* p = buf + tile_off(PITCH, tb, fbyte >> 4, n) + (fbyte & 15);
+                if constexpr (BITS == 8) {
+                  const i4 a = *(const i4*)p;
+                  acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
+                  acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
+                } else if constexpr (BITS == 4) {
+                  const u2 x = *(const u2*)p;
+                  const i4 a = qk_b4(x[0], x[1]);
+                  acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
+                  acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
+                } else if constexpr (BITS == 2) {
+                  const i4 a = qk_b2(*(const uint32_t*)p);
+                  acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
+                  acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
+                } else {
+                  const u4 x0 = *(const u4*)p;
+                  const u4 x1 = *(const u4*)(p + 256);           // next segment of the same token
+                  i4 hi, lo;
+                  qk_b16(x0, x1, hi, lo);
+                  acc[tb][0] = mfma_i8(hi, qh[c], acc[tb][0]);
+                  acc[tb][1] = mfma_i8(hi, ql[c], acc[tb][1]);
+                  acc[tb][2] = mfma_i8(lo, qh[c], acc[tb][2]);
+                }
+              }
+            }
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                if constexpr (BITS == 16)
+                  sqv[tb][j] = 256.0f * (float)(128 * acc[tb][0][j] + acc[tb][1][j]) + (float)(128 * acc[tb][2][j] + qbias);
+                else
+                  sqv[tb][j] = (float)(128 * acc[tb][0][j] + acc[tb][1][j] - qbias);
+              }
+          };
+          switch (KC) {
+            case 1: qk_chunks(std::integral_constant<int, 1>{}); break;
+            case 2: qk_chunks(std::integral_constant<int, 2>{}); break;
+            case 3: qk_chunks(std::integral_constant<int, 3>{}); break;
+            case 4: qk_chunks(std::integral_constant<int, 4>{}); break;
+            case 5: qk_chunks(std::integral_constant<int, 5>{}); break;
+            case 6: qk_chunks(std::integral_constant<int, 6>{}); break;
+            case 7: qk_chunks(std::integral_constant<int, 7>{}); break;
+            case 8: qk_chunks(std::integral_constant<int, 8>{}); break;
+            default: qk_chunks(std::integral_constant<int, kMaxChunks64>{}); break;
+          }
 
-      // ---- online softmax for these rows ----
-      f4 scv[2];
-      scv[0] = *(const f4*)(sc + 4 * g);
-      scv[1] = *(const f4*)(sc + 16 + 4 * g);
-      float z[2][4], smax = 0.0f, tmax = -INFINITY;
+          // ---- online softmax for these rows (branch-free) ----
+          f4 scv[TB];
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
+          for (int tb = 0; tb < TB; ++tb) scv[tb] = *(const f4*)(sc + 16 * tb + 4 * g);
+          float z[TB][4], smax = 0.0f, tmax = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bool valid = 16 * tb + 4 * g + j < tvalid;
-          const float sq = sqv[tb][j];
-          const float st = valid ? scv[tb][j] : 0.0f;
-          scv[tb][j] = st;
-          smax = fmaxf(smax, st);
-          z[tb][j] = valid ? sq * rowf * st : -INFINITY;
-          tmax = fmaxf(tmax, z[tb][j]);
-        }
-      smax = max_xor_16_32(smax);
-      tmax = max_xor_16_32(tmax);
-      const bool raise_e = smax > ldexpf(1.0f, Ecur + kScaleHeadroom);
-      const bool move_m = tmax > m_run + kLazyRescale;
-      int flag = 0;
-      if (__any(move_m) || raise_e) {
-        const float mnew = fmaxf(m_run, tmax);
-        int enew = Ecur;
-        if (raise_e) (void)frexpf(smax, &enew);
-        const float am = exp2f(m_run - mnew);
-        l_lane *= am;
-        const float alpha = am * ldexpf(1.0f, Ecur - enew);
-        m_run = mnew;
-        Ecur = enew;
-        if (g == 0) alpha_lds[my_row] = alpha;
-        flag = 1;
-      }
-      if (lane == 0) flag_lds[wave] = flag;
-      const float sprime = ldexpf(1.0f, -Ecur);
-      h8 pf;
+          for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-      for (int tb = 0; tb < 2; ++tb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float e = __builtin_amdgcn_exp2f(z[tb][j] - m_run);
-          l_lane += e;
-          pf[4 * tb + j] = (_Float16)(e * (scv[tb][j] * sprime));
-        }
-      ((h8*)pbuf)[wave * 64 + lane] = pf;
-    }
-    lds_barrier();                              // (C) P' and rescale factors visible
-
-    // ---- P.V over this wave's output units ----
-    h8 pfr[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-      pfr[rb] = ((const h8*)pbuf)[rb * 64 + lane];
-      if (flag_lds[rb]) {
-        const float al = alpha_lds[16 * rb + n];
-#pragma unroll
-        for (int u = 0; u < NUW; ++u)
-#pragma unroll
-          for (int f = 0; f < 2; ++f) oacc[u][f][rb] *= al;
-      }
-    }
-    // units of this wave: u = wave + 4*ui for ui < UW; all operand reads first
-    auto pv_units = [&](auto uw) {
-      constexpr int UW = decltype(uw)::value;
-      u2 rv[UW > 0 ? UW : 1][BITS == 16 ? 4 : BITS == 8 ? 2 : 1];
-#pragma unroll
-      for (int ui = 0; ui < UW; ++ui) {
-        if constexpr (BITS == 16) {
-          if (ui > 0) __builtin_amdgcn_sched_barrier(0);
-        }
-        const int u = wave + kWaves * ui;
-        if constexpr (BITS == 8) {
-#pragma unroll
-          for (int f = 0; f < 2; ++f) {
-            const int e = n >> 1, h = n & 1, tb = e >> 2;
-            const char* p = buf + tile_off(PITCH, tb, 2 * u + f, 4 * g + (e & 3)) + 8 * h;
-            rv[ui][f] = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i2, p)));
-          }
-        }
-        if constexpr (BITS == 4 || BITS == 2) {
-          const int e = n & 7, half = n >> 3;
-          const int tb = (e >> 1) & 1, t = 4 * g + 2 * (e & 1) + (e >> 2);
-          const char* p = BITS == 4 ? buf + tile_off(PITCH, tb, u, t) + 8 * half
-                                    : buf + tile_off(PITCH, tb, u >> 1, t) + 8 * (u & 1);
-          rv[ui][0] = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr4_b64_v2i32(LDS_PTR(i2, p)));
-        }
-        if constexpr (BITS == 16) {
-#pragma unroll
-          for (int f = 0; f < 2; ++f) {
-            const int fb = 2 * u + f, e = n >> 2, q = n & 3;
-            const int seg = 2 * fb + (q >> 1), off = 8 * (q & 1);
+            for (int j = 0; j < 4; ++j) {
+              const bool valid = 16 * tb + 4 * g + j < tvalid;
+              const float st_ = valid ? scv[tb][j] : 0.0f;
+              scv[tb][j] = st_;
+              smax = fmaxf(smax, st_);
+              z[tb][j] = valid ? sqv[tb][j] * rowf * st_ : -INFINITY;
+              tmax = fmaxf(tmax, z[tb][j]);
+            }
+          smax = max_xor_16_32(smax);
+          tmax = max_xor_16_32(tmax);
+          const bool raise_e = smax > ldexpf(1.0f, Ecur + kScaleHeadroom);   // wave-uniform
+          const bool upd = __any(tmax > m_run + kLazyRescale) || raise_e;    // wave-uniform
+          const float mnew = upd ? fmaxf(m_run, tmax) : m_run;
+          int es = Ecur;
+          (void)frexpf(smax, &es);
+          const int enew = raise_e ? es : Ecur;
+          const float am = exp2f(m_run - mnew);
+          l_lane *= am;
+          const float alpha = am * ldexpf(1.0f, Ecur - enew);
+          m_run = mnew;
+          Ecur = enew;
+          const int par = tq & 1;
+          if (g == 0) alpha_lds[64 * par + my_row] = alpha;
+          if (lane == 0) flag_lds[4 * par + wave] = upd ? 1 : 0;
+          const float sprime = ldexpf(1.0f, -Ecur);
+          char* pdst = pbuf + par * (kPbufBytes / 2) + (wave * 64 + lane) * 16;
+          if constexpr (TB == 2) {
+            h8 pf;
 #pragma unroll
             for (int tb = 0; tb < 2; ++tb)
-              rv[ui][2 * f + tb] = __builtin_bit_cast(
-                  u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s4, buf + tile_off(PITCH, tb, seg, 4 * g + e) + off)));
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const float e = __builtin_amdgcn_exp2f(z[tb][j] - m_run);
+                l_lane += e;
+                pf[4 * tb + j] = (_Float16)(e * (scv[tb][j] * sprime));
+              }
+            *(h8*)pdst = pf;
+          } else {
+            h4 pf;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float e = __builtin_amdgcn_exp2f(z[0][j] - m_run);
+              l_lane += e;
+              pf[j] = (_Float16)(e * (scv[0][j] * sprime));
+            }
+            *(h4*)pdst = pf;
           }
         }
       }
-#pragma unroll
-      for (int ui = 0; ui < UW; ++ui) {
-        // b = 16 holds twice the operands per unit: one unit at a time
-        if constexpr (BITS == 16) {
-          if (ui > 0) __builtin_amdgcn_sched_barrier(0);
-        }
-        h8 a[2], alo[2];
-        if constexpr (BITS == 8) {
-          a[0] = cvt_b8(rv[ui][0][0], rv[ui][0][1]);
-          a[1] = cvt_b8(rv[ui][1][0], rv[ui][1][1]);
-        }
-        if constexpr (BITS == 4) { a[0] = cvt_b4(rv[ui][0][0]); a[1] = cvt_b4(rv[ui][0][1]); }
-        if constexpr (BITS == 2) { a[0] = cvt_b2_nib(rv[ui][0][0], 0); a[1] = cvt_b2_nib(rv[ui][0][0], 1); }
-        if constexpr (BITS == 16) {
-#pragma unroll
-          for (int f = 0; f < 2; ++f)
-            cvt_b16(u4{rv[ui][2 * f][0], rv[ui][2 * f][1], rv[ui][2 * f + 1][0], rv[ui][2 * f + 1][1]}, a[f], alo[f]);
-        }
-#pragma unroll
-        for (int f = 0; f < 2; ++f)
-#pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            oacc[ui][f][rb] = mfma_f16(a[f], pfr[rb], oacc[ui][f][rb]);
-            if constexpr (BITS == 16) oacc[ui][f][rb] = mfma_f16(alo[f], pfr[rb], oacc[ui][f][rb]);
-          }
-      }
-    };
-    switch (my_units) {
-      case 0: break;
-      case 1: pv_units(std::integral_constant<int, 1>{}); break;
-      case 2: pv_units(std::integral_constant<int, 2>{}); break;
-      case 3: pv_units(std::integral_constant<int, 3>{}); break;
-      default: pv_units(std::integral_constant<int, NUW>{}); break;
-    }
-  }
 
-  // ---- finish: row sums, then normalized output or split partial -----------------
-  if (qk_wave) {
-    const float lrow = sum_xor_16_32(l_lane);
-    if (g == 0) { ml_lds[2 * my_row] = m_run; ml_lds[2 * my_row + 1] = lrow; }
-    if (wave == 0 && lane == 0) misc_lds[0] = Ecur;
-  }
-  lds_barrier();
-  constexpr float kBitScale = BITS == 16 ? 256.0f : 1.0f;
-  const float outscale = ntiles > 0 ? ldexpf(kBitScale, misc_lds[0]) : 0.0f;
-  const bool split = E.splits > 1;
-  float* part = nullptr;
-  if (split) {
-    const int64_t slot = ((int64_t)(s * E.splits + ksplit) * E.nrc + chunk);
-    part = A.ws + E.ws_off + slot * partial_slot_floats(d);
-    if (tid < 16 * RB) {
-      part[64 * (int64_t)d + tid] = ml_lds[2 * tid];
-      part[64 * (int64_t)d + 64 + tid] = ml_lds[2 * tid + 1];
+      slot_qk = slot_qk + 1 == nbuf ? 0 : slot_qk + 1;
+      slot_pv = slot_pv + 1 == nbuf ? 0 : slot_pv + 1;
     }
-  }
+
+    // ---- finish: row sums, then normalized output or split partial -----------------
+    if constexpr (QKW) {
+      const float lrow = sum_xor_16_32(l_lane);
+      if (g == 0) { ml_lds[2 * my_row] = m_run; ml_lds[2 * my_row + 1] = lrow; }
+      if (wave == 0 && lane == 0) misc_lds[0] = Ecur;
+    }
+    lds_barrier();
+    constexpr float kBitScale = BITS == 16 ? 256.0f : 1.0f;
+    const float outscale = ntiles > 0 ? ldexpf(kBitScale, misc_lds[0]) : 0.0f;
+    const bool split = E.splits > 1;
+    float* part = nullptr;
+    if (split) {
+      const int64_t slotp = ((int64_t)(s * E.splits + ksplit) * E.nrc + chunk);
+      part = A.ws + E.ws_off + slotp * partial_slot_floats(d);
+      if (tid < 16 * RB) {
+        part[64 * (int64_t)d + tid] = ml_lds[2 * tid];
+        part[64 * (int64_t)d + 64 + tid] = ml_lds[2 * tid + 1];
+      }
+    }
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int rl = 16 * rb + n;
-    if (rl < nrows) {
-      const int gr = r0 + rl;
-      const int layer = A.group_layers[E.lay_begin + gr / A.heads], head = gr % A.heads;
-      const float lrow = ml_lds[2 * rl + 1];
-      const float fac = split ? outscale : (lrow > 0.0f ? outscale / lrow : 0.0f);
-      float* dst = split ? part + (int64_t)rl * d : A.out + A.layers[layer].out_off + ((int64_t)s * A.heads + head) * d;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int rl = 16 * rb + n;
+      if (rl < nrows) {
+        const int gr = r0 + rl;
+        const int layer = A.group_layers[E.lay_begin + gr / A.heads], head = gr % A.heads;
+        const float lrow = ml_lds[2 * rl + 1];
+        const float fac = split ? outscale : (lrow > 0.0f ? outscale / lrow : 0.0f);
+        float* dst = split ? part + (int64_t)rl * d : A.out + A.layers[layer].out_off + ((int64_t)s * A.heads + head) * d;
 #pragma unroll
-      for (int ui = 0; ui < NUW; ++ui) {
-        const int u = wave + kWaves * ui;
-        if constexpr (BITS == 2) {
-          const int fbase = 32 * u + 8 * g;
-          if (u < NU && fbase < d) {
-            const f4 e0 = oacc[ui][0][rb] * fac, e1 = oacc[ui][1][rb] * fac;
-            *(f4*)(dst + fbase) = f4{e0[0], e1[0], e0[1], e1[1]};
-            *(f4*)(dst + fbase + 4) = f4{e0[2], e1[2], e0[3], e1[3]};
-          }
-        } else {
+        for (int ui = 0; ui < UMAX; ++ui) {
+          const int u = ubase + ui;
+          if (ui < ucount) {
+            if constexpr (BITS == 2) {
+              const int fbase = 32 * u + 8 * g;
+              if (fbase < d) {
+                const f4 e0 = oacc[ui][0][rb] * fac, e1 = oacc[ui][1][rb] * fac;
+                *(f4*)(dst + fbase) = f4{e0[0], e1[0], e0[1], e1[1]};
+                *(f4*)(dst + fbase + 4) = f4{e0[2], e1[2], e0[3], e1[3]};
+              }
+            } else {
 #pragma unroll
-          for (int f = 0; f < 2; ++f) {
-            const int fbase = 32 * u + 16 * f + 4 * g;
-            if (u < NU && fbase < d) *(f4*)(dst + fbase) = oacc[ui][f][rb] * fac;
+              for (int f = 0; f < 2; ++f) {
+                const int fbase = 32 * u + 16 * f + 4 * g;
+                if (fbase < d) *(f4*)(dst + fbase) = oacc[ui][f][rb] * fac;
+              }
+            }
           }
         }
       }
     }
-  }
+  };
+
+  if (RB >= kWaves || wave < RB)
+    pipeline(std::true_type{}, std::integral_constant<int, qk_units_max<RB>()>{});
+  else
+    pipeline(std::false_type{}, std::integral_constant<int, pv_units_max<RB>()>{});
 }
 
 __device__ inline int find_entry(KArgs& A, int item) {
@@ -767,11 +848,11 @@ hipError_t launch_one(const DecodeArgs& a, int n, int lds, hipStream_t stream) {
 }  // namespace
 
 // Tile buffers per workgroup: as many as fit in the workgroup's share of the
-// 160 KB LDS, 2 to 8.
+// 160 KB LDS, 3 to 8 (two tiles are in use, the rest in flight).
 int decode_nbuf(int row_stride, int K, int bits) {
   const int budget = 160 * 1024 / decode_wg_per_cu(bits) - kPbufBytes - kMiscBytes;
   const int n = budget / tilebuf_bytes(row_stride, K, bits);
-  return n < 2 ? 2 : (n > 8 ? 8 : n);
+  return n < 3 ? 3 : (n > 8 ? 8 : n);
 }
 
 int decode_lds_bytes(int row_stride, int K, int bits) {

@@ -10,9 +10,8 @@ namespace kk {
 // ---- decode kernel geometry -------------------------------------------------
 constexpr int kWaves = 4;            // waves per workgroup (256 threads)
 constexpr int kThreads = 64 * kWaves;
-constexpr int kTile = 32;            // cached tokens per pipeline stage
+constexpr int kTile = 32;            // token granularity of splits (tiles are 32 or 16 tokens)
 constexpr int kMaxRowBlocks = 4;     // 16-row MFMA blocks per work item (<= 64 query rows)
-constexpr int kMaxUnitsPerWave = 4;  // 32-feature output units per wave in P.V (d <= 512)
 constexpr int kMaxMergeSplits = 64;  // token splits of one sequence
 constexpr int kMaxK = 576;           // d + d_R (the ABI limit)
 constexpr int kMaxEntries = 96;      // group entries per launch
