@@ -10,9 +10,10 @@
 // Bottleneck"), so the kernel is built around streaming the packed codes once.
 //
 // Work item = (chunk of <= 16*RB query rows of one anchor group, sequence,
-// token split).  A workgroup of 4 waves processes one item in 32-token tiles:
+// token split).  A workgroup of 4 waves processes one item in tiles of 32
+// tokens (16 for b = 16), two workgroups per CU:
 //   1. the tile's packed rows and scales are copied HBM -> LDS with direct
-//      loads (global_load_lds), double-buffered one tile ahead;
+//      loads (global_load_lds), several tiles ahead (explicit vmcnt waits);
 //   2. Q.K on the integer MFMA: wave w < RB owns query rows 16w..16w+15.  The
 //      codes are used as int8 operands directly (b = 8), after a shift/mask
 //      nibble or 2-bit expansion (b = 4, 2; offset-binary with an exact bias
@@ -23,11 +24,14 @@
 //      sm_scale applied in fp32, running max in the log2 domain moved lazily,
 //      P' = exp2(z - m) * scale_t * 2^-E written to LDS as fp16, with E a
 //      lazily raised power-of-two bound of the scales seen;
-//   4. P.V on the fp16 MFMA, output features split over the 4 waves in
-//      32-wide units; codes are read transposed with ds_read_b64_tr_b{4,8,16}
-//      and converted to exact fp16 integers (magic-number conversion).
-// Inheriting layers of a group are extra query rows of the same items.  Items
-// that were split write (m, l, O) partials; a small kernel merges them.
+//   4. P.V on the fp16 MFMA, output features split over the waves in 32-wide
+//      units; codes are read transposed with ds_read_b64_tr_b{4,8,16} and
+//      converted to fp16: exact integers for b <= 8 (magic-number conversion),
+//      rounded to 11 significant bits for b = 16.
+// Each stage runs P.V of tile t and Q.K + softmax of tile t+1 between two
+// barriers.  Inheriting layers of a group are extra query rows of the same
+// items.  Items that were split write (m, l, O) partials; a small kernel
+// merges them.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -61,10 +65,10 @@ constexpr int kMaxChunks64 = (kMaxK + 63) / 64;
 
 // ---- LDS map (bytes, dynamic shared memory) ----------------------------------
 //  [0, nbuf*buf)  tile buffers: codes of token block 0 [| block 1] | slack | scales
-//  pbuf           P' fragments [tile parity][row block][64 lanes] 16 B
+//  pbuf           P' fragments [tile parity][row block][64 lanes] 8 B per 16 tokens
 //  alpha[2][64] flags[2][4] ml[64][2] misc[16]
-constexpr int kPbufBytes = 2 * kMaxRowBlocks * 64 * 16;
 constexpr int kMiscBytes = 2 * 64 * 4 + 2 * 4 * 4 + 64 * 8 + 64;
+__host__ __device__ inline int pbuf_bytes(int rb, int tile_blocks) { return 2 * rb * 64 * 8 * tile_blocks; }
 
 __host__ __device__ inline int nseg_of(int row_stride) { return row_stride >> 4; }
 __host__ __device__ inline int chunks64_of(int K) { return (K + 63) >> 6; }
@@ -73,10 +77,10 @@ __host__ __device__ inline int nsegpad_of(int K, int bits) { return (chunks64_of
 // 16-token blocks per tile (see tile_blocks below)
 __host__ __device__ inline int tile_blocks_of(int bits) { return bits == 16 ? 1 : 2; }
 // Tile buffer: all but the last token block at full pitch, the last one padded
-// for whole-chunk Q.K reads, then 256 bytes for the scales.
+// for whole-chunk Q.K reads, then the tile's fp32 scales (4 bytes per token).
 __host__ __device__ inline int tilebuf_bytes(int row_stride, int K, int bits) {
-  const int nseg = nseg_of(row_stride), pad = nsegpad_of(K, bits);
-  return ((tile_blocks_of(bits) - 1) * nseg + (pad > nseg ? pad : nseg)) * 256 + 256;
+  const int nseg = nseg_of(row_stride), pad = nsegpad_of(K, bits), tb = tile_blocks_of(bits);
+  return ((tb - 1) * nseg + (pad > nseg ? pad : nseg)) * 256 + 64 * tb;
 }
 
 // ---- operand conversions ------------------------------------------------------
@@ -99,19 +103,21 @@ __device__ inline h8 cvt_b8(uint32_t x0, uint32_t x1) {
                as_h2(perm(0x64646464u, x1, 0x04010400u)) + bias, as_h2(perm(0x64646464u, x1, 0x04030402u)) + bias);
 }
 // 8 signed nibbles of x (element k at bits 4k) -> fp16 in order (0,4,1,5,2,6,3,7).
+// (nibble & 15) ^ 8 is the offset-binary code c + 8; the exponent bits 0x6400
+// are merged by the same xor (they are zero after the mask): 1024 + c + 8.
 __device__ inline h8 cvt_b4(uint32_t x) {
   const h2 bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  x ^= 0x88888888u;
-  return pack8(as_h2((x & 0x000F000Fu) | 0x64006400u) + bias, as_h2(((x >> 4) & 0x000F000Fu) | 0x64006400u) + bias,
-               as_h2(((x >> 8) & 0x000F000Fu) | 0x64006400u) + bias, as_h2(((x >> 12) & 0x000F000Fu) | 0x64006400u) + bias);
+  return pack8(as_h2((x & 0x000F000Fu) ^ 0x64086408u) + bias, as_h2(((x >> 4) & 0x000F000Fu) ^ 0x64086408u) + bias,
+               as_h2(((x >> 8) & 0x000F000Fu) ^ 0x64086408u) + bias, as_h2(((x >> 12) & 0x000F000Fu) ^ 0x64086408u) + bias);
 }
 // 2-bit fields of nibble-packed data from a 4-bit transpose read: element e at
 // bits 4e (even field) or 4e + 2 (odd field); result order (0,4,1,5,2,6,3,7).
-__device__ inline h8 cvt_b2_nib(uint32_t x, int odd) {
+template <int ODD>
+__device__ inline h8 cvt_b2_nib(uint32_t x) {
   const h2 bias = {(_Float16)-1026.0f, (_Float16)-1026.0f};
-  const uint32_t y = (x ^ 0xAAAAAAAAu) >> (odd ? 2 : 0);
-  return pack8(as_h2((y & 0x00030003u) | 0x64006400u) + bias, as_h2(((y >> 4) & 0x00030003u) | 0x64006400u) + bias,
-               as_h2(((y >> 8) & 0x00030003u) | 0x64006400u) + bias, as_h2(((y >> 12) & 0x00030003u) | 0x64006400u) + bias);
+  const uint32_t y = x >> (2 * ODD);
+  return pack8(as_h2((y & 0x00030003u) ^ 0x64026402u) + bias, as_h2(((y >> 4) & 0x00030003u) ^ 0x64026402u) + bias,
+               as_h2(((y >> 8) & 0x00030003u) ^ 0x64026402u) + bias, as_h2(((y >> 12) & 0x00030003u) ^ 0x64026402u) + bias);
 }
 // 8 int16 codes (w0..w3 little-endian) -> hi (signed high byte) and lo/256
 // (unsigned low byte scaled by 2^-8, exact: fp16 0x44XX = 4 + XX/256).
@@ -125,18 +131,22 @@ __device__ inline void cvt_b16(u4 w, h8& hi, h8& lo) {
              as_h2(perm(0x44444444u, w[2], 0x04020400u)) + bl, as_h2(perm(0x44444444u, w[3], 0x04020400u)) + bl);
 }
 
-// int8 operands for the Q.K MFMA (16 features per lane).
-// b = 4: 16 nibbles (x0: 0..7, x1: 8..15) -> offset-binary bytes (code + 8),
+// int8 operands for the Q.K MFMA (16 features per lane).  A b-bit two's
+// complement field moved to the top of its byte, with the bits below cleared,
+// is the signed byte 2^(8-b) * code exactly, so no offset or bias correction
+// is needed; the factor 2^(8-b) is divided out with the row scale.
+// b = 4: 16 nibbles (x0: 0..7, x1: 8..15) -> 16 * code,
 //        slot order 0,2,4,6 | 1,3,5,7 | 8,10,12,14 | 9,11,13,15.
 __device__ inline i4 qk_b4(uint32_t x0, uint32_t x1) {
-  x0 ^= 0x88888888u; x1 ^= 0x88888888u;
-  return i4{(int)(x0 & 0x0F0F0F0Fu), (int)((x0 >> 4) & 0x0F0F0F0Fu), (int)(x1 & 0x0F0F0F0Fu), (int)((x1 >> 4) & 0x0F0F0F0Fu)};
+  return i4{(int)((x0 << 4) & 0xF0F0F0F0u), (int)(x0 & 0xF0F0F0F0u), (int)((x1 << 4) & 0xF0F0F0F0u), (int)(x1 & 0xF0F0F0F0u)};
 }
-// b = 2: 16 fields of x -> offset-binary bytes (code + 2); slot 4j + k holds field 4k + j.
+// b = 2: 16 fields of x -> 64 * code; slot 4j + k holds field 4k + j.
 __device__ inline i4 qk_b2(uint32_t x) {
-  x ^= 0xAAAAAAAAu;
-  return i4{(int)(x & 0x03030303u), (int)((x >> 2) & 0x03030303u), (int)((x >> 4) & 0x03030303u), (int)((x >> 6) & 0x03030303u)};
+  return i4{(int)((x << 6) & 0xC0C0C0C0u), (int)((x << 4) & 0xC0C0C0C0u), (int)((x << 2) & 0xC0C0C0C0u), (int)(x & 0xC0C0C0C0u)};
 }
+// Q.K operand scale of b-bit codes (see qk_b4 / qk_b2)
+template <int BITS>
+constexpr float qk_code_scale() { return BITS == 4 ? 1.0f / 16.0f : BITS == 2 ? 1.0f / 64.0f : 1.0f; }
 // b = 16: 16 int16 (w0..w7) -> signed high bytes and low bytes minus 128.
 __device__ inline void qk_b16(u4 a, u4 b, i4& hi, i4& lo) {
   hi = i4{(int)perm(a[1], a[0], 0x07050301u), (int)perm(a[3], a[2], 0x07050301u),
@@ -191,15 +201,23 @@ __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_b
 // the LDS base; the nop covers the M0-write hazard.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-__device__ inline void copy16_to_lds(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base) : "memory", "m0");
+// Address = 64-bit scalar base + 32-bit per-lane byte offset (SADDR form).
+__device__ inline void copy16_to_lds(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
 }
-__device__ inline void copy4_to_lds(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds_base) : "memory", "m0");
+__device__ inline void copy4_to_lds(uint32_t voff, const void* sbase, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
 }
 #pragma clang diagnostic pop
 __device__ inline uint32_t lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)LDS_PTR(const void, p));
+}
+__device__ inline const void* uniform_ptr(const void* p) {
+  const uint64_t x = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x), hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Wait until at most n vector-memory operations of this wave are outstanding
@@ -246,15 +264,11 @@ constexpr int pv_units_max() { return RB == 3 ? 7 : 5; }
 
 __device__ inline f4 mfma_f16_k16(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
 
-// 4 int16 codes (w0, w1 little-endian) -> signed high bytes and low bytes / 256 as fp16.
-__device__ inline void cvt_b16_4(u2 w, h4& hi, h4& lo) {
-  const h2 bh = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  const h2 bl = {(_Float16)-4.0f, (_Float16)-4.0f};
-  const uint32_t x0 = w[0] ^ 0x80008000u, x1 = w[1] ^ 0x80008000u;
-  const h2 a0 = as_h2(perm(0x64646464u, x0, 0x04030401u)) + bh, a1 = as_h2(perm(0x64646464u, x1, 0x04030401u)) + bh;
-  const h2 b0 = as_h2(perm(0x44444444u, w[0], 0x04020400u)) + bl, b1 = as_h2(perm(0x44444444u, w[1], 0x04020400u)) + bl;
-  hi = h4{a0[0], a0[1], a1[0], a1[1]};
-  lo = h4{b0[0], b0[1], b1[0], b1[1]};
+// 4 int16 codes (w0, w1 little-endian) -> fp16, rounded to nearest even (11
+// significant bits; relative error <= 2^-11, the same size as the fp16 P').
+__device__ inline h4 cvt_i16x4(u2 w) {
+  return h4{(_Float16)(short)(w[0] & 0xFFFFu), (_Float16)(short)(w[0] >> 16), (_Float16)(short)(w[1] & 0xFFFFu),
+            (_Float16)(short)(w[1] >> 16)};
 }
 
 // One work item: a chunk of <= 16*RB query rows of one anchor group, one
@@ -273,8 +287,10 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   const int NSEG = nseg_of(E.row_stride), PITCH = NSEG * 256;
   const int bufbytes = tilebuf_bytes(E.row_stride, K, BITS);
   const int nbuf = E.nbuf;                    // >= 3 tile buffers
-  char* pbuf = lds + nbuf * bufbytes;         // [2][kMaxRowBlocks][64 lanes] 16 B
-  float* alpha_lds = (float*)(pbuf + kPbufBytes);   // [2][64]
+  constexpr int PSLOT = 8 * TB;               // P' bytes per lane and row block
+  constexpr int PPAR = RB * 64 * PSLOT;       // P' bytes per tile parity
+  char* pbuf = lds + nbuf * bufbytes;         // [2][RB][64 lanes] PSLOT bytes
+  float* alpha_lds = (float*)(pbuf + 2 * PPAR);     // [2][64]
   int* flag_lds = (int*)(alpha_lds + 128);          // [2][4]
   float* ml_lds = (float*)(flag_lds + 8);           // [64][2]
   int* misc_lds = (int*)(ml_lds + 128);
@@ -302,27 +318,31 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   const int block_pieces = NSEG * 16;
   const int npos = TB * block_pieces;            // 16-byte pieces of codes in a tile
   const int ninst = (npos + 63) >> 6;            // 64-lane copy instructions per tile
-  // this wave's copy instructions per tile (wave-uniform, so the waits below are scalar code)
-  const int copies = __builtin_amdgcn_readfirstlane((ninst > wave ? (ninst - wave + kWaves - 1) / kWaves : 0) +
-                                                    (wave == kWaves - 1 ? 1 : 0));
+  // The copy loop runs on scalar registers: wave index, tile base address and
+  // LDS addresses are wave-uniform; each lane only adds its 32-bit offset.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int copies = __builtin_amdgcn_readfirstlane((ninst > wave_u ? (ninst - wave_u + kWaves - 1) / kWaves : 0) +
+                                                    (wave_u == kWaves - 1 ? 1 : 0));
+  const uint32_t lds0 = lds_addr(lds);
+  const int rstride = E.row_stride;
+  const uint8_t* item_codes = (const uint8_t*)uniform_ptr(codes + row0 * (int64_t)rstride);
+  const float* item_scales = (const float*)uniform_ptr(scales + row0);
   auto issue_tile = [&](int it, int slotb) {
-    char* buf = lds + slotb * bufbytes;
+    const uint32_t buf = lds0 + slotb * bufbytes;
     const int tok0 = it * TILE;
     const int tlast = min(TILE, ntok - tok0) - 1;
-    for (int i = wave; i < ninst; i += kWaves) {
+    const void* tbase = item_codes + (int64_t)tok0 * rstride;
+    for (int i = wave_u; i < ninst; i += kWaves) {
       const int p = i * 64 + lane;
       const int tb = (TB == 2 && p >= block_pieces) ? 1 : 0;
       const int rem = p - tb * block_pieces;
       const int seg = rem >> 4, slot = rem & 15;
       const int t = min(16 * tb + (slot ^ (tb << 2)), tlast);
-      if (p < npos) {                            // lane 0 always copies: the instruction is issued
-        const uint8_t* gp = codes + (row0 + tok0 + t) * (int64_t)E.row_stride + seg * 16;
-        copy16_to_lds(gp, lds_addr(buf + i * 1024));
-      }
+      if (p < npos)                              // lane 0 always copies: the instruction is issued
+        copy16_to_lds((uint32_t)(t * rstride + seg * 16), tbase, buf + i * 1024);
     }
-    if (wave == kWaves - 1 && lane < TILE) {
-      copy4_to_lds(scales + row0 + tok0 + min(lane, tlast), lds_addr(buf + TB * PITCH));
-    }
+    if (wave_u == kWaves - 1 && lane < TILE)
+      copy4_to_lds((uint32_t)(min(lane, tlast) * 4), item_scales + tok0, buf + TB * PITCH);
   };
   // prologue: tiles 0 .. nbuf-3; stage st issues tile st + nbuf - 1
   for (int it = 0; it < nbuf - 2 && it < ntiles; ++it) issue_tile(it, it);
@@ -432,9 +452,9 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
         ql[c] = i4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
       }
       qsum = isum_xor_16_32(qsum);
-      if (my_layer >= 0) rowf = A.layers[my_layer].sm_scale * kLog2e * ldexpf(1.0f, e - kQFrac);
-      // offset-binary bias of the Q.K operand (exact integer correction)
-      qbias = BITS == 4 ? 8 * qsum : BITS == 2 ? 2 * qsum : BITS == 16 ? 128 * qsum : 0;
+      if (my_layer >= 0) rowf = A.layers[my_layer].sm_scale * kLog2e * ldexpf(qk_code_scale<BITS>(), e - kQFrac);
+      // b = 16: offset-binary bias of the low-byte operand (exact integer correction)
+      qbias = BITS == 16 ? 128 * qsum : 0;
     }
 
     f4 oacc[UMAX][2][RB];
@@ -456,7 +476,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       if (st >= 0) {
         const char* buf = lds + slot_pv * bufbytes;
         const int par = st & 1;
-        const char* psrc = pbuf + par * (kPbufBytes / 2);
+        const char* psrc = pbuf + par * PPAR;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           if (flag_lds[4 * par + rb]) {
@@ -472,7 +492,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           if constexpr (TB == 2) {
             h8 pfr[RB];
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) pfr[rb] = *(const h8*)(psrc + (rb * 64 + lane) * 16);
+            for (int rb = 0; rb < RB; ++rb) pfr[rb] = *(const h8*)(psrc + (rb * 64 + lane) * PSLOT);
             u2 rv[UW][BITS == 16 ? 4 : BITS == 8 ? 2 : 1];
 #pragma unroll
             for (int ui = 0; ui < UW; ++ui) {
@@ -501,17 +521,17 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
                 a[1] = cvt_b8(rv[ui][1][0], rv[ui][1][1]);
               }
               if constexpr (BITS == 4) { a[0] = cvt_b4(rv[ui][0][0]); a[1] = cvt_b4(rv[ui][0][1]); }
-              if constexpr (BITS == 2) { a[0] = cvt_b2_nib(rv[ui][0][0], 0); a[1] = cvt_b2_nib(rv[ui][0][0], 1); }
+              if constexpr (BITS == 2) { a[0] = cvt_b2_nib<0>(rv[ui][0][0]); a[1] = cvt_b2_nib<1>(rv[ui][0][0]); }
 #pragma unroll
               for (int f = 0; f < 2; ++f)
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) oacc[ui][f][rb] = mfma_f16(a[f], pfr[rb], oacc[ui][f][rb]);
             }
           } else {
-            // b = 16, 16-token tiles: k = 16 MFMAs on the high byte and the low byte / 256
+            // b = 16, 16-token tiles: k = 16 MFMAs on the codes rounded to fp16
             h4 pfr[RB];
 #pragma unroll
-            for (int rb = 0; rb < RB; ++rb) pfr[rb] = *(const h4*)(psrc + (rb * 64 + lane) * 16);
+            for (int rb = 0; rb < RB; ++rb) pfr[rb] = *(const h4*)(psrc + (rb * 64 + lane) * PSLOT);
 #pragma unroll
             for (int ui = 0; ui < UW; ++ui) {
               const int u = ubase + ui;
@@ -525,13 +545,9 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
               }
 #pragma unroll
               for (int f = 0; f < 2; ++f) {
-                h4 hi, lo;
-                cvt_b16_4(rv[f], hi, lo);
+                const h4 a = cvt_i16x4(rv[f]);
 #pragma unroll
-                for (int rb = 0; rb < RB; ++rb) {
-                  oacc[ui][f][rb] = mfma_f16_k16(hi, pfr[rb], oacc[ui][f][rb]);
-                  oacc[ui][f][rb] = mfma_f16_k16(lo, pfr[rb], oacc[ui][f][rb]);
-                }
+                for (int rb = 0; rb < RB; ++rb) oacc[ui][f][rb] = mfma_f16_k16(a, pfr[rb], oacc[ui][f][rb]);
               }
             }
           }
@@ -606,7 +622,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
                 if constexpr (BITS == 16)
                   sqv[tb][j] = 256.0f * (float)(128 * acc[tb][0][j] + acc[tb][1][j]) + (float)(128 * acc[tb][2][j] + qbias);
                 else
-                  sqv[tb][j] = (float)(128 * acc[tb][0][j] + acc[tb][1][j] - qbias);
+                  sqv[tb][j] = (float)(128 * acc[tb][0][j] + acc[tb][1][j]);
               }
           };
           switch (KC) {
@@ -626,17 +642,28 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb) scv[tb] = *(const f4*)(sc + 16 * tb + 4 * g);
           float z[TB][4], smax = 0.0f, tmax = -INFINITY;
+          if (tvalid == TILE) {                      // every tile but an item's last: no masking
 #pragma unroll
-          for (int tb = 0; tb < TB; ++tb)
+            for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const bool valid = 16 * tb + 4 * g + j < tvalid;
-              const float st_ = valid ? scv[tb][j] : 0.0f;
-              scv[tb][j] = st_;
-              smax = fmaxf(smax, st_);
-              z[tb][j] = valid ? sqv[tb][j] * rowf * st_ : -INFINITY;
-              tmax = fmaxf(tmax, z[tb][j]);
-            }
+              for (int j = 0; j < 4; ++j) {
+                smax = fmaxf(smax, scv[tb][j]);
+                z[tb][j] = sqv[tb][j] * rowf * scv[tb][j];
+                tmax = fmaxf(tmax, z[tb][j]);
+              }
+          } else {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                const bool valid = 16 * tb + 4 * g + j < tvalid;
+                const float st_ = valid ? scv[tb][j] : 0.0f;
+                scv[tb][j] = st_;
+                smax = fmaxf(smax, st_);
+                z[tb][j] = valid ? sqv[tb][j] * rowf * st_ : -INFINITY;
+                tmax = fmaxf(tmax, z[tb][j]);
+              }
+          }
           smax = max_xor_16_32(smax);
           tmax = max_xor_16_32(tmax);
           const bool raise_e = smax > ldexpf(1.0f, Ecur + kScaleHeadroom);   // wave-uniform
@@ -654,7 +681,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           if (g == 0) alpha_lds[64 * par + my_row] = alpha;
           if (lane == 0) flag_lds[4 * par + wave] = upd ? 1 : 0;
           const float sprime = ldexpf(1.0f, -Ecur);
-          char* pdst = pbuf + par * (kPbufBytes / 2) + (wave * 64 + lane) * 16;
+          char* pdst = pbuf + par * PPAR + (wave * 64 + lane) * PSLOT;
           if constexpr (TB == 2) {
             h8 pf;
 #pragma unroll
@@ -690,8 +717,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       if (wave == 0 && lane == 0) misc_lds[0] = Ecur;
     }
     lds_barrier();
-    constexpr float kBitScale = BITS == 16 ? 256.0f : 1.0f;
-    const float outscale = ntiles > 0 ? ldexpf(kBitScale, misc_lds[0]) : 0.0f;
+    const float outscale = ntiles > 0 ? ldexpf(1.0f, misc_lds[0]) : 0.0f;
     const bool split = E.splits > 1;
     float* part = nullptr;
     if (split) {
@@ -848,15 +874,16 @@ hipError_t launch_one(const DecodeArgs& a, int n, int lds, hipStream_t stream) {
 }  // namespace
 
 // Tile buffers per workgroup: as many as fit in the workgroup's share of the
-// 160 KB LDS, 3 to 8 (two tiles are in use, the rest in flight).
-int decode_nbuf(int row_stride, int K, int bits) {
-  const int budget = 160 * 1024 / decode_wg_per_cu(bits) - kPbufBytes - kMiscBytes;
+// 160 KB LDS, 3 to 12 (two tiles are in use, the rest in flight).
+int decode_nbuf(int row_stride, int K, int bits, int rb) {
+  const int budget = 160 * 1024 / decode_wg_per_cu(bits) - pbuf_bytes(rb, tile_blocks_of(bits)) - kMiscBytes;
   const int n = budget / tilebuf_bytes(row_stride, K, bits);
-  return n < 3 ? 3 : (n > 8 ? 8 : n);
+  return n < 3 ? 3 : (n > 12 ? 12 : n);
 }
 
-int decode_lds_bytes(int row_stride, int K, int bits) {
-  return decode_nbuf(row_stride, K, bits) * tilebuf_bytes(row_stride, K, bits) + kPbufBytes + kMiscBytes;
+int decode_lds_bytes(int row_stride, int K, int bits, int rb) {
+  return decode_nbuf(row_stride, K, bits, rb) * tilebuf_bytes(row_stride, K, bits) +
+         pbuf_bytes(rb, tile_blocks_of(bits)) + kMiscBytes;
 }
 
 hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t stream) {

@@ -185,8 +185,8 @@ kk_status make_plan(const kk_model_cfg* c, int batch, int max_len, int split_tok
       e.merge_base = merges;
       merges += e.nrc * batch;
     }
-    e.nbuf = (int16_t)kk::decode_nbuf(e.row_stride, e.d + c->d_rope, e.bits);
-    Lc.lds_bytes = std::max(Lc.lds_bytes, kk::decode_lds_bytes(e.row_stride, e.d + c->d_rope, e.bits));
+    e.nbuf = (int16_t)kk::decode_nbuf(e.row_stride, e.d + c->d_rope, e.bits, RB);
+    Lc.lds_bytes = std::max(Lc.lds_bytes, kk::decode_lds_bytes(e.row_stride, e.d + c->d_rope, e.bits, RB));
     if (Lc.lds_bytes > 160 * 1024 / kk::decode_wg_per_cu(0)) return KK_ERR_UNSUPPORTED;
     A.entries[i] = e;
     P.entry_anchor[i] = ents[i].anchor;

@@ -84,8 +84,8 @@ struct DecodeLaunch {
   int merge_blocks;
 };
 
-int decode_nbuf(int row_stride, int K, int bits);
-int decode_lds_bytes(int row_stride, int K, int bits);
+int decode_nbuf(int row_stride, int K, int bits, int row_blocks);
+int decode_lds_bytes(int row_stride, int K, int bits, int row_blocks);
 hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t stream);
 
 }  // namespace kk
