@@ -153,6 +153,22 @@ def test_inheritor_equals_one_layer_call_on_anchor_cache(kk):
         assert torch.equal(d1.layer_out(0), dec.layer_out(l)), f"inheritor {l}"
 
 
+@pytest.mark.parametrize("heads", [64, 100, 128])
+def test_many_heads_row_chunks(kk, heads):
+    """64 heads: four 16-row blocks per item; 100 and 128 heads: 64-row chunks
+    that cross layer boundaries inside an inheriting group."""
+    table = [[0, 256, 4], [0, 0, 0], [2, 128, 16], [3, 192, 8], [3, 0, 0], [3, 0, 0]]
+    w = synth.small_workload(16, len(table), heads, 2, 300, 256, 64, table)
+    lens = [300, 77]
+    model, caches, dec, ql, qr = run_gpu(kk, w, seq_lens=lens, t_cap=320)
+    worst = 0.0
+    for s in range(w.batch):
+        src = {a: source_cpu(w, a, s) for a in w.anchors()}
+        for l in range(w.n_layers):
+            worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, lens[s], src))
+    print(f"heads {heads}: worst err ratio {worst:.2e}")
+
+
 def test_outliers_and_zero_tokens(kk):
     table = [[0, 128, 2], [1, 128, 4], [2, 128, 8], [3, 128, 16]]
     w = synth.small_workload(14, 4, 16, 1, 200, 128, 32, table)
