@@ -65,7 +65,7 @@ int bits_class(int bits) { return bits == 2 ? 0 : bits == 4 ? 1 : bits == 8 ? 2 
 // and 8-bit codes (fixed per-tile work dominates), up to 1.7x for 16-bit codes,
 // which stream 2-8x the bytes (measured on MI355X).
 int64_t tile_cost(int bits, int d) { return 10 + (bits == 16 ? (7 * d + 511) / 512 : 0); }
-constexpr int kItemWaves = 3;       // waves of items over the resident slots
+constexpr int kItemWaves = 6;       // waves of items over the resident slots
 constexpr int kMinSplitTiles = 8;   // no split shorter than 8 tiles (256 tokens)
 
 // Work plan of one decode step.  Groups: an anchor and the layers inheriting
