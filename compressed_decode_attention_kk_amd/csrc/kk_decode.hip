@@ -22,7 +22,7 @@
 //      14 bits) held as two int8 limbs, so scores accumulate exactly in int32;
 //   3. online softmax in the same wave (no exchange): per-token scale and
 //      sm_scale applied in fp32, running max in the log2 domain moved lazily,
-//      P' = exp2(z - m) * scale_t * 2^-E written to LDS as fp16, with E a
+//      P' = exp2(z - m - E) * scale_t written to LDS as fp16, with E a
 //      lazily raised power-of-two bound of the scales seen;
 //   4. P.V on the fp16 MFMA, output features split over the waves in 32-wide
 //      units; codes are read transposed with ds_read_b64_tr_b{4,8,16} and
@@ -672,15 +672,15 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           int es = Ecur;
           (void)frexpf(smax, &es);
           const int enew = raise_e ? es : Ecur;
-          const float am = exp2f(m_run - mnew);
-          l_lane *= am;
-          const float alpha = am * ldexpf(1.0f, Ecur - enew);
+          // l is kept in units of 2^-E like O, so one factor rescales both
+          const float alpha = exp2f(m_run - mnew) * ldexpf(1.0f, Ecur - enew);
+          l_lane *= alpha;
           m_run = mnew;
           Ecur = enew;
           const int par = tq & 1;
           if (g == 0) alpha_lds[64 * par + my_row] = alpha;
           if (lane == 0) flag_lds[4 * par + wave] = upd ? 1 : 0;
-          const float sprime = ldexpf(1.0f, -Ecur);
+          const float mE = m_run + (float)Ecur;     // P~ = 2^(z - m - E), P' = P~ * scale_t
           char* pdst = pbuf + par * PPAR + (wave * 64 + lane) * PSLOT;
           if constexpr (TB == 2) {
             h8 pf;
@@ -688,18 +688,18 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const float e = __builtin_amdgcn_exp2f(z[tb][j] - m_run);
+                const float e = __builtin_amdgcn_exp2f(z[tb][j] - mE);
                 l_lane += e;
-                pf[4 * tb + j] = (_Float16)(e * (scv[tb][j] * sprime));
+                pf[4 * tb + j] = (_Float16)(e * scv[tb][j]);
               }
             *(h8*)pdst = pf;
           } else {
             h4 pf;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float e = __builtin_amdgcn_exp2f(z[0][j] - m_run);
+              const float e = __builtin_amdgcn_exp2f(z[0][j] - mE);
               l_lane += e;
-              pf[j] = (_Float16)(e * (scv[0][j] * sprime));
+              pf[j] = (_Float16)(e * scv[0][j]);
             }
             *(h4*)pdst = pf;
           }
@@ -717,6 +717,8 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       if (wave == 0 && lane == 0) misc_lds[0] = Ecur;
     }
     lds_barrier();
+    // O and l are in units of 2^-E: the normalized output is O / l; split
+    // partials are written in true units (O * 2^E, l * 2^E) for the merge.
     const float outscale = ntiles > 0 ? ldexpf(1.0f, misc_lds[0]) : 0.0f;
     const bool split = E.splits > 1;
     float* part = nullptr;
@@ -725,7 +727,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       part = A.ws + E.ws_off + slotp * partial_slot_floats(d);
       if (tid < 16 * RB) {
         part[64 * (int64_t)d + tid] = ml_lds[2 * tid];
-        part[64 * (int64_t)d + 64 + tid] = ml_lds[2 * tid + 1];
+        part[64 * (int64_t)d + 64 + tid] = ml_lds[2 * tid + 1] * outscale;
       }
     }
 #pragma unroll
@@ -735,7 +737,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
         const int gr = r0 + rl;
         const int layer = A.group_layers[E.lay_begin + gr / A.heads], head = gr % A.heads;
         const float lrow = ml_lds[2 * rl + 1];
-        const float fac = split ? outscale : (lrow > 0.0f ? outscale / lrow : 0.0f);
+        const float fac = split ? outscale : (lrow > 0.0f ? 1.0f / lrow : 0.0f);
         float* dst = split ? part + (int64_t)rl * d : A.out + A.layers[layer].out_off + ((int64_t)s * A.heads + head) * d;
 #pragma unroll
         for (int ui = 0; ui < UMAX; ++ui) {
