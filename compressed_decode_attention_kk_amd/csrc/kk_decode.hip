@@ -62,6 +62,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kQFrac = 13;           // query fixed point: |q'| < 1 -> |q'| * 2^13 <= 8192
 constexpr int kScaleHeadroom = 6;    // scales may exceed 2^E by 2^6 before E is raised
 constexpr int kMaxChunks64 = (kMaxK + 63) / 64;
+// Copy instructions (1 KB each) per tile: a tile holds at most 32 * K bytes of
+// codes (32 tokens of 8-bit codes or 16 tokens of 16-bit codes), shared
+// round-robin by the waves, so each wave issues at most kCopyRounds of them.
+constexpr int kCopyRounds = 5;
+static_assert((32 * kMaxK / 1024 + kWaves - 1) / kWaves <= kCopyRounds, "copy rounds too few for K");
 
 // ---- LDS map (bytes, dynamic shared memory) ----------------------------------
 //  [0, nbuf*buf)  tile buffers: codes of token block 0 [| block 1] | slack | scales
@@ -220,20 +225,36 @@ __device__ inline const void* uniform_ptr(const void* p) {
   return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Wait until at most n vector-memory operations of this wave are outstanding
-// (n is clamped to 31; a smaller count only waits longer).
+// Waits until at most n (wave-uniform, clamped to 0..63) vector memory
+// operations of this wave are outstanding.  s_waitcnt only takes an immediate,
+// so this jumps into a table of 64 "s_waitcnt vmcnt(k); s_branch end" pairs
+// (8 bytes each) at 8*k bytes past its start: two jumps per call, where a
+// compare-and-branch tree over the same cases costs five or six.  s_getpc
+// yields the address of the instruction after it, which is where the
+// label-difference offset is measured from.
+#define KK_VMW(k) "s_waitcnt vmcnt(" #k ")\n\ts_branch .Lend%=\n\t"
+#define KK_VMW10(a) \
+  KK_VMW(a##0) KK_VMW(a##1) KK_VMW(a##2) KK_VMW(a##3) KK_VMW(a##4) KK_VMW(a##5) KK_VMW(a##6) KK_VMW(a##7) KK_VMW(a##8) KK_VMW(a##9)
 __device__ inline void vm_wait(int n) {
-  // s_waitcnt immediate: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt at their maxima
-#define KK_VM(k) case k: __builtin_amdgcn_s_waitcnt(0x3f70 | ((k) & 15) | (((k) >> 4) << 14)); break;
-  switch (n) {
-    KK_VM(0) KK_VM(1) KK_VM(2) KK_VM(3) KK_VM(4) KK_VM(5) KK_VM(6) KK_VM(7)
-    KK_VM(8) KK_VM(9) KK_VM(10) KK_VM(11) KK_VM(12) KK_VM(13) KK_VM(14) KK_VM(15)
-    KK_VM(16) KK_VM(17) KK_VM(18) KK_VM(19) KK_VM(20) KK_VM(21) KK_VM(22) KK_VM(23)
-    KK_VM(24) KK_VM(25) KK_VM(26) KK_VM(27) KK_VM(28) KK_VM(29) KK_VM(30) KK_VM(31)
-    default: __builtin_amdgcn_s_waitcnt(0x3f70 | 15 | (1 << 14)); break;
-  }
-#undef KK_VM
+  const int k = __builtin_amdgcn_readfirstlane(n < 0 ? 0 : n > 63 ? 63 : n);
+  asm volatile(
+      "s_getpc_b64 s[98:99]\n"
+      ".Lpc%=:\n\t"
+      "s_lshl_b32 s97, %0, 3\n\t"
+      "s_add_u32 s98, s98, s97\n\t"
+      "s_addc_u32 s99, s99, 0\n\t"
+      "s_add_u32 s98, s98, .Ltab%=-.Lpc%=\n\t"
+      "s_addc_u32 s99, s99, 0\n\t"
+      "s_setpc_b64 s[98:99]\n"
+      ".Ltab%=:\n\t"
+      KK_VMW(0) KK_VMW(1) KK_VMW(2) KK_VMW(3) KK_VMW(4) KK_VMW(5) KK_VMW(6) KK_VMW(7) KK_VMW(8) KK_VMW(9)
+      KK_VMW10(1) KK_VMW10(2) KK_VMW10(3) KK_VMW10(4) KK_VMW10(5)
+      KK_VMW(60) KK_VMW(61) KK_VMW(62) KK_VMW(63)
+      ".Lend%=:\n" ::"s"(k)
+      : "s97", "s98", "s99", "scc", "memory");
 }
+#undef KK_VMW10
+#undef KK_VMW
 
 __device__ inline int isum_xor_16_32(int v) {
   const auto a = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
@@ -332,7 +353,10 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
     const int tok0 = it * TILE;
     const int tlast = min(TILE, ntok - tok0) - 1;
     const void* tbase = item_codes + (int64_t)tok0 * rstride;
-    for (int i = wave_u; i < ninst; i += kWaves) {
+#pragma unroll
+    for (int k = 0; k < kCopyRounds; ++k) {       // straight-line: one exit branch, not a loop
+      const int i = wave_u + kWaves * k;
+      if (i >= ninst) break;
       const int p = i * 64 + lane;
       const int tb = (TB == 2 && p >= block_pieces) ? 1 : 0;
       const int rem = p - tb * block_pieces;
@@ -394,44 +418,62 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       int qsum = 0;                               // sum of the fixed-point q of this row
       float qv[kMaxChunks64][16];
       float mx = 0.0f;
+      // The loads of every chunk are issued before any of them is used, so the
+      // query costs one memory round trip: a chunk outside the row or past K
+      // reads the (valid) first query element and is zeroed afterwards.
+      const bool row_ok = my_layer >= 0;
+      const int64_t qrow = row_ok ? ((int64_t)my_layer * A.batch + s) * A.heads + my_head : 0;
+      bool ok[kMaxChunks64];
+      int64_t off[kMaxChunks64];
+      bool lat[kMaxChunks64];
 #pragma unroll
       for (int c = 0; c < kMaxChunks64; ++c) {
         const int f0 = 64 * c + 16 * g;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) qv[c][i] = 0.0f;
-        if (my_layer >= 0 && f0 < K) {
-          const int64_t qrow = ((int64_t)my_layer * A.batch + s) * A.heads + my_head;
-          const bool lat = f0 < d;
-          const int64_t off = lat ? qrow * A.r + f0 : qrow * A.d_rope + (f0 - d);
-          const void* base = lat ? A.q_lat : A.q_rope;
-          float x[16];
-          if (A.q_is_f32) {
-            const f4* p = (const f4*)((const float*)base + off);
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const f4 a = p[v];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) x[4 * v + i] = a[i];
-            }
-          } else {
-            const u4* p = (const u4*)((const uint16_t*)base + off);
-#pragma unroll
-            for (int v = 0; v < 2; ++v) {
-              const u4 w = p[v];
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                x[8 * v + 2 * i] = __uint_as_float(w[i] << 16);
-                x[8 * v + 2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
-              }
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            qv[c][i] = x[qk_slot_feature<BITS>(i)];
-            mx = fmaxf(mx, fabsf(x[i]));
-          }
-        }
+        ok[c] = row_ok && f0 < K;
+        lat[c] = !ok[c] || f0 < d;
+        off[c] = !ok[c] ? 0 : f0 < d ? qrow * A.r + f0 : qrow * A.d_rope + (f0 - d);
       }
+      float x[kMaxChunks64][16];
+      if (A.q_is_f32) {
+        f4 raw[kMaxChunks64][4];
+#pragma unroll
+        for (int c = 0; c < kMaxChunks64; ++c) {
+          const f4* p = (const f4*)((const float*)(lat[c] ? A.q_lat : A.q_rope) + off[c]);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) raw[c][v] = p[v];
+        }
+#pragma unroll
+        for (int c = 0; c < kMaxChunks64; ++c)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[c][4 * v + i] = raw[c][v][i];
+      } else {
+        u4 raw[kMaxChunks64][2];
+#pragma unroll
+        for (int c = 0; c < kMaxChunks64; ++c) {
+          const u4* p = (const u4*)((const uint16_t*)(lat[c] ? A.q_lat : A.q_rope) + off[c]);
+#pragma unroll
+          for (int v = 0; v < 2; ++v) raw[c][v] = p[v];
+        }
+#pragma unroll
+        for (int c = 0; c < kMaxChunks64; ++c)
+#pragma unroll
+          for (int v = 0; v < 2; ++v)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              x[c][8 * v + 2 * i] = __uint_as_float(raw[c][v][i] << 16);
+              x[c][8 * v + 2 * i + 1] = __uint_as_float(raw[c][v][i] & 0xFFFF0000u);
+            }
+      }
+#pragma unroll
+      for (int c = 0; c < kMaxChunks64; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float xi = ok[c] ? x[c][qk_slot_feature<BITS>(i)] : 0.0f;
+          qv[c][i] = xi;
+          mx = fmaxf(mx, fabsf(xi));
+        }
       mx = max_xor_16_32(mx);
       int e = 0;
       if (mx > 0.0f) (void)frexpf(mx, &e);          // mx * 2^-e in [0.5, 1)
@@ -477,6 +519,11 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
         const char* buf = lds + slot_pv * bufbytes;
         const int par = st & 1;
         const char* psrc = pbuf + par * PPAR;
+        // one uniform test for the rare rescale (a branch per row block costs more)
+        int fany = 0;
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) fany |= flag_lds[4 * par + rb];
+        if (__builtin_amdgcn_readfirstlane(fany))
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           if (flag_lds[4 * par + rb]) {
