@@ -34,6 +34,7 @@
 // merges them.
 #include <hip/hip_runtime.h>
 
+#include <cfloat>
 #include <type_traits>
 
 #include "kk_internal.h"
@@ -176,13 +177,20 @@ __device__ inline i4 mfma_i8(i4 a, i4 b, i4 c) { return __builtin_amdgcn_mfma_i3
 // both operands equal, they return (row 0, row 0, row 2, row 2) and
 // (row 1, row 1, row 3, row 3) (resp. (half 0, half 0), (half 1, half 1)), so
 // op(r[0], r[1]) is the pairwise result, in the same operand order on every lane.
+// v_max_f32 on values known to be ordinary floats or infinities: fmaxf would
+// first canonicalize operands that arrive through an integer bit cast.
+__device__ inline float max_plain(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ inline float max_xor_16_32(float v) {
   const uint32_t x = __float_as_uint(v);
   const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = max_plain(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const uint32_t y = __float_as_uint(v);
   const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max_plain(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ inline float sum_xor_16_32(float v) {
   const uint32_t x = __float_as_uint(v);
@@ -406,7 +414,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
     // ---- q as two int8 limbs of a 14-bit fixed-point number per row ------------------
     // chunk c, lane (g, n): row 16*wave + n, features 64c + 16g + qk_slot_feature(i).
     i4 qh[QKW ? kMaxChunks64 : 1], ql[QKW ? kMaxChunks64 : 1];
-    float rowf = 0.0f;
+    float rowf = 1.0f;
     int qbias = 0;
     if constexpr (QKW) {
       int my_layer = -1, my_head = 0;
@@ -477,7 +485,10 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       mx = max_xor_16_32(mx);
       int e = 0;
       if (mx > 0.0f) (void)frexpf(mx, &e);          // mx * 2^-e in [0.5, 1)
-      const float pre = ldexpf(1.0f, kQFrac - e);
+      // A negative softmax scale is carried by q (z = |scale| * (-q) . k), so the
+      // row factor below is positive, as the softmax needs.
+      const float sm = my_layer >= 0 ? A.layers[my_layer].sm_scale : 0.0f;
+      const float pre = ldexpf(sm < 0.0f ? -1.0f : 1.0f, kQFrac - e);
 #pragma unroll
       for (int c = 0; c < kMaxChunks64; ++c) {
         uint32_t hw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
@@ -494,7 +505,9 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
         ql[c] = i4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
       }
       qsum = isum_xor_16_32(qsum);
-      if (my_layer >= 0) rowf = A.layers[my_layer].sm_scale * kLog2e * ldexpf(qk_code_scale<BITS>(), e - kQFrac);
+      // rowf >= FLT_MIN: a zero scale (or a padding row, q = 0) still maps the
+      // masked tokens' t = -inf to z = -inf; its logits are then below 1e-29.
+      rowf = fmaxf(fabsf(sm) * kLog2e * ldexpf(qk_code_scale<BITS>(), e - kQFrac), FLT_MIN);
       // b = 16: offset-binary bias of the low-byte operand (exact integer correction)
       qbias = BITS == 16 ? 128 * qsum : 0;
     }
@@ -684,35 +697,35 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
             default: qk_chunks(std::integral_constant<int, kMaxChunks64>{}); break;
           }
 
-          // ---- online softmax for these rows (branch-free) ----
+          // ---- online softmax for these rows ----
+          // t = integer score x token scale; the log2-domain logit is z = t * rowf
+          // with rowf > 0, so the row maximum of z is rowf times that of t.
           f4 scv[TB];
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb) scv[tb] = *(const f4*)(sc + 16 * tb + 4 * g);
-          float z[TB][4], smax = 0.0f, tmax = -INFINITY;
-          if (tvalid == TILE) {                      // every tile but an item's last: no masking
+          float t[TB][4];
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t[tb][j] = sqv[tb][j] * scv[tb][j];
+          if (tvalid < TILE) {        // an item's last tile: tokens past the end get z = -inf
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                smax = fmaxf(smax, scv[tb][j]);
-                z[tb][j] = sqv[tb][j] * rowf * scv[tb][j];
-                tmax = fmaxf(tmax, z[tb][j]);
-              }
-          } else {
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const bool valid = 16 * tb + 4 * g + j < tvalid;
-                const float st_ = valid ? scv[tb][j] : 0.0f;
-                scv[tb][j] = st_;
-                smax = fmaxf(smax, st_);
-                z[tb][j] = valid ? sqv[tb][j] * rowf * st_ : -INFINITY;
-                tmax = fmaxf(tmax, z[tb][j]);
-              }
+              for (int j = 0; j < 4; ++j)
+                if (16 * tb + 4 * g + j >= tvalid) t[tb][j] = -INFINITY;
           }
+          // (scales past the end repeat the last valid token's, so smax is unchanged)
+          float smax = 0.0f, tmax = -INFINITY;
+#pragma unroll
+          for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              smax = fmaxf(smax, scv[tb][j]);
+              tmax = fmaxf(tmax, t[tb][j]);
+            }
           smax = max_xor_16_32(smax);
-          tmax = max_xor_16_32(tmax);
+          tmax = max_xor_16_32(tmax) * rowf;
           const bool raise_e = smax > ldexpf(1.0f, Ecur + kScaleHeadroom);   // wave-uniform
           const bool upd = __any(tmax > m_run + kLazyRescale) || raise_e;    // wave-uniform
           const float mnew = upd ? fmaxf(m_run, tmax) : m_run;
@@ -735,7 +748,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const float e = __builtin_amdgcn_exp2f(z[tb][j] - mE);
+                const float e = __builtin_amdgcn_exp2f(fmaf(t[tb][j], rowf, -mE));
                 l_lane += e;
                 pf[4 * tb + j] = (_Float16)(e * scv[tb][j]);
               }
@@ -744,7 +757,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
             h4 pf;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float e = __builtin_amdgcn_exp2f(z[0][j] - mE);
+              const float e = __builtin_amdgcn_exp2f(fmaf(t[0][j], rowf, -mE));
               l_lane += e;
               pf[j] = (_Float16)(e * scv[0][j]);
             }

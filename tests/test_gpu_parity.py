@@ -169,6 +169,25 @@ def test_many_heads_row_chunks(kk, heads):
     print(f"heads {heads}: worst err ratio {worst:.2e}")
 
 
+def test_softmax_scale_sign_zero_and_extremes(kk):
+    """Per-layer softmax scales that are negative (the logits flip sign), zero
+    (uniform weights), tiny, and large (close to an argmax), on ragged lengths
+    so that the masked last tile meets each of them."""
+    from synth.gen import LayerSpec
+    table = [[0, 64, 4], [0, 0, 0], [0, 0, 0], [3, 128, 16], [3, 0, 0], [5, 96, 2]]
+    w = synth.small_workload(13, len(table), 24, 2, 300, 128, 32, table)
+    scales = [-0.09, 0.0, 0.9, -1.5, 1e-30, -0.2]
+    w.layers = [LayerSpec(x.anchor, x.d, x.bits, sc) for x, sc in zip(w.layers, scales)]
+    lens = [300, 45]
+    model, caches, dec, ql, qr = run_gpu(kk, w, seq_lens=lens, t_cap=320)
+    worst = 0.0
+    for s in range(w.batch):
+        src = {a: source_cpu(w, a, s) for a in w.anchors()}
+        for l in range(w.n_layers):
+            worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, lens[s], src))
+    print(f"softmax scales: worst err ratio {worst:.2e}")
+
+
 def test_outliers_and_zero_tokens(kk):
     table = [[0, 128, 2], [1, 128, 4], [2, 128, 8], [3, 128, 16]]
     w = synth.small_workload(14, 4, 16, 1, 200, 128, 32, table)
