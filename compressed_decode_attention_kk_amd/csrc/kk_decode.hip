@@ -16,8 +16,9 @@
 //      loads (global_load_lds), several tiles ahead (explicit vmcnt waits);
 //   2. Q.K on the integer MFMA: wave w < RB owns query rows 16w..16w+15.  The
 //      codes are used as int8 operands directly (b = 8), after a shift/mask
-//      nibble or 2-bit expansion (b = 4, 2; offset-binary with an exact bias
-//      correction), or as a signed high byte and biased low byte (b = 16).
+//      that moves each field to the top of its byte (b = 4, 2), or (b = 16)
+//      as the row's two byte planes: signed high bytes and offset-binary low
+//      bytes, with an exact integer bias correction.
 //      The query is a per-row fixed-point number (power-of-two prescale,
 //      14 bits) held as two int8 limbs, so scores accumulate exactly in int32;
 //   3. online softmax in the same wave (no exchange): per-token scale and
@@ -25,9 +26,10 @@
 //      P' = exp2(z - m - E) * scale_t written to LDS as fp16, with E a
 //      lazily raised power-of-two bound of the scales seen;
 //   4. P.V on the fp16 MFMA, output features split over the waves in 32-wide
-//      units; codes are read transposed with ds_read_b64_tr_b{4,8,16} and
+//      units; codes are read transposed with ds_read_b64_tr_b{4,8} and
 //      converted to fp16: exact integers for b <= 8 (magic-number conversion),
-//      rounded to 11 significant bits for b = 16.
+//      int16 rebuilt from the two planes and rounded to 11 significant bits
+//      for b = 16.
 // Each stage runs P.V of tile t and Q.K + softmax of tile t+1 between two
 // barriers.  Inheriting layers of a group are extra query rows of the same
 // items.  Items that were split write (m, l, O) partials; a small kernel
@@ -125,17 +127,6 @@ __device__ inline h8 cvt_b2_nib(uint32_t x) {
   return pack8(as_h2((y & 0x00030003u) ^ 0x64026402u) + bias, as_h2(((y >> 4) & 0x00030003u) ^ 0x64026402u) + bias,
                as_h2(((y >> 8) & 0x00030003u) ^ 0x64026402u) + bias, as_h2(((y >> 12) & 0x00030003u) ^ 0x64026402u) + bias);
 }
-// 8 int16 codes (w0..w3 little-endian) -> hi (signed high byte) and lo/256
-// (unsigned low byte scaled by 2^-8, exact: fp16 0x44XX = 4 + XX/256).
-__device__ inline void cvt_b16(u4 w, h8& hi, h8& lo) {
-  const h2 bh = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  const h2 bl = {(_Float16)-4.0f, (_Float16)-4.0f};
-  const u4 x = w ^ 0x80008000u;
-  hi = pack8(as_h2(perm(0x64646464u, x[0], 0x04030401u)) + bh, as_h2(perm(0x64646464u, x[1], 0x04030401u)) + bh,
-             as_h2(perm(0x64646464u, x[2], 0x04030401u)) + bh, as_h2(perm(0x64646464u, x[3], 0x04030401u)) + bh);
-  lo = pack8(as_h2(perm(0x44444444u, w[0], 0x04020400u)) + bl, as_h2(perm(0x44444444u, w[1], 0x04020400u)) + bl,
-             as_h2(perm(0x44444444u, w[2], 0x04020400u)) + bl, as_h2(perm(0x44444444u, w[3], 0x04020400u)) + bl);
-}
 
 // int8 operands for the Q.K MFMA (16 features per lane).  A b-bit two's
 // complement field moved to the top of its byte, with the bits below cleared,
@@ -153,13 +144,6 @@ __device__ inline i4 qk_b2(uint32_t x) {
 // Q.K operand scale of b-bit codes (see qk_b4 / qk_b2)
 template <int BITS>
 constexpr float qk_code_scale() { return BITS == 4 ? 1.0f / 16.0f : BITS == 2 ? 1.0f / 64.0f : 1.0f; }
-// b = 16: 16 int16 (w0..w7) -> signed high bytes and low bytes minus 128.
-__device__ inline void qk_b16(u4 a, u4 b, i4& hi, i4& lo) {
-  hi = i4{(int)perm(a[1], a[0], 0x07050301u), (int)perm(a[3], a[2], 0x07050301u),
-          (int)perm(b[1], b[0], 0x07050301u), (int)perm(b[3], b[2], 0x07050301u)};
-  lo = i4{(int)(perm(a[1], a[0], 0x06040200u) ^ 0x80808080u), (int)(perm(a[3], a[2], 0x06040200u) ^ 0x80808080u),
-          (int)(perm(b[1], b[0], 0x06040200u) ^ 0x80808080u), (int)(perm(b[3], b[2], 0x06040200u) ^ 0x80808080u)};
-}
 // feature (within a lane's 16) held by operand slot i
 template <int BITS>
 __device__ constexpr int qk_slot_feature(int i) {
@@ -369,7 +353,10 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       const int tb = (TB == 2 && p >= block_pieces) ? 1 : 0;
       const int rem = p - tb * block_pieces;
       const int seg = rem >> 4, slot = rem & 15;
-      const int t = min(16 * tb + (slot ^ (tb << 2)), tlast);
+      // token held by this slot: block 1 of a two-block tile swaps slot groups
+      // of 4; b = 16 swaps halves (slot ^ 8) in the low-byte plane
+      const int swz = BITS == 16 ? (seg >= (NSEG >> 1) ? 8 : 0) : (tb << 2);
+      const int t = min(16 * tb + (slot ^ swz), tlast);
       if (p < npos)                              // lane 0 always copies: the instruction is issued
         copy16_to_lds((uint32_t)(t * rstride + seg * 16), tbase, buf + i * 1024);
     }
@@ -598,14 +585,20 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
               u2 rv[2];
 #pragma unroll
               for (int f = 0; f < 2; ++f) {
-                const int fb = 2 * u + f, e = n >> 2, q = n & 3;
-                const int seg = 2 * fb + (q >> 1), off = 8 * (q & 1);
+                // transposed byte read of 8 rows: high-plane rows of tokens
+                // 4g..4g+3, then the low-plane rows of the same tokens; lane n
+                // gets feature 16*fb + n: high bytes in rv[0], low bytes in rv[1]
+                const int fb = 2 * u + f, k = n >> 1, h = n & 1;
+                const int seg = k < 4 ? fb : (NSEG >> 1) + fb, slot = k < 4 ? 4 * g + k : (4 * g + k - 4) ^ 8;
                 rv[f] = __builtin_bit_cast(
-                    u2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(LDS_PTR(s4, buf + tile_off(PITCH, 0, seg, 4 * g + e) + off)));
+                    u2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i2, buf + tile_off(PITCH, 0, seg, slot) + 8 * h)));
               }
 #pragma unroll
               for (int f = 0; f < 2; ++f) {
-                const h4 a = cvt_i16x4(rv[f]);
+                // int16 codes of tokens (t0, t1), (t2, t3): low byte (bit 7 restored), high byte
+                const uint32_t w0 = perm(rv[f][1], rv[f][0], 0x01050004u) ^ 0x00800080u;
+                const uint32_t w1 = perm(rv[f][1], rv[f][0], 0x03070206u) ^ 0x00800080u;
+                const h4 a = cvt_i16x4(u2{w0, w1});
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) oacc[ui][f][rb] = mfma_f16_k16(a, pfr[rb], oacc[ui][f][rb]);
               }
@@ -665,10 +658,10 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
                   acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
                   acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
                 } else {
-                  const u4 x0 = *(const u4*)p;
-                  const u4 x1 = *(const u4*)(p + 256);           // next segment of the same token
-                  i4 hi, lo;
-                  qk_b16(x0, x1, hi, lo);
+                  // byte planes: signed high bytes and offset-binary low bytes of
+                  // these 16 features are each one 16-byte row (low plane: slot n ^ 8)
+                  const i4 hi = *(const i4*)(buf + tile_off(PITCH, 0, 4 * c + g, n));
+                  const i4 lo = *(const i4*)(buf + tile_off(PITCH, 0, (NSEG >> 1) + 4 * c + g, n ^ 8));
                   acc[tb][0] = mfma_i8(hi, qh[c], acc[tb][0]);
                   acc[tb][1] = mfma_i8(hi, ql[c], acc[tb][1]);
                   acc[tb][2] = mfma_i8(lo, qh[c], acc[tb][2]);

@@ -5,7 +5,9 @@
 // rank axis (item 2) keeps the first d latent coordinates plus the RoPE key.
 //
 // One wave quantizes one token.  Lane w owns 32-bit word w of the packed row
-// (32/b consecutive fields), so the packed stores are fully coalesced.  The
+// (32/b consecutive fields), so the packed stores are fully coalesced.  For
+// b = 16 the row is two byte planes (the K high bytes, then the K low bytes
+// with bit 7 flipped): lane w's two fields go to 16-bit slots of each plane.  The
 // absmax is a wave max (exact, order independent); scale and codes use
 // IEEE fp32 division with round-to-nearest-even and rint (ties to even), so
 // the result is bit-identical to any other correct implementation of the
@@ -77,7 +79,15 @@ __global__ void __launch_bounds__(256) write_kernel(WriteArgs a) {
       }
       word |= ((uint32_t)c & ((1u << BITS) - 1u)) << (f * BITS);
     }
-    ((uint32_t*)row)[w] = word;
+    if constexpr (BITS == 16) {
+      // word = (code 2w+1 << 16) | code 2w: high bytes to plane 0, low bytes ^ 0x80 to plane 1
+      if (2 * w < K) {
+        ((uint16_t*)row)[w] = (uint16_t)(((word >> 8) & 0xFFu) | ((word >> 16) & 0xFF00u));
+        ((uint16_t*)(row + K))[w] = (uint16_t)(((word & 0xFFu) | ((word >> 8) & 0xFF00u)) ^ 0x8080u);
+      }
+    } else {
+      ((uint32_t*)row)[w] = word;
+    }
   }
   if (lane == 0) a.scales[slot] = scale;
 }

@@ -33,8 +33,12 @@
  *   codes  : uint8 [batch][t_cap][row_stride]; row = d + d_R fields of b bits,
  *            field j (latent coordinate j for j < d, RoPE coordinate j - d
  *            after) is the two's-complement code at bit offset j*b of the row,
- *            bytes little-endian; row_stride = ceil((d + d_R)*b/8 / 16) * 16,
- *            padding bytes are zero.  16-byte aligned.
+ *            bytes little-endian (b = 2, 4, 8).  b = 16 is stored as two
+ *            byte planes: bytes [0, K) hold the high bytes of fields 0..K-1,
+ *            bytes [K, 2K) their low bytes with bit 7 flipped (K = d + d_R),
+ *            so that the integer MFMA reads each plane as int8 operands.
+ *            row_stride = ceil((d + d_R)*b/8 / 16) * 16, padding bytes are
+ *            zero.  16-byte aligned.
  *   scales : float32 [batch][t_cap], one per token.  16-byte aligned.
  *   Quantization of one token v = [c[0:d] || k^R[0:d_R]] (fp32):
  *     qmax = 2^(b-1) - 1; amax = max |v_j|; scale = amax / qmax (IEEE fp32

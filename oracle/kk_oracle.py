@@ -33,6 +33,8 @@ Readings where the pages are silent (each is listed in the design doc):
 * A scale costs 32 bits per anchor layer per token on top of c(a).
 * Codes are b-bit two's-complement fields, field j at bit offset j*b of the
   row (little-endian bytes), rows zero-padded to a multiple of 16 bytes.
+  b = 16 is stored as two byte planes: the K high bytes (field order), then
+  the K low bytes with bit 7 flipped (offset binary).
 * Absorbed-MLA attention per head h: z_t = sm_scale * (q_lat[:d] . c_t[:d] +
   q_rope . k^R_t) on the dequantized cache, softmax over the cached tokens,
   o = sum_t p_t c_t[:d].  An empty cache gives o = 0.
@@ -112,8 +114,9 @@ def pack_rows(codes: np.ndarray, bits: int) -> np.ndarray:
     out = np.zeros((n, row_stride(k, bits)), dtype=np.uint8)
     mask = (1 << bits) - 1
     u = (codes & mask).astype(np.uint64)                    # two's-complement field value
-    if bits == 16:
-        out[:, :nb] = np.stack([u & 0xFF, u >> 8], axis=2).reshape(n, nb).astype(np.uint8)
+    if bits == 16:                                        # byte planes
+        out[:, :k] = (u >> np.uint64(8)).astype(np.uint8)
+        out[:, k:2 * k] = ((u & np.uint64(0xFF)) ^ np.uint64(0x80)).astype(np.uint8)
         return out
     per_byte = 8 // bits
     u = u.reshape(n, nb, per_byte)
@@ -131,7 +134,7 @@ def unpack_rows(packed: np.ndarray, bits: int, k: int) -> np.ndarray:
     nb = row_bytes(k, bits)
     b = packed[:, :nb].astype(np.int64)
     if bits == 16:
-        u = (b[:, 0::2] | (b[:, 1::2] << 8))
+        u = (b[:, k:2 * k] ^ 0x80) | (b[:, :k] << 8)
     else:
         per_byte = 8 // bits
         mask = (1 << bits) - 1

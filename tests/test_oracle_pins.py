@@ -65,8 +65,12 @@ def brute_quantize_row(v: np.ndarray, bits: int):
 
 
 def bitstring_pack(codes, bits):
-    """Row as one big little-endian integer: field j at bit j*b."""
+    """Row as one big little-endian integer: field j at bit j*b.  b = 16: the
+    high bytes of the fields in order, then their low bytes with bit 7 flipped."""
     k = len(codes)
+    if bits == 16:
+        raw = bytes(((int(c) & 0xFFFF) >> 8) for c in codes) + bytes(((int(c) & 0xFF) ^ 0x80) for c in codes)
+        return raw + bytes((len(raw) + 15) // 16 * 16 - len(raw))
     acc = 0
     for j, c in enumerate(codes):
         acc |= (int(c) & ((1 << bits) - 1)) << (j * bits)
@@ -148,6 +152,16 @@ def test_pack_worked_example_two_bit():
     # fields (1, -1, 0, 1) at 2 bits, LSB first: 01 | 11<<2 | 00<<4 | 01<<6 = 0x4D
     packed = ko.pack_rows(np.array([[1, -1, 0, 1, 0, 0, 0, 0]]), 2)
     assert packed[0, 0] == 0x4D and packed[0, 1] == 0 and packed.shape[1] == 16
+
+
+def test_pack_worked_example_sixteen_bit_planes():
+    # codes (1, -1, 256, -32767) -> high bytes 00 FF 01 80, low bytes 01 FF 00 01 with bit 7 flipped
+    codes = np.array([[1, -1, 256, -32767] + [0] * 4])
+    packed = ko.pack_rows(codes, 16)
+    assert list(packed[0, :4]) == [0x00, 0xFF, 0x01, 0x80]
+    assert list(packed[0, 8:12]) == [0x81, 0x7F, 0x80, 0x81]
+    assert list(packed[0, 4:8]) == [0, 0, 0, 0] and list(packed[0, 12:16]) == [0x80] * 4
+    assert np.array_equal(ko.unpack_rows(packed, 16, 8), codes)
 
 
 @pytest.mark.parametrize("bits,k", [(2, 48), (2, 576), (4, 48), (4, 320), (8, 48), (8, 576), (16, 48), (16, 576)])
