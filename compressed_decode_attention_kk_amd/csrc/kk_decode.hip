@@ -721,12 +721,13 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           tmax = max_xor_16_32(tmax) * rowf;
           const bool raise_e = smax > ldexpf(1.0f, Ecur + kScaleHeadroom);   // wave-uniform
           const bool upd = __any(tmax > m_run + kLazyRescale) || raise_e;    // wave-uniform
-          const float mnew = upd ? fmaxf(m_run, tmax) : m_run;
+          const float mnew = upd ? max_plain(m_run, tmax) : m_run;
           int es = Ecur;
           (void)frexpf(smax, &es);
           const int enew = raise_e ? es : Ecur;
           // l is kept in units of 2^-E like O, so one factor rescales both
-          const float alpha = exp2f(m_run - mnew) * ldexpf(1.0f, Ecur - enew);
+          // (one v_exp: m_run - mnew <= 0, Ecur - enew <= 0; results below 2^-126 are 0)
+          const float alpha = __builtin_amdgcn_exp2f((m_run - mnew) + (float)(Ecur - enew));
           l_lane *= alpha;
           m_run = mnew;
           Ecur = enew;

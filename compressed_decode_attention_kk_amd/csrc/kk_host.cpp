@@ -65,8 +65,9 @@ int bits_class(int bits) { return bits == 2 ? 0 : bits == 4 ? 1 : bits == 8 ? 2 
 // and 8-bit codes (fixed per-tile work dominates), up to 1.7x for 16-bit codes,
 // which stream 2-8x the bytes (measured on MI355X).
 int64_t tile_cost(int bits, int d) { return 10 + (bits == 16 ? (7 * d + 511) / 512 : 0); }
-constexpr int kItemWaves = 6;       // waves of items over the resident slots
+constexpr int kItemWaves = 4;       // waves of items over the resident slots (mixed tables)
 constexpr int kMinSplitTiles = 8;   // no split shorter than 8 tiles (256 tokens)
+constexpr int64_t kItemOverhead = 40;   // per-item fixed cost (query setup, pipeline fill, stores)
 
 // Work plan of one decode step.  Groups: an anchor and the layers inheriting
 // its cache.  Each group's query rows (layer-major, head-minor) form entries of
@@ -138,16 +139,33 @@ kk_status make_plan(const kk_model_cfg* c, int batch, int max_len, int split_tok
   int64_t total_cost = 0;
   for (auto& E : ents) total_cost += E.cost_tile * max_tiles * E.e.nrc * batch;
   const int64_t slots = (int64_t)kk::kCUs * kk::decode_wg_per_cu(0);
-  const int64_t target = std::max<int64_t>(1, total_cost / (kItemWaves * slots));
-  for (auto& E : ents) {
+  auto split_of = [&](const Ent& E, int waves) {
+    const int64_t target = std::max<int64_t>(1, total_cost / (waves * slots));
     int64_t sp;
     if (split_tokens > 0) sp = (max_len + split_tokens - 1) / split_tokens;
     else sp = (E.cost_tile * max_tiles + target - 1) / target;
     if (split_tokens <= 0) sp = std::min<int64_t>(sp, std::max(1, max_tiles / kMinSplitTiles));
     sp = std::max<int64_t>(1, std::min<int64_t>(sp, max_tiles));
-    sp = std::min<int64_t>(sp, kk::kMaxMergeSplits);
-    E.e.splits = (int16_t)sp;
+    return std::min<int64_t>(sp, kk::kMaxMergeSplits);
+  };
+  // Mixed tables: longest-first order leaves short items for the end, so few,
+  // long items are best (kItemWaves).  When every entry is alike, all items are
+  // equal and the last wave of items decides: pick the wave count whose items
+  // fill whole waves best, i.e. the least (waves of items) x (item time).
+  int waves = kItemWaves;
+  bool alike = split_tokens <= 0 && !ents.empty();
+  for (auto& E : ents)
+    alike = alike && E.e.bits == ents[0].e.bits && E.e.d == ents[0].e.d && E.e.nrc == ents[0].e.nrc;
+  if (alike) {
+    int64_t best = -1;
+    for (int w = 4; w <= 8; ++w) {
+      const int64_t sp = split_of(ents[0], w);
+      const int64_t n = sp * ents[0].e.nrc * batch * (int64_t)ents.size();
+      const int64_t t = ((n + slots - 1) / slots) * (((max_tiles + sp - 1) / sp) * ents[0].cost_tile + kItemOverhead);
+      if (best < 0 || t < best) { best = t; waves = w; }
+    }
   }
+  for (auto& E : ents) E.e.splits = (int16_t)split_of(E, waves);
   // Order: within a bit width, longest items first; the widths are interleaved
   // in proportion to their entry counts, so that the workgroups resident at
   // any time mix bandwidth-bound and arithmetic-bound items.
