@@ -358,7 +358,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       const int swz = BITS == 16 ? (seg >= (NSEG >> 1) ? 8 : 0) : (tb << 2);
       const int t = min(16 * tb + (slot ^ swz), tlast);
       if (p < npos)                              // lane 0 always copies: the instruction is issued
-        copy16_to_lds((uint32_t)(t * rstride + seg * 16), tbase, buf + i * 1024);
+        copy16_to_lds(__umul24(t, rstride) + seg * 16, tbase, buf + i * 1024);   // t < 32, stride <= 1152
     }
     if (wave_u == kWaves - 1 && lane < TILE)
       copy4_to_lds((uint32_t)(min(lane, tlast) * 4), item_scales + tok0, buf + TB * PITCH);
@@ -771,18 +771,22 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       if (wave == 0 && lane == 0) misc_lds[0] = Ecur;
     }
     lds_barrier();
-    // O and l are in units of 2^-E: the normalized output is O / l; split
-    // partials are written in true units (O * 2^E, l * 2^E) for the merge.
-    const float outscale = ntiles > 0 ? ldexpf(1.0f, misc_lds[0]) : 0.0f;
+    // O and l are in units of 2^-E: the normalized output is O / l.  A split
+    // writes O / l as fp16 in units of 2^(E+6) (|O / l| <= qmax * 2^(E+6), so
+    // it stays below 2^15), l in true units (l * 2^E) and m, for the merge.
+    const int Eitem = misc_lds[0];
     const bool split = E.splits > 1;
-    float* part = nullptr;
+    _Float16* part = nullptr;
     if (split) {
       const int64_t slotp = ((int64_t)(s * E.splits + ksplit) * E.nrc + chunk);
-      part = A.ws + E.ws_off + slotp * partial_slot_floats(d);
+      float* slot = A.ws + E.ws_off + slotp * partial_slot_floats(d);
+      part = (_Float16*)slot;
+      float* ml = slot + partial_ml_offset(d);
       if (tid < 16 * RB) {
-        part[64 * (int64_t)d + tid] = ml_lds[2 * tid];
-        part[64 * (int64_t)d + 64 + tid] = ml_lds[2 * tid + 1] * outscale;
+        ml[tid] = ml_lds[2 * tid];
+        ml[64 + tid] = ntiles > 0 ? ldexpf(ml_lds[2 * tid + 1], Eitem) : 0.0f;
       }
+      if (tid == 0) ml[128] = ntiles > 0 ? ldexpf(1.0f, Eitem + 6) : 0.0f;
     }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -791,8 +795,10 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
         const int gr = r0 + rl;
         const int layer = A.group_layers[E.lay_begin + gr / A.heads], head = gr % A.heads;
         const float lrow = ml_lds[2 * rl + 1];
-        const float fac = split ? outscale : (lrow > 0.0f ? 1.0f / lrow : 0.0f);
-        float* dst = split ? part + (int64_t)rl * d : A.out + A.layers[layer].out_off + ((int64_t)s * A.heads + head) * d;
+        const float inv = lrow > 0.0f ? 1.0f / lrow : 0.0f;
+        const float fac = split ? (lrow > 0.0f ? ldexpf(inv, -(Eitem + 6)) : 0.0f) : inv;
+        float* dst = split ? nullptr : A.out + A.layers[layer].out_off + ((int64_t)s * A.heads + head) * d;
+        _Float16* dsth = split ? part + (int64_t)rl * d : nullptr;
 #pragma unroll
         for (int ui = 0; ui < UMAX; ++ui) {
           const int u = ubase + ui;
@@ -801,14 +807,23 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
               const int fbase = 32 * u + 8 * g;
               if (fbase < d) {
                 const f4 e0 = oacc[ui][0][rb] * fac, e1 = oacc[ui][1][rb] * fac;
-                *(f4*)(dst + fbase) = f4{e0[0], e1[0], e0[1], e1[1]};
-                *(f4*)(dst + fbase + 4) = f4{e0[2], e1[2], e0[3], e1[3]};
+                if (split) {
+                  *(h8*)(dsth + fbase) = h8{(_Float16)e0[0], (_Float16)e1[0], (_Float16)e0[1], (_Float16)e1[1],
+                                            (_Float16)e0[2], (_Float16)e1[2], (_Float16)e0[3], (_Float16)e1[3]};
+                } else {
+                  *(f4*)(dst + fbase) = f4{e0[0], e1[0], e0[1], e1[1]};
+                  *(f4*)(dst + fbase + 4) = f4{e0[2], e1[2], e0[3], e1[3]};
+                }
               }
             } else {
 #pragma unroll
               for (int f = 0; f < 2; ++f) {
                 const int fbase = 32 * u + 16 * f + 4 * g;
-                if (fbase < d) *(f4*)(dst + fbase) = oacc[ui][f][rb] * fac;
+                if (fbase < d) {
+                  const f4 e = oacc[ui][f][rb] * fac;
+                  if (split) *(h4*)(dsth + fbase) = h4{(_Float16)e[0], (_Float16)e[1], (_Float16)e[2], (_Float16)e[3]};
+                  else *(f4*)(dst + fbase) = e;
+                }
               }
             }
           }
@@ -891,31 +906,66 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs) {
   const int64_t slotf = partial_slot_floats(d);
   const float* base = A.ws + E.ws_off + (int64_t)(s * S) * E.nrc * slotf + chunk * slotf;
   const int64_t kstride = E.nrc * slotf;
+  // o = sum_k w_k (O/l)_k with w_k = l_k 2^(m_k - M) / sum_j l_j 2^(m_j - M);
+  // the stored (O/l)_k are in units of the slot scale, folded into w_k.
+  // (one pass over the splits with a running maximum; loads of 8 splits at a time)
   for (int rl = threadIdx.x; rl < nrows; rl += 256) {
-    float M = -INFINITY;
-    for (int k = 0; k < S; ++k) {
-      const float* p = base + k * kstride + 64 * (int64_t)d;
-      if (p[64 + rl] > 0.0f) M = fmaxf(M, p[rl]);
+    float M = -INFINITY, L = 0.0f;
+    for (int k0 = 0; k0 < S; k0 += 8) {
+      float mk[8], lk[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float* p = base + min(k0 + j, S - 1) * kstride + partial_ml_offset(d);
+        mk[j] = p[rl];
+        lk[j] = k0 + j < S ? p[64 + rl] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (lk[j] > 0.0f) {
+          const float Mn = fmaxf(M, mk[j]);
+          L = L * exp2f(M - Mn) + lk[j] * exp2f(mk[j] - Mn);
+          M = Mn;
+        }
+      }
     }
-    float L = 0.0f;
     for (int k = 0; k < S; ++k) {
-      const float* p = base + k * kstride + 64 * (int64_t)d;
-      L += p[64 + rl] > 0.0f ? p[64 + rl] * exp2f(p[rl] - M) : 0.0f;
-    }
-    for (int k = 0; k < S; ++k) {
-      const float* p = base + k * kstride + 64 * (int64_t)d;
-      wgt[k][rl] = (L > 0.0f && p[64 + rl] > 0.0f) ? exp2f(p[rl] - M) / L : 0.0f;
+      const float* p = base + k * kstride + partial_ml_offset(d);
+      wgt[k][rl] = (L > 0.0f && p[64 + rl] > 0.0f) ? p[64 + rl] * exp2f(p[rl] - M) / L * p[128] : 0.0f;
     }
   }
   __syncthreads();
   const int d4 = d >> 2;
-  for (int idx = threadIdx.x; idx < nrows * d4; idx += 256) {
-    const int rl = idx / d4, f = (idx - rl * d4) * 4;
-    f4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < S; ++k) acc += *(const f4*)(base + k * kstride + (int64_t)rl * d + f) * wgt[k][rl];
-    const int gr = r0 + rl;
-    const int layer = A.group_layers[E.lay_begin + gr / A.heads], head = gr % A.heads;
-    *(f4*)(A.out + A.layers[layer].out_off + ((int64_t)s * A.heads + head) * d + f) = acc;
+  // Each thread merges 4 output vectors at once: all partial loads of a split
+  // are issued before any store (the stores could alias them for the compiler).
+  constexpr int kMergeVec = 4;
+  const int total = nrows * d4;
+  for (int i0 = threadIdx.x; i0 < total; i0 += kMergeVec * 256) {
+    int rl[kMergeVec], f[kMergeVec];
+    f4 acc[kMergeVec];
+#pragma unroll
+    for (int j = 0; j < kMergeVec; ++j) {
+      const int idx = min(i0 + 256 * j, total - 1);
+      rl[j] = idx / d4;
+      f[j] = (idx - rl[j] * d4) * 4;
+      acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+    for (int k = 0; k < S; ++k) {
+      const _Float16* pk = (const _Float16*)(base + k * kstride);
+      h4 h[kMergeVec];
+#pragma unroll
+      for (int j = 0; j < kMergeVec; ++j) h[j] = *(const h4*)(pk + (int64_t)rl[j] * d + f[j]);
+#pragma unroll
+      for (int j = 0; j < kMergeVec; ++j)
+        acc[j] += f4{(float)h[j][0], (float)h[j][1], (float)h[j][2], (float)h[j][3]} * wgt[k][rl[j]];
+    }
+#pragma unroll
+    for (int j = 0; j < kMergeVec; ++j) {
+      if (i0 + 256 * j < total) {
+        const int gr = r0 + rl[j];
+        const int layer = A.group_layers[E.lay_begin + gr / A.heads], head = gr % A.heads;
+        *(f4*)(A.out + A.layers[layer].out_off + ((int64_t)s * A.heads + head) * d + f[j]) = acc[j];
+      }
+    }
   }
 }
 

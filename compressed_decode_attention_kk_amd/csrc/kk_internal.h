@@ -61,8 +61,13 @@ struct DecodeArgs {
   EntryArg entries[kMaxEntries];
 };
 
-// Partial slot of one work item in the workspace: O [64][d] then m[64], l[64].
-__host__ __device__ inline int64_t partial_slot_floats(int d) { return 64 * (int64_t)d + 128; }
+// Partial slot of one work item in the workspace (float offsets):
+//   [0, 32d)        O/l as fp16 [64 rows][d], in units of the slot scale
+//   32d + [0, 64)   m, the row max (log2 domain)
+//   32d + [64, 128) l, the row sum of 2^(z - m)
+//   32d + 128       the slot scale 2^(E+6) (E bounds the item's token scales)
+__host__ __device__ inline int64_t partial_slot_floats(int d) { return 32 * (int64_t)d + 192; }
+__host__ __device__ inline int64_t partial_ml_offset(int d) { return 32 * (int64_t)d; }
 
 struct WriteArgs {
   const void* latent;
