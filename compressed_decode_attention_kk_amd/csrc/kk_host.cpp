@@ -67,6 +67,7 @@ int bits_class(int bits) { return bits == 2 ? 0 : bits == 4 ? 1 : bits == 8 ? 2 
 int64_t tile_cost(int bits, int d) { return 10 + (bits == 16 ? (7 * d + 511) / 512 : 0); }
 constexpr int kItemWaves = 4;       // waves of items over the resident slots (mixed tables)
 constexpr int kMinSplitTiles = 8;   // no split shorter than 8 tiles (256 tokens)
+constexpr int64_t kTailPercent = 15;  // share of the work (last dispatched) cut twice as fine
 constexpr int64_t kItemOverhead = 40;   // per-item fixed cost (query setup, pipeline fill, stores)
 
 // Work plan of one decode step.  Groups: an anchor and the layers inheriting
@@ -184,6 +185,18 @@ kk_status make_plan(const kk_model_cfg* c, int batch, int max_len, int split_tok
     std::stable_sort(ents.begin(), ents.end(), [](const Ent& x, const Ent& y) {
       return (int64_t)x.key_num * y.key_den < (int64_t)y.key_num * x.key_den;
     });
+  }
+  // Tail: the last items dispatched decide how evenly the slots finish, so the
+  // entries holding the last kTailPercent of the work are cut twice as fine.
+  if (!alike && split_tokens <= 0) {
+    int64_t acc = 0;
+    const int64_t tail_from = total_cost - total_cost * kTailPercent / 100;
+    for (auto& E : ents) {
+      if (acc >= tail_from)
+        E.e.splits = (int16_t)std::min<int64_t>({2 * (int64_t)E.e.splits, std::max(1, max_tiles / kMinSplitTiles),
+                                                 (int64_t)kk::kMaxMergeSplits});
+      acc += E.cost_tile * max_tiles * E.e.nrc * batch;
+    }
   }
   int64_t items = 0, ws = 0;
   int merges = 0;
