@@ -168,6 +168,8 @@ def main():
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--append", action="store_true",
+                    help="time kk_append_decode (write each sequence's newest token into every anchor, then decode)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run 3 device-to-device copies of this size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -204,12 +206,19 @@ def main():
     ql, qr = synth.queries(w, "cuda")
     seq_lens = torch.full((w.batch,), w.seq_len, dtype=torch.int32, device="cuda")
     dec = kk.Decoder(model, caches, w.batch, w.seq_len, w.seq_len, split_tokens=args.split_tokens)
+    step = lambda: dec(ql, qr, seq_lens)
+    if args.append:
+        # the newest token of each sequence (row seq_len - 1) is rewritten from seeded rows every step
+        g = torch.Generator(device="cuda").manual_seed(1234)
+        new_lat = torch.randn(w.n_layers, w.batch, w.r, generator=g, device="cuda")
+        new_rope = torch.randn(w.n_layers, w.batch, w.d_rope, generator=g, device="cuda")
+        step = lambda: dec.append(new_lat, new_rope, ql, qr, seq_lens)
     torch.cuda.synchronize()
     print(f"[bench] setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
-        dec(ql, qr, seq_lens)
+        step()
     torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
@@ -217,7 +226,7 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
-        dec(ql, qr, seq_lens)
+        step()
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -266,8 +275,10 @@ def main():
         "config": {"workload": w.name, "layers": w.n_layers, "heads": w.n_heads, "batch": w.batch,
                    "cached_tokens": w.seq_len, "r": w.r, "d_rope": w.d_rope, "anchors": len(anchors),
                    "bits_per_token": bits_tok, "q_dtype": str(w.q_dtype).replace("torch.", ""),
-                   "split_tokens": args.split_tokens or "auto", "parallelism": "none (one GPU)"},
-        "roofline": {"bound": "hbm", "kernel": "decode step: decode_kernel + merge_kernel",
+                   "split_tokens": args.split_tokens or "auto", "parallelism": "none (one GPU)",
+                   "step": "append + decode" if args.append else "decode"},
+        "roofline": {"bound": "hbm", "kernel": ("append_kernel + " if args.append else "") +
+                     "decode step: decode_kernel + merge_kernel",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_step": U, "device_ms_per_step": mean_dev_ms,

@@ -314,10 +314,12 @@ kk_status kk_decode_workspace_bytes(const kk_model_cfg* cfg, int32_t batch, int3
   return KK_OK;
 }
 
-kk_status kk_decode_attn(const kk_model_cfg* cfg, const kk_cache* caches, int32_t batch, int32_t t_cap,
+namespace {
+// Argument checks and work plan of one decode step (nothing is enqueued).
+kk_status prepare_decode(const kk_model_cfg* cfg, const kk_cache* caches, int32_t batch, int32_t t_cap,
                          const int32_t* seq_lens, int32_t max_seq_len, const void* q_lat, const void* q_rope,
                          kk_dtype q_dtype, float* out, int32_t split_tokens, void* workspace, size_t workspace_bytes,
-                         hipStream_t stream) {
+                         Plan& P) {
   kk_status st = check_model(cfg);
   if (st != KK_OK) return st;
   if (!caches || batch < 1 || t_cap < 1 || max_seq_len < 0 || max_seq_len > t_cap) return KK_ERR_INVALID_ARGUMENT;
@@ -332,7 +334,6 @@ kk_status kk_decode_attn(const kk_model_cfg* cfg, const kk_cache* caches, int32_
     if (!aligned(caches[l].codes, 16) || !aligned(caches[l].scales, 16)) return KK_ERR_INVALID_ARGUMENT;
   }
   if ((int64_t)cfg->n_layers * batch * cfg->n_heads > ((int64_t)1 << 31)) return KK_ERR_UNSUPPORTED;
-  Plan P;
   st = make_plan(cfg, batch, max_seq_len, split_tokens, P);
   if (st != KK_OK) return st;
   const size_t need = (size_t)P.ws_floats * sizeof(float);
@@ -357,7 +358,57 @@ kk_status kk_decode_attn(const kk_model_cfg* cfg, const kk_cache* caches, int32_
   A.d_rope = cfg->d_rope;
   A.t_cap = t_cap;
   A.q_is_f32 = q_dtype == KK_DTYPE_F32;
-  return kk::launch_decode(A, P.launch, stream) == hipSuccess ? KK_OK : KK_ERR_DEVICE;
+  return KK_OK;
+}
+}  // namespace
+
+kk_status kk_decode_attn(const kk_model_cfg* cfg, const kk_cache* caches, int32_t batch, int32_t t_cap,
+                         const int32_t* seq_lens, int32_t max_seq_len, const void* q_lat, const void* q_rope,
+                         kk_dtype q_dtype, float* out, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  Plan P;
+  const kk_status st = prepare_decode(cfg, caches, batch, t_cap, seq_lens, max_seq_len, q_lat, q_rope, q_dtype, out,
+                                      split_tokens, workspace, workspace_bytes, P);
+  if (st != KK_OK) return st;
+  return kk::launch_decode(P.args, P.launch, stream) == hipSuccess ? KK_OK : KK_ERR_DEVICE;
+}
+
+kk_status kk_append_decode(const kk_model_cfg* cfg, const kk_cache* caches, int32_t batch, int32_t t_cap,
+                           const int32_t* seq_lens, int32_t max_seq_len, const void* new_latent,
+                           const void* new_rope, kk_dtype src_dtype, const void* q_lat, const void* q_rope,
+                           kk_dtype q_dtype, float* out, int32_t split_tokens, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  // every check of both steps runs before anything is enqueued
+  Plan P;
+  kk_status st = prepare_decode(cfg, caches, batch, t_cap, seq_lens, max_seq_len, q_lat, q_rope, q_dtype, out,
+                                split_tokens, workspace, workspace_bytes, P);
+  if (st != KK_OK) return st;
+  if (src_dtype != KK_DTYPE_F32 && src_dtype != KK_DTYPE_BF16) return KK_ERR_INVALID_ARGUMENT;
+  const size_t ea = src_dtype == KK_DTYPE_F32 ? 4 : 2;
+  if (!new_latent || !new_rope || !aligned(new_latent, ea) || !aligned(new_rope, ea)) return KK_ERR_INVALID_ARGUMENT;
+  kk::AppendArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.latent = new_latent;
+  a.rope = new_rope;
+  a.seq_lens = seq_lens;
+  a.latent_ld = cfg->r;
+  a.rope_ld = cfg->d_rope;
+  a.batch = batch;
+  a.t_cap = t_cap;
+  a.d_rope = cfg->d_rope;
+  a.src_bf16 = src_dtype == KK_DTYPE_BF16;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    if (cfg->layers[l].anchor != l) continue;
+    kk::AppendAnchor& x = a.anchors[a.n_anchors++];
+    x.codes = caches[l].codes;
+    x.scales = caches[l].scales;
+    x.layer = l;
+    x.d = cfg->layers[l].d;
+    x.bits = cfg->layers[l].bits;
+    x.row_stride = (int32_t)stride_of(x.d, cfg->d_rope, x.bits);
+  }
+  if (kk::launch_append(a, stream) != hipSuccess) return KK_ERR_DEVICE;
+  return kk::launch_decode(P.args, P.launch, stream) == hipSuccess ? KK_OK : KK_ERR_DEVICE;
 }
 
 const char* kk_status_string(kk_status s) {

@@ -81,6 +81,22 @@ struct WriteArgs {
 };
 
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
+
+// Append of one token per sequence to every anchor cache (see kk_append_decode).
+struct AppendAnchor {
+  uint8_t* codes;
+  float* scales;
+  int32_t layer, d, bits, row_stride;
+};
+struct AppendArgs {
+  const void* latent;        // [n_layers][batch][latent_ld]
+  const void* rope;          // [n_layers][batch][rope_ld]
+  const int32_t* seq_lens;   // lengths after the append
+  int64_t latent_ld, rope_ld;
+  int32_t n_anchors, batch, t_cap, d_rope, src_bf16;
+  AppendAnchor anchors[kMaxLayers];
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // One decode launch covers every work item of the step (all bit widths).
 struct DecodeLaunch {
   int items;

@@ -27,19 +27,16 @@ __device__ inline float load_src(const void* p, int64_t idx, int bf16) {
   return ((const float*)p)[idx];
 }
 
+// Quantizes one token (the wave's 64 lanes) from its source rows and packs it
+// into `row` with its scale at *scale_out.  The source rows hold the latent
+// (first d used) and the RoPE key (d_rope), fp32 or bf16.
 template <int BITS>
-__global__ void __launch_bounds__(256) write_kernel(WriteArgs a) {
+__device__ inline void quantize_token(const void* lat_row, const void* rope_row, int bf16, int d, int d_rope,
+                                      int row_stride, uint8_t* row, float* scale_out, int lane) {
   constexpr int kFields = 32 / BITS;              // fields per 32-bit word
   constexpr int kMaxWords = (640 * BITS / 32 + 63) / 64;   // words per lane (K <= 640)
-  const int lane = threadIdx.x & 63;
-  const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tok >= a.n_tokens) return;
-  const int64_t src = a.src_index ? (int64_t)a.src_index[tok] : tok;
-  const int64_t slot = a.dst_slot[tok];
-  if (src < 0 || src >= a.n_src || slot < 0 || slot >= a.n_slots) return;
-
-  const int K = a.d + a.d_rope;
-  const int words = a.row_stride >> 2;
+  const int K = d + d_rope;
+  const int words = row_stride >> 2;
   float v[kMaxWords][kFields];
   float amax = 0.0f;
 #pragma unroll
@@ -49,10 +46,7 @@ __global__ void __launch_bounds__(256) write_kernel(WriteArgs a) {
     for (int f = 0; f < kFields; ++f) {
       const int j = w * kFields + f;
       float x = 0.0f;
-      if (w < words && j < K) {
-        x = j < a.d ? load_src(a.latent, src * a.latent_ld + j, a.src_bf16)
-                    : load_src(a.rope, src * a.rope_ld + (j - a.d), a.src_bf16);
-      }
+      if (w < words && j < K) x = j < d ? load_src(lat_row, j, bf16) : load_src(rope_row, j - d, bf16);
       v[wi][f] = x;
       amax = fmaxf(amax, fabsf(x));
     }
@@ -62,7 +56,6 @@ __global__ void __launch_bounds__(256) write_kernel(WriteArgs a) {
 
   const float qmax = (float)((1 << (BITS - 1)) - 1);
   const float scale = __fdiv_rn(amax, qmax);
-  uint8_t* row = a.codes + slot * a.row_stride;
 #pragma unroll
   for (int wi = 0; wi < kMaxWords; ++wi) {
     const int w = lane + 64 * wi;
@@ -89,7 +82,45 @@ __global__ void __launch_bounds__(256) write_kernel(WriteArgs a) {
       ((uint32_t*)row)[w] = word;
     }
   }
-  if (lane == 0) a.scales[slot] = scale;
+  if (lane == 0) *scale_out = scale;
+}
+
+template <int BITS>
+__global__ void __launch_bounds__(256) write_kernel(WriteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= a.n_tokens) return;
+  const int64_t src = a.src_index ? (int64_t)a.src_index[tok] : tok;
+  const int64_t slot = a.dst_slot[tok];
+  if (src < 0 || src >= a.n_src || slot < 0 || slot >= a.n_slots) return;
+  const size_t es = a.src_bf16 ? 2 : 4;
+  quantize_token<BITS>((const char*)a.latent + src * a.latent_ld * es, (const char*)a.rope + src * a.rope_ld * es,
+                       a.src_bf16, a.d, a.d_rope, a.row_stride, a.codes + slot * a.row_stride, a.scales + slot, lane);
+}
+
+// Append: one wave per (anchor, sequence) writes the sequence's new token at
+// row seq_lens[s] - 1 of the anchor's cache (nothing when that is outside
+// [0, t_cap)).  The bit width is uniform per wave.
+__global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t w = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= (int64_t)a.n_anchors * a.batch) return;
+  const int j = (int)(w / a.batch), s = (int)(w - (int64_t)j * a.batch);
+  const int pos = a.seq_lens[s] - 1;
+  if (pos < 0 || pos >= a.t_cap) return;
+  const AppendAnchor& A = a.anchors[j];
+  const size_t es = a.src_bf16 ? 2 : 4;
+  const int64_t src = (int64_t)A.layer * a.batch + s;
+  const char* lat = (const char*)a.latent + src * a.latent_ld * es;
+  const char* rope = (const char*)a.rope + src * a.rope_ld * es;
+  const int64_t slot = (int64_t)s * a.t_cap + pos;
+  uint8_t* row = A.codes + slot * A.row_stride;
+  switch (A.bits) {
+    case 2: quantize_token<2>(lat, rope, a.src_bf16, A.d, a.d_rope, A.row_stride, row, A.scales + slot, lane); break;
+    case 4: quantize_token<4>(lat, rope, a.src_bf16, A.d, a.d_rope, A.row_stride, row, A.scales + slot, lane); break;
+    case 8: quantize_token<8>(lat, rope, a.src_bf16, A.d, a.d_rope, A.row_stride, row, A.scales + slot, lane); break;
+    default: quantize_token<16>(lat, rope, a.src_bf16, A.d, a.d_rope, A.row_stride, row, A.scales + slot, lane); break;
+  }
 }
 
 }  // namespace
@@ -104,6 +135,13 @@ hipError_t launch_write(const WriteArgs& a, hipStream_t stream) {
     case 16: hipLaunchKernelGGL(write_kernel<16>, grid, block, 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+  const int64_t waves = (int64_t)a.n_anchors * a.batch;
+  if (waves <= 0) return hipSuccess;
+  hipLaunchKernelGGL(append_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -67,10 +67,15 @@ def lib():
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p]
+        L.kk_append_decode.argtypes = [ctypes.POINTER(ModelCfg), ctypes.POINTER(Cache), ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
         L.kk_status_string.restype = ctypes.c_char_p
         L.kk_status_string.argtypes = [ctypes.c_int]
         for name in ("kk_validate_model", "kk_cache_bytes", "kk_out_offsets", "kk_quantize_write",
-                     "kk_decode_workspace_bytes", "kk_decode_attn"):
+                     "kk_decode_workspace_bytes", "kk_decode_attn", "kk_append_decode"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -221,6 +226,27 @@ class Decoder:
                                   _ptr(q_lat), _ptr(q_rope), _dtype_code(q_lat.dtype), _ptr(self.out),
                                   self.split_tokens, ctypes.c_void_p(wptr), self.ws_bytes, _stream(stream))
         _check(st, "kk_decode_attn")
+        return self.out
+
+    def append(self, new_latent: torch.Tensor, new_rope: torch.Tensor, q_lat: torch.Tensor, q_rope: torch.Tensor,
+               seq_lens: torch.Tensor, stream=None):
+        """kk_append_decode: write each sequence's new token (row seq_lens[s] - 1) into
+        every anchor cache, then decode over the extended caches.  new_latent
+        [n_layers, batch, r] and new_rope [n_layers, batch, d_rope], one dtype."""
+        m = self.model
+        assert new_latent.is_contiguous() and new_rope.is_contiguous() and new_latent.dtype == new_rope.dtype
+        assert tuple(new_latent.shape) == (m.n_layers, self.batch, m.r)
+        assert tuple(new_rope.shape) == (m.n_layers, self.batch, m.d_rope)
+        assert q_lat.is_contiguous() and q_rope.is_contiguous() and q_lat.dtype == q_rope.dtype
+        assert tuple(q_lat.shape) == (m.n_layers, self.batch, m.n_heads, m.r)
+        assert tuple(q_rope.shape) == (m.n_layers, self.batch, m.n_heads, m.d_rope)
+        assert seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.numel() == self.batch
+        wptr = (self.workspace.data_ptr() + 255) // 256 * 256
+        st = lib().kk_append_decode(m.cfg, self._ctab, self.batch, self.t_cap, _ptr(seq_lens), self.max_seq_len,
+                                    _ptr(new_latent), _ptr(new_rope), _dtype_code(new_latent.dtype),
+                                    _ptr(q_lat), _ptr(q_rope), _dtype_code(q_lat.dtype), _ptr(self.out),
+                                    self.split_tokens, ctypes.c_void_p(wptr), self.ws_bytes, _stream(stream))
+        _check(st, "kk_append_decode")
         return self.out
 
     def layer_out(self, l: int) -> torch.Tensor:

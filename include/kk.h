@@ -176,6 +176,29 @@ kk_status kk_decode_attn(const kk_model_cfg* cfg, const kk_cache* caches, int32_
                          int32_t split_tokens, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/* One generated token per sequence: append it to every anchor cache, then
+ * attend (the decode step right after the write; KV-Kaizen summary page,
+ * "Background: The KV Cache Bottleneck": every new token is cached and then
+ * the whole cache is read).
+ *
+ * seq_lens   : device int32 [batch], lengths AFTER the append.  For each s
+ *              with 1 <= seq_lens[s] <= t_cap and each anchor a, row
+ *              seq_lens[s] - 1 of sequence s in a's cache is written with the
+ *              quantized [new_latent[a][s][0:d_a] || new_rope[a][s]] (as
+ *              kk_quantize_write would); other sequences append nothing.
+ * new_latent : device [n_layers][batch][r], src_dtype (rows of inheriting
+ *              layers are not read).
+ * new_rope   : device [n_layers][batch][d_rope], src_dtype.
+ * Every other argument is as for kk_decode_attn, which then runs over the
+ * extended caches.  All checks of both steps happen before anything is
+ * enqueued; the write and the decode go to `stream` in that order (two
+ * launches, no host synchronization). */
+kk_status kk_append_decode(const kk_model_cfg* cfg, const kk_cache* caches, int32_t batch, int32_t t_cap,
+                           const int32_t* seq_lens, int32_t max_seq_len, const void* new_latent,
+                           const void* new_rope, kk_dtype src_dtype, const void* q_lat, const void* q_rope,
+                           kk_dtype q_dtype, float* out, int32_t split_tokens, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code. */
 const char* kk_status_string(kk_status status);
 

@@ -33,7 +33,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kk_quantize_write", "kk_decode_attn", "kk_decode_workspace_bytes", "kk_cache_bytes",
-              "kk_out_offsets", "kk_validate_model", "kk_row_stride_bytes", "kk_status_string"):
+              "kk_out_offsets", "kk_validate_model", "kk_row_stride_bytes", "kk_status_string",
+              "kk_append_decode"):
         assert n in names
 
 
@@ -180,6 +181,34 @@ def test_decode_attn_rejects_bad_arguments_before_launch(kk):
     assert call(caches=bad) == kk.KK_ERR_INVALID_ARGUMENT
     bad[2] = kk.Cache(fake(3, 8).value, fake(4).value)                 # codes not 16-byte aligned
     assert call(caches=bad) == kk.KK_ERR_INVALID_ARGUMENT
+
+
+def test_append_decode_rejects_bad_arguments_before_launch(kk):
+    L = kk.lib()
+    rows = [[0, 128, 4], [0, 0, 0], [2, 64, 8]]
+    m = table(rows, r=128, dr=32, heads=16, kk=kk)
+    fake = _Fake()
+    caches = (kk.Cache * 3)()
+    caches[0] = kk.Cache(fake(1).value, fake(2).value)
+    caches[2] = kk.Cache(fake(3).value, fake(4).value)
+    B, T = 4, 1024
+    need = kk.workspace_bytes(m, B, T, 64)
+
+    def call(**kw):
+        a = dict(lat=fake(10), rope=fake(11), src=kk.KK_DTYPE_F32, ws_bytes=need, q_dtype=kk.KK_DTYPE_BF16,
+                 caches=caches)
+        a.update(kw)
+        return L.kk_append_decode(m.cfg, a["caches"], B, T, fake(5), T, a["lat"], a["rope"], a["src"], fake(6),
+                                  fake(7), a["q_dtype"], fake(8), 64, fake(9), a["ws_bytes"], None)
+
+    assert call(src=3) == kk.KK_ERR_INVALID_ARGUMENT                   # source dtype
+    assert call(lat=None) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(rope=fake(11, 2)) == kk.KK_ERR_INVALID_ARGUMENT        # f32 rows not 4-byte aligned
+    assert call(ws_bytes=need - 1) == kk.KK_ERR_WORKSPACE_TOO_SMALL    # decode checks come first
+    assert call(q_dtype=9) == kk.KK_ERR_INVALID_ARGUMENT
+    bad = (kk.Cache * 3)()
+    bad[0] = caches[0]
+    assert call(caches=bad) == kk.KK_ERR_INVALID_ARGUMENT             # anchor 2 has no buffers
 
 
 def test_quantize_write_rejects_bad_arguments_before_launch(kk):

@@ -188,6 +188,50 @@ def test_softmax_scale_sign_zero_and_extremes(kk):
     print(f"softmax scales: worst err ratio {worst:.2e}")
 
 
+def test_append_then_attend(kk):
+    """kk_append_decode writes each sequence's next token into every anchor
+    cache (row seq_lens[s] - 1 of the lengths after the append) and decodes: the
+    caches equal the plain writer's for the new lengths, the output equals a
+    separate kk_decode_attn on them bit for bit, and both match the oracle.
+    A sequence of length 0 after the append writes nothing and gives zeros."""
+    table = [[0, 96, 4], [0, 0, 0], [2, 64, 16], [3, 128, 2], [3, 0, 0], [5, 64, 8]]
+    w = synth.small_workload(14, len(table), 24, 5, 128, 128, 32, table, q_dtype=torch.float32)
+    before, after = [100, 31, 0, 127, 0], [101, 32, 1, 128, 0]
+    model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+    caches = build_caches(kk, model, w, 128, seq_lens=before)
+    new_lat = torch.zeros(w.n_layers, w.batch, w.r, dtype=torch.float32, device="cuda")
+    new_rope = torch.zeros(w.n_layers, w.batch, w.d_rope, dtype=torch.float32, device="cuda")
+    for a in w.anchors():
+        lat, rope, _ = synth.source_rows(w, a, "cuda")
+        for s in range(w.batch):
+            if after[s] > 0:
+                new_lat[a, s] = lat[s, after[s] - 1]
+                new_rope[a, s] = rope[s, after[s] - 1]
+    ql, qr = synth.queries(w, "cuda")
+    sl = torch.tensor(after, dtype=torch.int32, device="cuda")
+    dec = kk.Decoder(model, caches, w.batch, 128, 128)
+    dec.append(new_lat, new_rope, ql, qr, sl)
+    torch.cuda.synchronize()
+    ref_caches = build_caches(kk, model, w, 128, seq_lens=after)
+    for a in w.anchors():
+        assert torch.equal(caches[a][0], ref_caches[a][0]), f"codes of anchor {a}"
+        assert torch.equal(caches[a][1].view(torch.int32), ref_caches[a][1].view(torch.int32)), f"scales of anchor {a}"
+    ref = kk.Decoder(model, ref_caches, w.batch, 128, 128)
+    ref(ql, qr, sl)
+    torch.cuda.synchronize()
+    assert torch.equal(dec.out, ref.out)
+    worst = 0.0
+    for s in range(w.batch):
+        if after[s] == 0:
+            for l in range(w.n_layers):
+                assert torch.all(dec.layer_out(l)[s] == 0)
+            continue
+        src = {a: source_cpu(w, a, s) for a in w.anchors()}
+        for l in range(w.n_layers):
+            worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, after[s], src))
+    print(f"append then attend: worst err ratio {worst:.2e}")
+
+
 def test_outliers_and_zero_tokens(kk):
     table = [[0, 128, 2], [1, 128, 4], [2, 128, 8], [3, 128, 16]]
     w = synth.small_workload(14, 4, 16, 1, 200, 128, 32, table)
