@@ -519,21 +519,29 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
         const char* buf = lds + slot_pv * bufbytes;
         const int par = st & 1;
         const char* psrc = pbuf + par * PPAR;
-        // one uniform test for the rare rescale (a branch per row block costs more)
-        int fany = 0;
+        // Rescale flags of this tile's rows: read here, tested only after the
+        // P.V operand reads are issued, so that the two LDS round trips overlap.
+        // One uniform test for the rare rescale (a branch per row block costs more).
+        int fl[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) fany |= flag_lds[4 * par + rb];
-        if (__builtin_amdgcn_readfirstlane(fany))
+        for (int rb = 0; rb < RB; ++rb) fl[rb] = flag_lds[4 * par + rb];
+        auto rescale = [&](auto uw) {
+          constexpr int UW = decltype(uw)::value;
+          int fany = 0;
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-          if (flag_lds[4 * par + rb]) {
-            const float al = alpha_lds[64 * par + 16 * rb + n];
+          for (int rb = 0; rb < RB; ++rb) fany |= fl[rb];
+          if (__builtin_amdgcn_readfirstlane(fany))
 #pragma unroll
-            for (int u = 0; u < UMAX; ++u)
+            for (int rb = 0; rb < RB; ++rb) {
+              if (fl[rb]) {
+                const float al = alpha_lds[64 * par + 16 * rb + n];
 #pragma unroll
-              for (int f = 0; f < 2; ++f) oacc[u][f][rb] *= al;
-          }
-        }
+                for (int u = 0; u < UW; ++u)
+#pragma unroll
+                  for (int f = 0; f < 2; ++f) oacc[u][f][rb] *= al;
+              }
+            }
+        };
         auto pv_units = [&](auto uw) {
           constexpr int UW = decltype(uw)::value;
           if constexpr (TB == 2) {
@@ -560,6 +568,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
                 rv[ui][0] = __builtin_bit_cast(u2, __builtin_amdgcn_ds_read_tr4_b64_v2i32(LDS_PTR(i2, p)));
               }
             }
+            rescale(uw);
 #pragma unroll
             for (int ui = 0; ui < UW; ++ui) {
               h8 a[2];
@@ -579,10 +588,10 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
             h4 pfr[RB];
 #pragma unroll
             for (int rb = 0; rb < RB; ++rb) pfr[rb] = *(const h4*)(psrc + (rb * 64 + lane) * PSLOT);
+            u2 rv[UW][2];
 #pragma unroll
             for (int ui = 0; ui < UW; ++ui) {
               const int u = ubase + ui;
-              u2 rv[2];
 #pragma unroll
               for (int f = 0; f < 2; ++f) {
                 // transposed byte read of 8 rows: high-plane rows of tokens
@@ -590,14 +599,18 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
                 // gets feature 16*fb + n: high bytes in rv[0], low bytes in rv[1]
                 const int fb = 2 * u + f, k = n >> 1, h = n & 1;
                 const int seg = k < 4 ? fb : (NSEG >> 1) + fb, slot = k < 4 ? 4 * g + k : (4 * g + k - 4) ^ 8;
-                rv[f] = __builtin_bit_cast(
+                rv[ui][f] = __builtin_bit_cast(
                     u2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(LDS_PTR(i2, buf + tile_off(PITCH, 0, seg, slot) + 8 * h)));
               }
+            }
+            rescale(uw);
+#pragma unroll
+            for (int ui = 0; ui < UW; ++ui) {
 #pragma unroll
               for (int f = 0; f < 2; ++f) {
                 // int16 codes of tokens (t0, t1), (t2, t3): low byte (bit 7 restored), high byte
-                const uint32_t w0 = perm(rv[f][1], rv[f][0], 0x01050004u) ^ 0x00800080u;
-                const uint32_t w1 = perm(rv[f][1], rv[f][0], 0x03070206u) ^ 0x00800080u;
+                const uint32_t w0 = perm(rv[ui][f][1], rv[ui][f][0], 0x01050004u) ^ 0x00800080u;
+                const uint32_t w1 = perm(rv[ui][f][1], rv[ui][f][0], 0x03070206u) ^ 0x00800080u;
                 const h4 a = cvt_i16x4(u2{w0, w1});
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb) oacc[ui][f][rb] = mfma_f16_k16(a, pfr[rb], oacc[ui][f][rb]);
@@ -628,11 +641,15 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           // leading term, below the 14-bit rounding of q itself.
           constexpr int NACC = BITS == 16 ? 3 : 2;
           float sqv[TB][4];                         // integer scores (exact in fp32 for b < 16)
+          f4 scv[TB];                               // this lane's 4 token scales per token block
           // The chunk count is a compile-time constant in each case below, so every
           // LDS read of the tile is straight-line code the scheduler can hoist
           // ahead of the MFMAs that consume it.
           auto qk_chunks = [&](auto nc) {
             constexpr int NC = decltype(nc)::value;
+            // the scales are read with the codes, not after the MFMAs
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) scv[tb] = *(const f4*)(sc + 16 * tb + 4 * g);
             i4 acc[TB][NACC];
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb)
@@ -693,9 +710,6 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           // ---- online softmax for these rows ----
           // t = integer score x token scale; the log2-domain logit is z = t * rowf
           // with rowf > 0, so the row maximum of z is rowf times that of t.
-          f4 scv[TB];
-#pragma unroll
-          for (int tb = 0; tb < TB; ++tb) scv[tb] = *(const f4*)(sc + 16 * tb + 4 * g);
           float t[TB][4];
 #pragma unroll
           for (int tb = 0; tb < TB; ++tb)
