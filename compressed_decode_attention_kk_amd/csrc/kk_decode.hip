@@ -256,9 +256,12 @@ __device__ inline int isum_xor_16_32(int v) {
 }
 
 // Byte offset of (token block tb, segment seg, token-in-block t) inside a tile
-// buffer.  Token block 1 swaps slot groups of 4 (t ^ 4) so that the transposed
-// P.V reads of tokens {4g..4g+3} of both blocks land in different LDS banks.
-__device__ inline int tile_off(int pitch, int tb, int seg, int t) { return tb * pitch + seg * 256 + ((t ^ (tb << 2)) << 4); }
+// buffer.  Token block 1 swaps the two halves of each 256-byte segment
+// (t ^ 8): a transposed P.V read takes tokens 4g..4g+3 of both blocks, and with
+// the swap the 32 lanes of g = 0, 1 (and of g = 2, 3) cover all 64 banks once;
+// with a swap of groups of 4 (t ^ 4) they would hit 32 banks twice (measured:
+// two-way conflicts on gfx950, which serves 32 lanes x 8 bytes per pass).
+__device__ inline int tile_off(int pitch, int tb, int seg, int t) { return tb * pitch + seg * 256 + ((t ^ (tb << 3)) << 4); }
 
 // ---- per-item decode ----------------------------------------------------------
 // Tiles hold 2 token blocks of 16 (32 tokens) for b <= 8 and 1 block (16
@@ -353,9 +356,9 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       const int tb = (TB == 2 && p >= block_pieces) ? 1 : 0;
       const int rem = p - tb * block_pieces;
       const int seg = rem >> 4, slot = rem & 15;
-      // token held by this slot: block 1 of a two-block tile swaps slot groups
-      // of 4; b = 16 swaps halves (slot ^ 8) in the low-byte plane
-      const int swz = BITS == 16 ? (seg >= (NSEG >> 1) ? 8 : 0) : (tb << 2);
+      // token held by this slot: block 1 of a two-block tile swaps segment
+      // halves (slot ^ 8), as does the low-byte plane of b = 16
+      const int swz = BITS == 16 ? (seg >= (NSEG >> 1) ? 8 : 0) : (tb << 3);
       const int t = min(16 * tb + (slot ^ swz), tlast);
       if (p < npos)                              // lane 0 always copies: the instruction is issued
         copy16_to_lds(__umul24(t, rstride) + seg * 16, tbase, buf + i * 1024);   // t < 32, stride <= 1152
