@@ -734,24 +734,41 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
               smax = fmaxf(smax, scv[tb][j]);
               tmax = fmaxf(tmax, t[tb][j]);
             }
+          // The running max and E usually stay: the exponentials are taken
+          // with them right away, in parallel with the row reductions, and are
+          // redone in the rare stage that moves either.
+          float e[TB][4];
+          {
+            const float mE0 = m_run + (float)Ecur;    // P~ = 2^(z - m - E), P' = P~ * scale_t
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) e[tb][j] = __builtin_amdgcn_exp2f(fmaf(t[tb][j], rowf, -mE0));
+          }
           smax = max_xor_16_32(smax);
           tmax = max_xor_16_32(tmax) * rowf;
           const bool raise_e = smax > ldexpf(1.0f, Ecur + kScaleHeadroom);   // wave-uniform
           const bool upd = __any(tmax > m_run + kLazyRescale) || raise_e;    // wave-uniform
-          const float mnew = upd ? max_plain(m_run, tmax) : m_run;
-          int es = Ecur;
-          (void)frexpf(smax, &es);
-          const int enew = raise_e ? es : Ecur;
-          // l is kept in units of 2^-E like O, so one factor rescales both
-          // (one v_exp: m_run - mnew <= 0, Ecur - enew <= 0; results below 2^-126 are 0)
-          const float alpha = __builtin_amdgcn_exp2f((m_run - mnew) + (float)(Ecur - enew));
-          l_lane *= alpha;
-          m_run = mnew;
-          Ecur = enew;
           const int par = tq & 1;
-          if (g == 0) alpha_lds[64 * par + my_row] = alpha;
+          if (upd) {
+            const float mnew = max_plain(m_run, tmax);
+            int es = Ecur;
+            (void)frexpf(smax, &es);
+            const int enew = raise_e ? es : Ecur;
+            // l is kept in units of 2^-E like O, so one factor rescales both
+            // (one v_exp: m_run - mnew <= 0, Ecur - enew <= 0; results below 2^-126 are 0)
+            const float alpha = __builtin_amdgcn_exp2f((m_run - mnew) + (float)(Ecur - enew));
+            l_lane *= alpha;
+            m_run = mnew;
+            Ecur = enew;
+            if (g == 0) alpha_lds[64 * par + my_row] = alpha;
+            const float mE = m_run + (float)Ecur;
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+              for (int j = 0; j < 4; ++j) e[tb][j] = __builtin_amdgcn_exp2f(fmaf(t[tb][j], rowf, -mE));
+          }
           if (lane == 0) flag_lds[4 * par + wave] = upd ? 1 : 0;
-          const float mE = m_run + (float)Ecur;     // P~ = 2^(z - m - E), P' = P~ * scale_t
           char* pdst = pbuf + par * PPAR + (wave * 64 + lane) * PSLOT;
           if constexpr (TB == 2) {
             h8 pf;
@@ -759,18 +776,16 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
             for (int tb = 0; tb < 2; ++tb)
 #pragma unroll
               for (int j = 0; j < 4; ++j) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(t[tb][j], rowf, -mE));
-                l_lane += e;
-                pf[4 * tb + j] = (_Float16)(e * scv[tb][j]);
+                l_lane += e[tb][j];
+                pf[4 * tb + j] = (_Float16)(e[tb][j] * scv[tb][j]);
               }
             *(h8*)pdst = pf;
           } else {
             h4 pf;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              const float e = __builtin_amdgcn_exp2f(fmaf(t[0][j], rowf, -mE));
-              l_lane += e;
-              pf[j] = (_Float16)(e * scv[0][j]);
+              l_lane += e[0][j];
+              pf[j] = (_Float16)(e[0][j] * scv[0][j]);
             }
             *(h4*)pdst = pf;
           }
