@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 
 
-def algorithmic_bytes(kk, w, model):
+def algorithmic_bytes(kk, w):
     """U = sum_anchors B*T*(row_stride + 4) + sum_l B*H*(d_eff + d_R)*sizeof(q) + sum_l B*H*d_eff*4."""
     qsize = 4 if str(w.q_dtype) == "torch.float32" else 2
     cache = sum(w.batch * w.seq_len * (kk.row_stride_bytes(w.layers[a].d, w.d_rope, w.layers[a].bits) + 4)
@@ -170,6 +170,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--append", action="store_true",
                     help="time kk_append_decode (write each sequence's newest token into every anchor, then decode)")
+    ap.add_argument("--hetero", action="store_true",
+                    help="time kk_multi_decode_attn on the heterogeneous 14B batch (four tables, 8 sequences each)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run 3 device-to-device copies of this size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -199,14 +201,36 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    w = synth.workload(args.workload)
-    model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
     t_setup = time.perf_counter()
-    caches = build_caches(kk, model, w)
-    ql, qr = synth.queries(w, "cuda")
-    seq_lens = torch.full((w.batch,), w.seq_len, dtype=torch.int32, device="cuda")
-    dec = kk.Decoder(model, caches, w.batch, w.seq_len, w.seq_len, split_tokens=args.split_tokens)
-    step = lambda: dec(ql, qr, seq_lens)
+    if args.hetero:
+        if args.append:
+            print("--append and --hetero are separate steps", file=sys.stderr)
+            sys.exit(2)
+        runs_w = synth.hetero_workloads()
+        w = runs_w[0]
+        runs, qls, qrs = [], [], []
+        for rw in runs_w:
+            m = kk.Model(rw.layers, rw.n_heads, rw.r, rw.d_rope)
+            runs.append((m, build_caches(kk, m, rw), rw.batch))
+            q = synth.queries(rw, "cuda")
+            qls.append(q[0])
+            qrs.append(q[1])
+        ql = torch.cat(qls, 1).contiguous()
+        qr = torch.cat(qrs, 1).contiguous()
+        del qls, qrs
+        batch = sum(rw.batch for rw in runs_w)
+        seq_lens = torch.full((batch,), w.seq_len, dtype=torch.int32, device="cuda")
+        dec = kk.MultiDecoder(runs, w.seq_len, w.seq_len, split_tokens=args.split_tokens)
+        step = lambda: dec(ql, qr, seq_lens)
+    else:
+        w = synth.workload(args.workload)
+        runs_w = [w]
+        model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+        caches = build_caches(kk, model, w)
+        ql, qr = synth.queries(w, "cuda")
+        seq_lens = torch.full((w.batch,), w.seq_len, dtype=torch.int32, device="cuda")
+        dec = kk.Decoder(model, caches, w.batch, w.seq_len, w.seq_len, split_tokens=args.split_tokens)
+        step = lambda: dec(ql, qr, seq_lens)
     if args.append:
         # the newest token of each sequence (row seq_len - 1) is rewritten from seeded rows every step
         g = torch.Generator(device="cuda").manual_seed(1234)
@@ -244,24 +268,26 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    U, cache_bytes = algorithmic_bytes(kk, w, model)
-    flops = useful_flops(w)
+    U = sum(algorithmic_bytes(kk, rw)[0] for rw in runs_w)
+    flops = sum(useful_flops(rw) for rw in runs_w)
     achieved = U / (mean_dev_ms * 1e-3) / 1e9
-    traffic = stored_traffic(w.name)
+    name = "14b_hetero_4tables" if args.hetero else w.name
+    batch = sum(rw.batch for rw in runs_w)
+    traffic = stored_traffic(name)
     print(f"[bench] device ms/step mean {mean_dev_ms:.4f} p10 {dev_ms[len(dev_ms) // 10]:.4f} "
           f"p90 {dev_ms[(9 * len(dev_ms)) // 10]:.4f}; wall ms/step {ms_per_step:.4f}; U {U / 1e9:.3f} GB; "
           f"{achieved:.0f} GB/s; MFMA-useful {flops / (mean_dev_ms * 1e-3) / 1e12:.1f} TFLOP/s",
           file=sys.stderr, flush=True)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.hetero:
         cpu = cpu_baseline(w, args.cpu_budget)
 
-    anchors = w.anchors()
-    bits_tok = sum((w.layers[a].d + w.d_rope) * w.layers[a].bits + 32 for a in anchors)
+    anchors = [len(rw.anchors()) for rw in runs_w]
+    bits_tok = [sum((rw.layers[a].d + rw.d_rope) * rw.layers[a].bits + 32 for a in rw.anchors()) for rw in runs_w]
     line = {
         "metric": "compressed decode-attn layer*tokens/s",
-        "value": w.n_layers * w.batch / (ms_per_step * 1e-3),
+        "value": w.n_layers * batch / (ms_per_step * 1e-3),
         "unit": "layer*tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -272,12 +298,16 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": w.name, "layers": w.n_layers, "heads": w.n_heads, "batch": w.batch,
-                   "cached_tokens": w.seq_len, "r": w.r, "d_rope": w.d_rope, "anchors": len(anchors),
-                   "bits_per_token": bits_tok, "q_dtype": str(w.q_dtype).replace("torch.", ""),
+        "config": {"workload": name, "layers": w.n_layers, "heads": w.n_heads, "batch": batch,
+                   "cached_tokens": w.seq_len, "r": w.r, "d_rope": w.d_rope,
+                   "anchors": anchors if args.hetero else anchors[0],
+                   "bits_per_token": bits_tok if args.hetero else bits_tok[0],
+                   "q_dtype": str(w.q_dtype).replace("torch.", ""),
                    "split_tokens": args.split_tokens or "auto", "parallelism": "none (one GPU)",
-                   "step": "append + decode" if args.append else "decode"},
-        "roofline": {"bound": "hbm", "kernel": ("append_kernel + " if args.append else "") +
+                   "step": ("append + decode" if args.append else
+                            "heterogeneous decode (4 tables x 8 sequences)" if args.hetero else "decode")},
+        "roofline": {"bound": "hbm", "kernel": ("append_kernel + " if args.append else
+                                                "store_kernel (plan upload) + " if args.hetero else "") +
                      "decode step: decode_kernel + merge_kernel",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,

@@ -37,6 +37,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
+#include <cstring>
 #include <type_traits>
 
 #include "kk_internal.h"
@@ -60,6 +61,18 @@ typedef short s4 __attribute__((ext_vector_type(4)));
 // address space, scalar loads).
 typedef __attribute__((address_space(4))) const DecodeArgs KArgs;
 typedef __attribute__((address_space(4))) const EntryArg KEntry;
+typedef __attribute__((address_space(4))) const LayerArg KLayer;
+typedef __attribute__((address_space(4))) const uint16_t KU16;
+
+// Plan arrays: in the launch arguments (one table) or in device memory
+// (several tables); both are read-only for the launch, so scalar loads.
+__device__ inline KEntry* entry_array(KArgs& A) { return A.plan.entries ? (KEntry*)A.plan.entries : A.entries; }
+__device__ inline KLayer& layer_at(KArgs& A, int i) {
+  return A.plan.entries ? ((KLayer*)A.plan.layers)[i] : A.layers[i];
+}
+__device__ inline int group_layer_at(KArgs& A, int i) {
+  return A.plan.entries ? ((KU16*)A.plan.group_layers)[i] : A.group_layers[i];
+}
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kQFrac = 13;           // query fixed point: |q'| < 1 -> |q'| * 2^13 <= 8192
@@ -316,7 +329,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   const int nrows = min(E.chunk_rows, E.row_end - r0);
 
   // token range of this split
-  int len = A.seq_lens[s];
+  int len = A.seq_lens[E.seq_base + s];
   len = len < 0 ? 0 : (len > A.t_cap ? A.t_cap : len);
   const int tps = ((len + E.splits - 1) / E.splits + kTile - 1) / kTile * kTile;
   const int t0 = ksplit * tps;
@@ -410,7 +423,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       int my_layer = -1, my_head = 0;
       if (my_row < nrows) {
         const int gr = r0 + my_row;
-        my_layer = A.group_layers[E.lay_begin + gr / A.heads];
+        my_layer = group_layer_at(A, E.lay_begin + gr / A.heads);
         my_head = gr % A.heads;
       }
       int qsum = 0;                               // sum of the fixed-point q of this row
@@ -420,7 +433,8 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       // query costs one memory round trip: a chunk outside the row or past K
       // reads the (valid) first query element and is zeroed afterwards.
       const bool row_ok = my_layer >= 0;
-      const int64_t qrow = row_ok ? ((int64_t)my_layer * A.batch + s) * A.heads + my_head : 0;
+      const int64_t qrow =
+          row_ok ? ((int64_t)(my_layer - E.layer_base) * A.batch + E.seq_base + s) * A.heads + my_head : 0;
       bool ok[kMaxChunks64];
       int64_t off[kMaxChunks64];
       bool lat[kMaxChunks64];
@@ -477,7 +491,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       if (mx > 0.0f) (void)frexpf(mx, &e);          // mx * 2^-e in [0.5, 1)
       // A negative softmax scale is carried by q (z = |scale| * (-q) . k), so the
       // row factor below is positive, as the softmax needs.
-      const float sm = my_layer >= 0 ? A.layers[my_layer].sm_scale : 0.0f;
+      const float sm = my_layer >= 0 ? layer_at(A, my_layer).sm_scale : 0.0f;
       const float pre = ldexpf(sm < 0.0f ? -1.0f : 1.0f, kQFrac - e);
 #pragma unroll
       for (int c = 0; c < kMaxChunks64; ++c) {
@@ -825,11 +839,11 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       const int rl = 16 * rb + n;
       if (rl < nrows) {
         const int gr = r0 + rl;
-        const int layer = A.group_layers[E.lay_begin + gr / A.heads], head = gr % A.heads;
+        const int layer = group_layer_at(A, E.lay_begin + gr / A.heads), head = gr % A.heads;
         const float lrow = ml_lds[2 * rl + 1];
         const float inv = lrow > 0.0f ? 1.0f / lrow : 0.0f;
         const float fac = split ? (lrow > 0.0f ? ldexpf(inv, -(Eitem + 6)) : 0.0f) : inv;
-        float* dst = split ? nullptr : A.out + A.layers[layer].out_off + ((int64_t)s * A.heads + head) * d;
+        float* dst = split ? nullptr : A.out + layer_at(A, layer).out_off + ((int64_t)s * A.heads + head) * d;
         _Float16* dsth = split ? part + (int64_t)rl * d : nullptr;
 #pragma unroll
         for (int ui = 0; ui < UMAX; ++ui) {
@@ -870,11 +884,14 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
     pipeline(std::false_type{}, std::integral_constant<int, pv_units_max<RB>()>{});
 }
 
-__device__ inline int find_entry(KArgs& A, int item) {
+// Last entry whose first decode block (merge: first merge block) is <= blk;
+// both are monotone over the entries.
+template <bool MERGE>
+__device__ inline int find_entry(KArgs& A, KEntry* ents, int blk) {
   int lo = 0, hi = A.n_entries - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (A.entries[mid].item_base <= item) lo = mid; else hi = mid - 1;
+    if ((MERGE ? ents[mid].merge_base : ents[mid].item_base) <= blk) lo = mid; else hi = mid - 1;
   }
   return lo;
 }
@@ -893,12 +910,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   KArgs& A = kernel_args();
   const int item = blockIdx.x;
-  const int ei = find_entry(A, item);
-  KEntry& E = A.entries[ei];
+  KEntry* ents = entry_array(A);
+  KEntry& E = ents[find_entry<false>(A, ents, item)];
   // item numbering: chunks of one (sequence, split) pair sit 8 blocks apart, so
   // they are dispatched to the same XCD at about the same time and share its L2.
   const int local = item - E.item_base;
-  const int J = A.batch * E.splits, nrc = E.nrc;
+  const int J = E.n_seq * E.splits, nrc = E.nrc;
   const int q8 = J >> 3, r8 = J & 7;
   int chunk, j;
   if (local < 8 * q8 * nrc) {
@@ -924,13 +941,10 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs) {
   __shared__ float wgt[kMaxMergeSplits][64];
   KArgs& A = kernel_args();
   const int blk = blockIdx.x;
-  int ei = -1;
-  for (int e = 0; e < A.n_entries; ++e)
-    if (A.entries[e].splits > 1 && A.entries[e].merge_base <= blk) ei = e;
-  if (ei < 0) return;
-  KEntry& E = A.entries[ei];
+  KEntry* ents = entry_array(A);
+  KEntry& E = ents[find_entry<true>(A, ents, blk)];
   const int local = blk - E.merge_base;
-  if (local >= A.batch * E.nrc) return;
+  if (E.splits <= 1 || local >= E.n_seq * E.nrc) return;
   const int s = local / E.nrc, chunk = local - s * E.nrc;
   const int d = E.d, S = E.splits;
   const int r0 = E.row_begin + chunk * E.chunk_rows;
@@ -994,11 +1008,27 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs) {
     for (int j = 0; j < kMergeVec; ++j) {
       if (i0 + 256 * j < total) {
         const int gr = r0 + rl[j];
-        const int layer = A.group_layers[E.lay_begin + gr / A.heads], head = gr % A.heads;
-        *(f4*)(A.out + A.layers[layer].out_off + ((int64_t)s * A.heads + head) * d + f[j]) = acc[j];
+        const int layer = group_layer_at(A, E.lay_begin + gr / A.heads), head = gr % A.heads;
+        *(f4*)(A.out + layer_at(A, layer).out_off + ((int64_t)s * A.heads + head) * d + f[j]) = acc[j];
       }
     }
   }
+}
+
+// Plan upload: each launch carries up to kStoreWords words in its arguments
+// and writes them to device memory.
+constexpr int kStoreWords = 1800;
+struct StoreArgs {
+  uint32_t* dst;
+  int32_t n;
+  int32_t pad_;
+  uint32_t w[kStoreWords];
+};
+typedef __attribute__((address_space(4))) const StoreArgs KStore;
+
+__global__ void __launch_bounds__(256) store_kernel(StoreArgs) {
+  KStore& a = *(KStore*)(__builtin_amdgcn_kernarg_segment_ptr());
+  for (int i = threadIdx.x; i < a.n; i += 256) a.dst[i] = a.w[i];
 }
 
 template <int RB>
@@ -1039,6 +1069,22 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t
   if (L.merge_blocks > 0) {
     hipLaunchKernelGGL(merge_kernel, dim3(L.merge_blocks), dim3(256), 0, stream, a);
     return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_store(uint32_t* dst, const uint32_t* words, int64_t n_words, hipStream_t stream) {
+  static_assert(sizeof(StoreArgs) < 7600, "kernel argument block too large");
+  StoreArgs a;
+  for (int64_t o = 0; o < n_words; o += kStoreWords) {
+    const int m = (int)(n_words - o < kStoreWords ? n_words - o : kStoreWords);
+    a.dst = dst + o;
+    a.n = m;
+    a.pad_ = 0;
+    std::memcpy(a.w, words + o, (size_t)m * sizeof(uint32_t));
+    hipLaunchKernelGGL(store_kernel, dim3(1), dim3(256), 0, stream, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }

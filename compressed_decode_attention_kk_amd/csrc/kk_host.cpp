@@ -52,10 +52,22 @@ size_t stride_of(int d, int dr, int bits) {
   return (size_t)((bitsum / 8 + 15) / 16 * 16);
 }
 
+// One table of the step: its layers, its caches and the sequences that use it.
+struct TableRef {
+  const kk_model_cfg* cfg;
+  const kk_cache* caches;   // host [n_layers]; null while only sizes are planned
+  int n_seq, seq_base;      // sequences [seq_base, seq_base + n_seq) of the batch
+  int layer_base;           // first slot of the table's layers in the layer array
+  int64_t out_base;         // float offset of the table's output block
+};
+
 struct Plan {
-  kk::DecodeArgs args;
+  kk::DecodeArgs args;                 // one table: the arrays travel in here
   kk::DecodeLaunch launch;
-  int entry_anchor[kk::kMaxEntries];   // anchor layer whose cache each entry reads
+  std::vector<kk::EntryArg> ents;
+  std::vector<int> entry_anchor, entry_table;
+  std::vector<kk::LayerArg> layers;    // slot = layer_base + layer
+  std::vector<uint16_t> group_layers;
   int64_t ws_floats = 0;
 };
 
@@ -71,35 +83,19 @@ constexpr int64_t kTailPercent = 15;  // share of the work (last dispatched) cut
 constexpr int64_t kItemOverhead = 40;   // per-item fixed cost (query setup, pipeline fill, stores)
 
 // Work plan of one decode step.  Groups: an anchor and the layers inheriting
-// its cache.  Each group's query rows (layer-major, head-minor) form entries of
-// <= 512 rows cut into chunks of <= 64 rows; an item is (chunk, seq, split).
+// its cache, per table.  Each group's query rows (layer-major, head-minor)
+// form entries of <= 8 chunks of <= 64 rows; an item is (chunk, seq, split).
 // Splits are chosen so that items carry similar byte counts; entries are
-// ordered by bytes per item, largest first.
-kk_status make_plan(const kk_model_cfg* c, int batch, int max_len, int split_tokens, Plan& P) {
-  kk::DecodeArgs& A = P.args;
-  std::memset(&A, 0, sizeof(A));
-  const int H = c->n_heads, L = c->n_layers;
-  std::vector<int> order;                              // layers grouped by anchor
-  std::vector<std::pair<int, int>> groups;             // (anchor, first index in order)
-  for (int a = 0; a < L; ++a) {
-    if (c->layers[a].anchor != a) continue;
-    groups.push_back({a, (int)order.size()});
-    for (int l = a; l < L; ++l)
-      if (c->layers[l].anchor == a) order.push_back(l);
-  }
-  for (int i = 0; i < L; ++i) A.group_layers[i] = (uint8_t)order[i];
-  int64_t off = 0;
-  for (int l = 0; l < L; ++l) {
-    const int a = c->layers[l].anchor;
-    A.layers[l].sm_scale = c->layers[l].sm_scale;
-    A.layers[l].d_eff = c->layers[a].d;
-    A.layers[l].out_off = off;
-    off += (int64_t)batch * H * c->layers[a].d;
-  }
-
+// ordered by bytes per item, largest first.  The tables share n_layers,
+// n_heads, r and d_rope (checked by the callers).
+kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_tokens, Plan& P) {
+  const kk_model_cfg* c0 = tabs[0].cfg;
+  const int H = c0->n_heads, L = c0->n_layers;
+  P.layers.assign((size_t)tabs.size() * L, kk::LayerArg{});
+  P.group_layers.clear();
   struct Ent {
     kk::EntryArg e;
-    int anchor;
+    int anchor, table;
     int64_t cost_tile;     // relative time of one 32-token tile of one item
     int key_num, key_den;  // position of the entry in its bit width's order
   };
@@ -110,35 +106,53 @@ kk_status make_plan(const kk_model_cfg* c, int batch, int max_len, int split_tok
   const int chunk_rows = H <= 64 ? H * ((16 * RB) / H) : 64;
   const int kEntryRows = 8 * chunk_rows;
   P.launch.row_blocks = RB;
-  for (size_t gi = 0; gi < groups.size(); ++gi) {
-    const int a = groups[gi].first, begin = groups[gi].second;
-    const int end = gi + 1 < groups.size() ? groups[gi + 1].second : L;
-    const int rows = (end - begin) * H;
-    for (int rb = 0; rb < rows; rb += kEntryRows) {
-      Ent E;
-      std::memset(&E.e, 0, sizeof(E.e));
-      E.e.d = (int16_t)c->layers[a].d;
-      E.e.bits = (int16_t)c->layers[a].bits;
-      E.e.row_stride = (int32_t)stride_of(c->layers[a].d, c->d_rope, c->layers[a].bits);
-      E.e.row_begin = rb;
-      E.e.row_end = std::min(rows, rb + kEntryRows);
-      const int n = E.e.row_end - E.e.row_begin;
-      E.e.nrc = (int16_t)((n + chunk_rows - 1) / chunk_rows);
-      E.e.chunk_rows = (int16_t)chunk_rows;
-      E.e.lay_begin = (int16_t)begin;
-      E.anchor = a;
-      E.cost_tile = tile_cost(E.e.bits, E.e.d);
-      ents.push_back(E);
+  for (size_t ti = 0; ti < tabs.size(); ++ti) {
+    const TableRef& T = tabs[ti];
+    const kk_model_cfg* c = T.cfg;
+    int64_t off = T.out_base;
+    for (int l = 0; l < L; ++l) {
+      const int a = c->layers[l].anchor;
+      kk::LayerArg& la = P.layers[(size_t)T.layer_base + l];
+      la.sm_scale = c->layers[l].sm_scale;
+      la.d_eff = c->layers[a].d;
+      la.out_off = off;
+      off += (int64_t)T.n_seq * H * c->layers[a].d;
+    }
+    for (int a = 0; a < L; ++a) {
+      if (c->layers[a].anchor != a) continue;
+      const int begin = (int)P.group_layers.size();
+      for (int l = a; l < L; ++l)
+        if (c->layers[l].anchor == a) P.group_layers.push_back((uint16_t)(T.layer_base + l));
+      const int rows = ((int)P.group_layers.size() - begin) * H;
+      for (int rb = 0; rb < rows; rb += kEntryRows) {
+        Ent E;
+        std::memset(&E.e, 0, sizeof(E.e));
+        E.e.d = (int16_t)c->layers[a].d;
+        E.e.bits = (int16_t)c->layers[a].bits;
+        E.e.row_stride = (int32_t)stride_of(c->layers[a].d, c->d_rope, c->layers[a].bits);
+        E.e.row_begin = rb;
+        E.e.row_end = std::min(rows, rb + kEntryRows);
+        const int n = E.e.row_end - E.e.row_begin;
+        E.e.nrc = (int16_t)((n + chunk_rows - 1) / chunk_rows);
+        E.e.chunk_rows = (int16_t)chunk_rows;
+        E.e.lay_begin = begin;
+        E.e.layer_base = T.layer_base;
+        E.e.seq_base = T.seq_base;
+        E.e.n_seq = T.n_seq;
+        E.anchor = a;
+        E.table = (int)ti;
+        E.cost_tile = tile_cost(E.e.bits, E.e.d);
+        ents.push_back(E);
+      }
     }
   }
-  if ((int)ents.size() > kk::kMaxEntries) return KK_ERR_UNSUPPORTED;
 
   // Splits: one launch runs every item, so items are sized by estimated time:
   // about kItemWaves waves of items over the resident workgroup slots, each at
   // least kMinSplitTiles tiles long.  Unsplit items need no merge pass.
   const int max_tiles = std::max(1, (max_len + kk::kTile - 1) / kk::kTile);
   int64_t total_cost = 0;
-  for (auto& E : ents) total_cost += E.cost_tile * max_tiles * E.e.nrc * batch;
+  for (auto& E : ents) total_cost += E.cost_tile * max_tiles * E.e.nrc * E.e.n_seq;
   const int64_t slots = (int64_t)kk::kCUs * kk::decode_wg_per_cu(0);
   auto split_of = [&](const Ent& E, int waves) {
     const int64_t target = std::max<int64_t>(1, total_cost / (waves * slots));
@@ -158,10 +172,12 @@ kk_status make_plan(const kk_model_cfg* c, int batch, int max_len, int split_tok
   for (auto& E : ents)
     alike = alike && E.e.bits == ents[0].e.bits && E.e.d == ents[0].e.d && E.e.nrc == ents[0].e.nrc;
   if (alike) {
+    int64_t n_items_per_split = 0;
+    for (auto& E : ents) n_items_per_split += (int64_t)E.e.nrc * E.e.n_seq;
     int64_t best = -1;
     for (int w = 4; w <= 8; ++w) {
       const int64_t sp = split_of(ents[0], w);
-      const int64_t n = sp * ents[0].e.nrc * batch * (int64_t)ents.size();
+      const int64_t n = sp * n_items_per_split;
       const int64_t t = ((n + slots - 1) / slots) * (((max_tiles + sp - 1) / sp) * ents[0].cost_tile + kItemOverhead);
       if (best < 0 || t < best) { best = t; waves = w; }
     }
@@ -195,39 +211,56 @@ kk_status make_plan(const kk_model_cfg* c, int batch, int max_len, int split_tok
       if (acc >= tail_from)
         E.e.splits = (int16_t)std::min<int64_t>({2 * (int64_t)E.e.splits, std::max(1, max_tiles / kMinSplitTiles),
                                                  (int64_t)kk::kMaxMergeSplits});
-      acc += E.cost_tile * max_tiles * E.e.nrc * batch;
+      acc += E.cost_tile * max_tiles * E.e.nrc * E.e.n_seq;
     }
   }
-  int64_t items = 0, ws = 0;
-  int merges = 0;
+  int64_t items = 0, ws = 0, merges = 0;
   kk::DecodeLaunch& Lc = P.launch;
   Lc.items = 0;
   Lc.lds_bytes = 0;
+  P.ents.resize(ents.size());
+  P.entry_anchor.resize(ents.size());
+  P.entry_table.resize(ents.size());
   for (size_t i = 0; i < ents.size(); ++i) {
     kk::EntryArg& e = ents[i].e;
-    e.merge_base = 0;
     e.codes = nullptr;
     e.scales = nullptr;
     e.item_base = (int32_t)std::min<int64_t>(items, 0x7fffffff);
-    items += (int64_t)e.nrc * batch * e.splits;
+    e.merge_base = (int32_t)std::min<int64_t>(merges, 0x7fffffff);
+    items += (int64_t)e.nrc * e.n_seq * e.splits;
     if (e.splits > 1) {
       e.ws_off = ws;
-      ws += (int64_t)e.nrc * batch * e.splits * kk::partial_slot_floats(e.d);
-      e.merge_base = merges;
-      merges += e.nrc * batch;
+      ws += (int64_t)e.nrc * e.n_seq * e.splits * kk::partial_slot_floats(e.d);
+      merges += (int64_t)e.nrc * e.n_seq;
     }
-    e.nbuf = (int16_t)kk::decode_nbuf(e.row_stride, e.d + c->d_rope, e.bits, RB);
-    Lc.lds_bytes = std::max(Lc.lds_bytes, kk::decode_lds_bytes(e.row_stride, e.d + c->d_rope, e.bits, RB));
+    e.nbuf = (int16_t)kk::decode_nbuf(e.row_stride, e.d + c0->d_rope, e.bits, RB);
+    Lc.lds_bytes = std::max(Lc.lds_bytes, kk::decode_lds_bytes(e.row_stride, e.d + c0->d_rope, e.bits, RB));
     if (Lc.lds_bytes > 160 * 1024 / kk::decode_wg_per_cu(0)) return KK_ERR_UNSUPPORTED;
-    A.entries[i] = e;
+    P.ents[i] = e;
     P.entry_anchor[i] = ents[i].anchor;
+    P.entry_table[i] = ents[i].table;
   }
-  if (items > 0x7fffffff) return KK_ERR_UNSUPPORTED;
-  A.n_entries = (int32_t)ents.size();
-  A.total_items = (int32_t)items;
+  if (items > 0x7fffffff || merges > 0x7fffffff) return KK_ERR_UNSUPPORTED;
   Lc.items = (int)items;
-  Lc.merge_blocks = merges;
+  Lc.merge_blocks = (int)merges;
   P.ws_floats = ws;
+  return KK_OK;
+}
+
+// Plan of one table whose arrays travel in the launch arguments.
+kk_status make_single_plan(const kk_model_cfg* c, const kk_cache* caches, int batch, int max_len, int split_tokens,
+                           Plan& P) {
+  std::vector<TableRef> tabs{TableRef{c, caches, batch, 0, 0, 0}};
+  const kk_status st = make_plan(tabs, max_len, split_tokens, P);
+  if (st != KK_OK) return st;
+  if (P.ents.size() > (size_t)kk::kMaxEntries) return KK_ERR_UNSUPPORTED;
+  kk::DecodeArgs& A = P.args;
+  std::memset(&A, 0, sizeof(A));
+  for (size_t i = 0; i < P.group_layers.size(); ++i) A.group_layers[i] = P.group_layers[i];
+  for (size_t i = 0; i < P.layers.size(); ++i) A.layers[i] = P.layers[i];
+  for (size_t i = 0; i < P.ents.size(); ++i) A.entries[i] = P.ents[i];
+  A.n_entries = (int32_t)P.ents.size();
+  A.total_items = P.launch.items;
   return KK_OK;
 }
 
@@ -308,7 +341,7 @@ kk_status kk_decode_workspace_bytes(const kk_model_cfg* cfg, int32_t batch, int3
   if (batch < 1 || max_seq_len < 0 || split_tokens < 0 || !bytes) return KK_ERR_INVALID_ARGUMENT;
   if (split_tokens % kk::kTile) return KK_ERR_INVALID_ARGUMENT;
   Plan P;
-  st = make_plan(cfg, batch, max_seq_len, split_tokens, P);
+  st = make_single_plan(cfg, nullptr, batch, max_seq_len, split_tokens, P);
   if (st != KK_OK) return st;
   *bytes = (size_t)P.ws_floats * sizeof(float);
   return KK_OK;
@@ -334,7 +367,7 @@ kk_status prepare_decode(const kk_model_cfg* cfg, const kk_cache* caches, int32_
     if (!aligned(caches[l].codes, 16) || !aligned(caches[l].scales, 16)) return KK_ERR_INVALID_ARGUMENT;
   }
   if ((int64_t)cfg->n_layers * batch * cfg->n_heads > ((int64_t)1 << 31)) return KK_ERR_UNSUPPORTED;
-  st = make_plan(cfg, batch, max_seq_len, split_tokens, P);
+  st = make_single_plan(cfg, caches, batch, max_seq_len, split_tokens, P);
   if (st != KK_OK) return st;
   const size_t need = (size_t)P.ws_floats * sizeof(float);
   if (need > 0) {
@@ -361,6 +394,146 @@ kk_status prepare_decode(const kk_model_cfg* cfg, const kk_cache* caches, int32_
   return KK_OK;
 }
 }  // namespace
+
+namespace {
+// Several tables: the tables' checks, their sequence ranges and output bases.
+kk_status check_tables(const kk_table_batch* tables, int32_t n_tables, bool need_caches, std::vector<TableRef>& tabs,
+                       int64_t* total_batch) {
+  if (!tables || n_tables < 1) return KK_ERR_INVALID_ARGUMENT;
+  if (n_tables > KK_MAX_TABLES) return KK_ERR_UNSUPPORTED;
+  const kk_model_cfg* c0 = tables[0].cfg;
+  int64_t seq = 0, out = 0;
+  tabs.clear();
+  for (int ti = 0; ti < n_tables; ++ti) {
+    const kk_model_cfg* c = tables[ti].cfg;
+    const kk_status st = check_model(c);
+    if (st != KK_OK) return st;
+    if (c->n_layers != c0->n_layers || c->n_heads != c0->n_heads || c->r != c0->r || c->d_rope != c0->d_rope)
+      return KK_ERR_INVALID_ARGUMENT;
+    const int b = tables[ti].batch;
+    if (b < 1) return KK_ERR_INVALID_ARGUMENT;
+    if (need_caches) {
+      const kk_cache* cc = tables[ti].caches;
+      if (!cc) return KK_ERR_INVALID_ARGUMENT;
+      for (int l = 0; l < c->n_layers; ++l) {
+        if (c->layers[l].anchor != l) continue;
+        if (!cc[l].codes || !cc[l].scales) return KK_ERR_INVALID_ARGUMENT;
+        if (!aligned(cc[l].codes, 16) || !aligned(cc[l].scales, 16)) return KK_ERR_INVALID_ARGUMENT;
+      }
+    }
+    if (seq + b > 0x7fffffff) return KK_ERR_UNSUPPORTED;
+    tabs.push_back(TableRef{c, tables[ti].caches, b, (int)seq, ti * c0->n_layers, out});
+    seq += b;
+    for (int l = 0; l < c->n_layers; ++l) out += (int64_t)b * c->n_heads * c->layers[c->layers[l].anchor].d;
+  }
+  if ((int64_t)c0->n_layers * seq * c0->n_heads > ((int64_t)1 << 31)) return KK_ERR_UNSUPPORTED;
+  *total_batch = seq;
+  return KK_OK;
+}
+
+// Workspace of a several-table step: the split partials, then the plan arrays
+// (entries, layers, group layers), each part 256-byte aligned.
+struct MultiLayout {
+  size_t plan_off, lay_off, grp_off, total;
+};
+MultiLayout multi_layout(const Plan& P) {
+  auto up = [](size_t x, size_t a) { return (x + a - 1) / a * a; };
+  MultiLayout m;
+  m.plan_off = up((size_t)P.ws_floats * sizeof(float), 256);
+  m.lay_off = up(m.plan_off + P.ents.size() * sizeof(kk::EntryArg), 16);
+  m.grp_off = m.lay_off + P.layers.size() * sizeof(kk::LayerArg);
+  m.total = up(m.grp_off + P.group_layers.size() * sizeof(uint16_t), 256);
+  return m;
+}
+}  // namespace
+
+kk_status kk_multi_out_offsets(const kk_table_batch* tables, int32_t n_tables, int64_t* offsets) {
+  std::vector<TableRef> tabs;
+  int64_t total = 0;
+  const kk_status st = check_tables(tables, n_tables, false, tabs, &total);
+  if (st != KK_OK) return st;
+  if (!offsets) return KK_ERR_INVALID_ARGUMENT;
+  int64_t off = 0;
+  size_t k = 0;
+  for (auto& T : tabs)
+    for (int l = 0; l < T.cfg->n_layers; ++l) {
+      offsets[k++] = off;
+      off += (int64_t)T.n_seq * T.cfg->n_heads * T.cfg->layers[T.cfg->layers[l].anchor].d;
+    }
+  offsets[k] = off;
+  return KK_OK;
+}
+
+kk_status kk_multi_decode_workspace_bytes(const kk_table_batch* tables, int32_t n_tables, int32_t max_seq_len,
+                                          int32_t split_tokens, size_t* bytes) {
+  std::vector<TableRef> tabs;
+  int64_t total = 0;
+  kk_status st = check_tables(tables, n_tables, false, tabs, &total);
+  if (st != KK_OK) return st;
+  if (max_seq_len < 0 || split_tokens < 0 || split_tokens % kk::kTile || !bytes) return KK_ERR_INVALID_ARGUMENT;
+  Plan P;
+  st = make_plan(tabs, max_seq_len, split_tokens, P);
+  if (st != KK_OK) return st;
+  *bytes = multi_layout(P).total;
+  return KK_OK;
+}
+
+kk_status kk_multi_decode_attn(const kk_table_batch* tables, int32_t n_tables, int32_t t_cap, const int32_t* seq_lens,
+                               int32_t max_seq_len, const void* q_lat, const void* q_rope, kk_dtype q_dtype,
+                               float* out, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  std::vector<TableRef> tabs;
+  int64_t batch = 0;
+  kk_status st = check_tables(tables, n_tables, true, tabs, &batch);
+  if (st != KK_OK) return st;
+  if (t_cap < 1 || max_seq_len < 0 || max_seq_len > t_cap) return KK_ERR_INVALID_ARGUMENT;
+  if (split_tokens < 0 || split_tokens % kk::kTile) return KK_ERR_INVALID_ARGUMENT;
+  if (q_dtype != KK_DTYPE_F32 && q_dtype != KK_DTYPE_BF16) return KK_ERR_INVALID_ARGUMENT;
+  if (!seq_lens || !q_lat || !q_rope || !out) return KK_ERR_INVALID_ARGUMENT;
+  if (!aligned(seq_lens, 4) || !aligned(q_lat, 16) || !aligned(q_rope, 16) || !aligned(out, 16))
+    return KK_ERR_INVALID_ARGUMENT;
+  Plan P;
+  st = make_plan(tabs, max_seq_len, split_tokens, P);
+  if (st != KK_OK) return st;
+  const MultiLayout m = multi_layout(P);
+  if (!workspace || !aligned(workspace, 256)) return KK_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < m.total) return KK_ERR_WORKSPACE_TOO_SMALL;
+  for (size_t i = 0; i < P.ents.size(); ++i) {
+    const kk_cache& cc = tabs[P.entry_table[i]].caches[P.entry_anchor[i]];
+    P.ents[i].codes = cc.codes;
+    P.ents[i].scales = cc.scales;
+  }
+  // plan image, uploaded into the workspace ahead of the decode launch
+  char* ws = static_cast<char*>(workspace);
+  std::vector<uint32_t> img((m.total - m.plan_off) / sizeof(uint32_t), 0u);
+  char* base = reinterpret_cast<char*>(img.data());
+  std::memcpy(base, P.ents.data(), P.ents.size() * sizeof(kk::EntryArg));
+  std::memcpy(base + (m.lay_off - m.plan_off), P.layers.data(), P.layers.size() * sizeof(kk::LayerArg));
+  std::memcpy(base + (m.grp_off - m.plan_off), P.group_layers.data(), P.group_layers.size() * sizeof(uint16_t));
+  kk::DecodeArgs& A = P.args;
+  std::memset(&A, 0, sizeof(A));
+  A.plan.entries = reinterpret_cast<const kk::EntryArg*>(ws + m.plan_off);
+  A.plan.layers = reinterpret_cast<const kk::LayerArg*>(ws + m.lay_off);
+  A.plan.group_layers = reinterpret_cast<const uint16_t*>(ws + m.grp_off);
+  A.n_entries = (int32_t)P.ents.size();
+  A.total_items = P.launch.items;
+  A.q_lat = q_lat;
+  A.q_rope = q_rope;
+  A.out = out;
+  A.ws = reinterpret_cast<float*>(ws);
+  A.seq_lens = seq_lens;
+  A.batch = (int32_t)batch;
+  A.heads = tabs[0].cfg->n_heads;
+  A.r = tabs[0].cfg->r;
+  A.d_rope = tabs[0].cfg->d_rope;
+  A.t_cap = t_cap;
+  A.q_is_f32 = q_dtype == KK_DTYPE_F32;
+  if (A.n_entries == 0 || P.launch.items == 0) return KK_OK;
+  if (kk::launch_store(reinterpret_cast<uint32_t*>(ws + m.plan_off), img.data(), (int64_t)img.size(), stream) !=
+      hipSuccess)
+    return KK_ERR_DEVICE;
+  return kk::launch_decode(A, P.launch, stream) == hipSuccess ? KK_OK : KK_ERR_DEVICE;
+}
 
 kk_status kk_decode_attn(const kk_model_cfg* cfg, const kk_cache* caches, int32_t batch, int32_t t_cap,
                          const int32_t* seq_lens, int32_t max_seq_len, const void* q_lat, const void* q_rope,

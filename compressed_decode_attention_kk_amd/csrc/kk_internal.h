@@ -14,7 +14,7 @@ constexpr int kTile = 32;            // token granularity of splits (tiles are 3
 constexpr int kMaxRowBlocks = 4;     // 16-row MFMA blocks per work item (<= 64 query rows)
 constexpr int kMaxMergeSplits = 64;  // token splits of one sequence
 constexpr int kMaxK = 576;           // d + d_R (the ABI limit)
-constexpr int kMaxEntries = 96;      // group entries per launch
+constexpr int kMaxEntries = 88;      // group entries held in the launch arguments
 constexpr int kMaxLayers = 64;
 constexpr int kCUs = 256;
 // Decode workgroups per CU (the same for every bit width: a second workgroup
@@ -22,8 +22,8 @@ constexpr int kCUs = 256;
 constexpr int decode_wg_per_cu(int) { return 2; }
 constexpr float kLazyRescale = 8.0f; // log2 headroom before the running max is moved
 
-// One layer: softmax scale, kept width of its anchor and the float offset of
-// its block in the packed output.
+// One layer of one table: softmax scale, kept width of its anchor and the
+// float offset of its block in the packed output.
 struct LayerArg {
   float sm_scale;
   int32_t d_eff;
@@ -31,20 +31,35 @@ struct LayerArg {
 };
 
 // One group entry: the query rows [row_begin, row_end) of one anchor group
-// (an anchor and the layers that inherit its cache), cut into nrc chunks of
-// at most 64 rows; every (chunk, sequence, split) triple is one work item.
+// (an anchor and the layers that inherit its cache) of one table, cut into nrc
+// chunks of at most 64 rows, over the n_seq sequences [seq_base, seq_base +
+// n_seq) of the batch that use the table; every (chunk, sequence, split)
+// triple is one work item.  The cache holds those sequences at indices
+// [0, n_seq); the layers of the group are group_layers[lay_begin ...], indices
+// into the layer array whose table starts at layer_base (model layer =
+// index - layer_base).
 struct EntryArg {
   const uint8_t* codes;
   const float* scales;
   int64_t ws_off;        // float offset of this entry's split partials
   int32_t item_base;     // first work item (decode kernel block)
-  int32_t merge_base;    // first merge block (only when splits > 1)
+  int32_t merge_base;    // first merge block (monotone over entries)
   int32_t row_stride;    // bytes per cached row
   int32_t row_begin, row_end;
+  int32_t seq_base, n_seq;
+  int32_t lay_begin, layer_base;
   int16_t d, bits;
   int16_t nrc, chunk_rows;
-  int16_t splits, lay_begin;
-  int16_t nbuf, pad_;    // LDS tile buffers of this entry (nbuf - 1 tiles in flight)
+  int16_t splits;
+  int16_t nbuf;          // LDS tile buffers of this entry (nbuf - 1 tiles in flight)
+};
+
+// The entry, layer and group-layer arrays sit in the launch arguments for one
+// table; for several tables they sit in device memory (plan != nullptr).
+struct DevicePlan {
+  const EntryArg* entries;
+  const LayerArg* layers;
+  const uint16_t* group_layers;
 };
 
 struct DecodeArgs {
@@ -53,10 +68,11 @@ struct DecodeArgs {
   float* out;
   float* ws;
   const int32_t* seq_lens;
+  DevicePlan plan;                    // entries == nullptr: the arrays below
   int32_t batch, heads, r, d_rope, t_cap;
   int32_t n_entries, total_items;
   int32_t q_is_f32;
-  uint8_t group_layers[kMaxLayers];   // layers ordered by group
+  uint16_t group_layers[kMaxLayers];  // layers ordered by group
   LayerArg layers[kMaxLayers];
   EntryArg entries[kMaxEntries];
 };
@@ -108,5 +124,10 @@ struct DecodeLaunch {
 int decode_nbuf(int row_stride, int K, int bits, int row_blocks);
 int decode_lds_bytes(int row_stride, int K, int bits, int row_blocks);
 hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t stream);
+
+// Copies `words` 32-bit words from host memory to device memory `dst` by
+// kernel launches whose arguments carry the data (stream-ordered, no host
+// memory has to outlive the call).
+hipError_t launch_store(uint32_t* dst, const uint32_t* words, int64_t n_words, hipStream_t stream);
 
 }  // namespace kk

@@ -41,6 +41,10 @@ class Cache(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
+class TableBatch(ctypes.Structure):
+    _fields_ = [("cfg", ctypes.POINTER(ModelCfg)), ("batch", ctypes.c_int32), ("caches", ctypes.POINTER(Cache))]
+
+
 _lib = None
 
 
@@ -72,10 +76,18 @@ def lib():
                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                        ctypes.c_void_p]
+        L.kk_multi_out_offsets.argtypes = [ctypes.POINTER(TableBatch), ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
+        L.kk_multi_decode_workspace_bytes.argtypes = [ctypes.POINTER(TableBatch), ctypes.c_int32, ctypes.c_int32,
+                                                      ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.kk_multi_decode_attn.argtypes = [ctypes.POINTER(TableBatch), ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                           ctypes.c_size_t, ctypes.c_void_p]
         L.kk_status_string.restype = ctypes.c_char_p
         L.kk_status_string.argtypes = [ctypes.c_int]
         for name in ("kk_validate_model", "kk_cache_bytes", "kk_out_offsets", "kk_quantize_write",
-                     "kk_decode_workspace_bytes", "kk_decode_attn", "kk_append_decode"):
+                     "kk_decode_workspace_bytes", "kk_decode_attn", "kk_append_decode", "kk_multi_out_offsets",
+                     "kk_multi_decode_workspace_bytes", "kk_multi_decode_attn"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -253,3 +265,59 @@ class Decoder:
         """View of layer l's output [B, H, d_eff]."""
         m = self.model
         return self.out[self.offsets[l]:self.offsets[l + 1]].view(self.batch, m.n_heads, m.d_eff(l))
+
+
+def _cache_table(model: Model, caches: dict):
+    tab = (Cache * model.n_layers)()
+    for l in range(model.n_layers):
+        if model.layers[l].anchor == l:
+            c, s = caches[l]
+            tab[l] = Cache(c.data_ptr(), s.data_ptr())
+    return tab
+
+
+class MultiDecoder:
+    """kk_multi_decode_attn: one decode step over a batch whose runs of
+    sequences use different tables.  runs: list of (Model, caches, batch); the
+    runs' sequences follow one another in the batch, in list order."""
+
+    def __init__(self, runs, t_cap: int, max_seq_len: int, split_tokens: int = 0, device="cuda"):
+        self.runs = list(runs)
+        self.models = [m for m, _, _ in self.runs]
+        m0 = self.models[0]
+        self.n_layers, self.n_heads, self.r, self.d_rope = m0.n_layers, m0.n_heads, m0.r, m0.d_rope
+        self.batches = [int(b) for _, _, b in self.runs]
+        self.batch = sum(self.batches)
+        self.t_cap, self.max_seq_len, self.split_tokens = t_cap, max_seq_len, split_tokens
+        self._ctabs = [_cache_table(m, c) if c is not None else None for m, c, _ in self.runs]
+        self._tabs = (TableBatch * len(self.runs))(*[
+            TableBatch(ctypes.pointer(m._cfg), b, ctab if ctab is not None else None)
+            for (m, _, b), ctab in zip(self.runs, self._ctabs)])
+        n = len(self.runs)
+        offs = (ctypes.c_int64 * (n * self.n_layers + 1))()
+        _check(lib().kk_multi_out_offsets(self._tabs, n, offs), "kk_multi_out_offsets")
+        self.offsets = list(offs)
+        self.out = torch.empty(self.offsets[-1], dtype=torch.float32, device=device)
+        wb = ctypes.c_size_t()
+        _check(lib().kk_multi_decode_workspace_bytes(self._tabs, n, max_seq_len, split_tokens, ctypes.byref(wb)),
+               "kk_multi_decode_workspace_bytes")
+        self.ws_bytes = wb.value
+        self.workspace = torch.empty(self.ws_bytes // 4 + 64, dtype=torch.float32, device=device)
+
+    def __call__(self, q_lat: torch.Tensor, q_rope: torch.Tensor, seq_lens: torch.Tensor, stream=None):
+        assert q_lat.is_contiguous() and q_rope.is_contiguous() and q_lat.dtype == q_rope.dtype
+        assert tuple(q_lat.shape) == (self.n_layers, self.batch, self.n_heads, self.r)
+        assert tuple(q_rope.shape) == (self.n_layers, self.batch, self.n_heads, self.d_rope)
+        assert seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.numel() == self.batch
+        wptr = (self.workspace.data_ptr() + 255) // 256 * 256
+        st = lib().kk_multi_decode_attn(self._tabs, len(self.runs), self.t_cap, _ptr(seq_lens), self.max_seq_len,
+                                        _ptr(q_lat), _ptr(q_rope), _dtype_code(q_lat.dtype), _ptr(self.out),
+                                        self.split_tokens, ctypes.c_void_p(wptr), self.ws_bytes, _stream(stream))
+        _check(st, "kk_multi_decode_attn")
+        return self.out
+
+    def layer_out(self, run: int, l: int) -> torch.Tensor:
+        """View of run `run`'s layer l output [batch_run, H, d_eff]."""
+        k = run * self.n_layers + l
+        return self.out[self.offsets[k]:self.offsets[k + 1]].view(self.batches[run], self.n_heads,
+                                                                   self.models[run].d_eff(l))

@@ -75,6 +75,7 @@ typedef enum { KK_DTYPE_F32 = 0, KK_DTYPE_BF16 = 1 } kk_dtype;
 #define KK_MAX_LAYERS 64
 #define KK_MAX_D 512           /* kept latent width d (and r >= d, any r) */
 #define KK_MAX_K 576           /* d + d_R (512 + 64, the MLA shape) */
+#define KK_MAX_TABLES 1024     /* tables of one heterogeneous step */
 
 /* One layer's action ("Action Space and Cost Model").
  *   anchor == own index : the layer is an anchor with action (d, bits);
@@ -198,6 +199,56 @@ kk_status kk_append_decode(const kk_model_cfg* cfg, const kk_cache* caches, int3
                            const void* new_rope, kk_dtype src_dtype, const void* q_lat, const void* q_rope,
                            kk_dtype q_dtype, float* out, int32_t split_tokens, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/* ---- Heterogeneous tables in one batch -------------------------------------
+ * The selector chooses a table per prompt, from that prompt's context, before
+ * its pre-fill (KV-Kaizen summary page, "Selector Architecture and Training":
+ * the context-adaptive selector and its Inference item), so the sequences of
+ * one serving batch can carry different tables.  One call decodes them all in
+ * one fused launch.
+ *
+ * The batch is cut into n_tables contiguous runs of sequences: run k holds
+ * tables[k].batch sequences, starting at the sum of the earlier runs' sizes,
+ * and is decoded exactly as kk_decode_attn would decode it with table
+ * tables[k].cfg over caches tables[k].caches (whose sequence index is the
+ * position within the run).  Every table has the same n_layers, n_heads, r
+ * and d_rope (they describe one model); anchors, widths, precisions and
+ * softmax scales may differ.  One table per sequence is n_tables = batch. */
+typedef struct {
+  const kk_model_cfg* cfg;     /* the table (host) */
+  int32_t batch;               /* sequences of the run, >= 1 */
+  const kk_cache* caches;      /* host [n_layers]: the run's anchor caches, each
+                                  [batch][t_cap] as for kk_decode_attn (may be
+                                  NULL for the size queries) */
+} kk_table_batch;
+
+/* Float offsets of the output blocks: offsets[k * n_layers + l] is where layer
+ * l of run k starts, as [tables[k].batch][n_heads][d_eff(k, l)] float32;
+ * offsets[n_tables * n_layers] = total floats.  Host array. */
+kk_status kk_multi_out_offsets(const kk_table_batch* tables, int32_t n_tables, int64_t* offsets);
+
+/* Workspace bytes of kk_multi_decode_attn (always > 0: the work plan lives in
+ * the workspace next to the split partials). */
+kk_status kk_multi_decode_workspace_bytes(const kk_table_batch* tables, int32_t n_tables, int32_t max_seq_len,
+                                          int32_t split_tokens, size_t* bytes);
+
+/* One decode step over a heterogeneous batch of B = sum of tables[k].batch
+ * sequences.
+ * seq_lens : device int32 [B], clamped to [0, t_cap] as for kk_decode_attn.
+ * q_lat    : device [n_layers][B][n_heads][r], q_dtype.
+ * q_rope   : device [n_layers][B][n_heads][d_rope], q_dtype.
+ * out      : device float32, packed as kk_multi_out_offsets describes.
+ * workspace: device, >= kk_multi_decode_workspace_bytes, 256-byte aligned.
+ *            The call first writes its work plan into the workspace (small
+ *            launches whose arguments carry it), then decodes; calls that
+ *            share a workspace must be ordered on one stream.
+ * max_seq_len and split_tokens as for kk_decode_attn.  Results for a run are
+ * those kk_decode_attn gives for it alone, within floating-point rounding
+ * (the split choice depends on the whole batch). */
+kk_status kk_multi_decode_attn(const kk_table_batch* tables, int32_t n_tables, int32_t t_cap, const int32_t* seq_lens,
+                               int32_t max_seq_len, const void* q_lat, const void* q_rope, kk_dtype q_dtype,
+                               float* out, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 /* Static description of a status code. */
 const char* kk_status_string(kk_status status);

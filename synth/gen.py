@@ -152,6 +152,25 @@ def workload(wid: int) -> Workload:
     raise ValueError(wid)
 
 
+HETERO_WID = 5   # data seeds of run k of the heterogeneous batch: workload HETERO_WID + k
+
+
+def hetero_tables_14b():
+    """The four frozen tables of the heterogeneous-batch workload."""
+    with open(os.path.join(GOLDEN_DIR, "tables_14b_hetero.json")) as f:
+        return [x["table"] for x in json.load(f)["tables"]]
+
+
+def hetero_workloads(batch_per_table: int = 8, seq_len: int = 8192, tables=None, n_heads: int = 40,
+                     r: int = 512, d_rope: int = 64):
+    """14B-shaped heterogeneous batch: run k (k = 0..3) holds batch_per_table
+    sequences that use table k, with its own data seeds.  Returns one
+    Workload per run; the runs follow one another in the batch."""
+    tables = hetero_tables_14b() if tables is None else tables
+    return [Workload(HETERO_WID + k, f"14b_hetero_run{k}", len(t), n_heads, batch_per_table, seq_len, r, d_rope,
+                     torch.bfloat16, layers_from_table(t, d_rope)) for k, t in enumerate(tables)]
+
+
 def small_workload(wid: int, n_layers: int, n_heads: int, batch: int, seq_len: int, r: int, d_rope: int,
                    table, q_dtype=torch.bfloat16, name="small") -> Workload:
     return Workload(wid, name, n_layers, n_heads, batch, seq_len, r, d_rope, q_dtype,

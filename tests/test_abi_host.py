@@ -34,7 +34,8 @@ def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("kk_quantize_write", "kk_decode_attn", "kk_decode_workspace_bytes", "kk_cache_bytes",
               "kk_out_offsets", "kk_validate_model", "kk_row_stride_bytes", "kk_status_string",
-              "kk_append_decode"):
+              "kk_append_decode", "kk_multi_out_offsets", "kk_multi_decode_workspace_bytes",
+              "kk_multi_decode_attn"):
         assert n in names
 
 
@@ -231,6 +232,95 @@ def test_quantize_write_rejects_bad_arguments_before_launch(kk):
     assert call(codes=fake(1, 8).value) == kk.KK_ERR_INVALID_ARGUMENT  # codes not 16-byte aligned
     assert call(latent=fake(3, 2)) == kk.KK_ERR_INVALID_ARGUMENT       # f32 rows not 4-byte aligned
     assert call(n_tok=0) == kk.KK_OK                                   # nothing to write: no launch
+
+
+def _runs(kk, specs, fake=None, heads=16, r=128, dr=32):
+    """specs: list of (table rows, batch); returns (models, TableBatch array, cache arrays)."""
+    models, ctabs = [], []
+    for i, (rows, b) in enumerate(specs):
+        m = table(rows, r=r, dr=dr, heads=heads, kk=kk)
+        models.append(m)
+        ct = None
+        if fake is not None:
+            ct = (kk.Cache * len(rows))()
+            for l, (a, _, _) in enumerate(rows):
+                if a == l:
+                    ct[l] = kk.Cache(fake(16 * i + 2 * l + 20).value, fake(16 * i + 2 * l + 21).value)
+        ctabs.append(ct)
+    arr = (kk.kk.TableBatch * len(specs))(*[kk.kk.TableBatch(ctypes.pointer(m._cfg), b, ct)
+                                           for m, (_, b), ct in zip(models, specs, ctabs)])
+    return models, arr, ctabs
+
+
+SPECS = [([[0, 128, 4], [0, 0, 0], [2, 64, 8]], 2), ([[0, 32, 16], [1, 96, 2], [1, 0, 0]], 3)]
+
+
+def test_multi_offsets_and_workspace(kk):
+    L = kk.lib()
+    models, arr, _ = _runs(kk, SPECS)
+    offs = (ctypes.c_int64 * 7)()
+    assert L.kk_multi_out_offsets(arr, 2, offs) == kk.KK_OK
+    want, base = [], 0
+    for m, (_, b) in zip(models, SPECS):
+        one = kk.out_offsets(m, b)
+        want += [base + x for x in one[:-1]]
+        base += one[-1]
+    assert list(offs) == want + [base]
+    ws = ctypes.c_size_t()
+    assert L.kk_multi_decode_workspace_bytes(arr, 2, 1024, 0, ctypes.byref(ws)) == kk.KK_OK
+    assert ws.value > 0 and ws.value % 256 == 0
+    ws_split = ctypes.c_size_t()
+    assert L.kk_multi_decode_workspace_bytes(arr, 2, 1024, 64, ctypes.byref(ws_split)) == kk.KK_OK
+    assert ws_split.value > ws.value                                    # partials of 16 splits
+    assert L.kk_multi_decode_workspace_bytes(arr, 2, 1024, 48, ctypes.byref(ws)) == kk.KK_ERR_INVALID_ARGUMENT
+    assert L.kk_multi_out_offsets(arr, 0, offs) == kk.KK_ERR_INVALID_ARGUMENT
+    assert L.kk_multi_out_offsets(None, 2, offs) == kk.KK_ERR_INVALID_ARGUMENT
+    # the tables must describe one model: same layers, heads, r and d_R
+    _, other, _ = _runs(kk, [SPECS[0], ([[0, 128, 4], [0, 0, 0], [2, 64, 8]], 1)], heads=8)
+    _, mixed, _ = _runs(kk, [SPECS[0]])
+    mix = (kk.kk.TableBatch * 2)(mixed[0], other[1])
+    assert L.kk_multi_out_offsets(mix, 2, offs) == kk.KK_ERR_INVALID_ARGUMENT
+    _, zero, _ = _runs(kk, [SPECS[0], (SPECS[1][0], 0)])
+    assert L.kk_multi_out_offsets(zero, 2, offs) == kk.KK_ERR_INVALID_ARGUMENT
+    _, badt, _ = _runs(kk, [SPECS[0], ([[0, 128, 4], [2, 0, 0], [2, 64, 8]], 1)])  # inherits from a later layer
+    assert L.kk_multi_out_offsets(badt, 2, offs) == kk.KK_ERR_INVALID_ARGUMENT
+    big = (kk.kk.TableBatch * 1025)(*([arr[0]] * 1025))
+    assert L.kk_multi_out_offsets(big, 1025, (ctypes.c_int64 * (3 * 1025 + 1))()) == kk.KK_ERR_UNSUPPORTED
+
+
+def test_multi_decode_rejects_bad_arguments_before_launch(kk):
+    L = kk.lib()
+    fake = _Fake()
+    models, arr, ctabs = _runs(kk, SPECS, fake)
+    T = 1024
+    need = ctypes.c_size_t()
+    assert L.kk_multi_decode_workspace_bytes(arr, 2, T, 64, ctypes.byref(need)) == kk.KK_OK
+    need = need.value
+
+    def call(**kw):
+        a = dict(tabs=arr, n=2, t_cap=T, seq_lens=fake(5), max_len=T, q_lat=fake(6), q_rope=fake(7),
+                 q_dtype=kk.KK_DTYPE_BF16, out=fake(8), split=64, ws=fake(9), ws_bytes=need)
+        a.update(kw)
+        return L.kk_multi_decode_attn(a["tabs"], a["n"], a["t_cap"], a["seq_lens"], a["max_len"], a["q_lat"],
+                                      a["q_rope"], a["q_dtype"], a["out"], a["split"], a["ws"], a["ws_bytes"], None)
+
+    assert call(ws_bytes=need - 1) == kk.KK_ERR_WORKSPACE_TOO_SMALL
+    assert call(ws=fake(9, 16)) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(ws=None) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(q_rope=fake(7, 8)) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(seq_lens=None) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(max_len=T + 1) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(split=33) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(q_dtype=4) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(n=0) == kk.KK_ERR_INVALID_ARGUMENT
+    nocache = (kk.kk.TableBatch * 2)(arr[0], kk.kk.TableBatch(ctypes.pointer(models[1]._cfg), 3, None))
+    assert call(tabs=nocache) == kk.KK_ERR_INVALID_ARGUMENT            # a run without caches
+    hole = (kk.Cache * 3)()
+    hole[0] = ctabs[1][0]                                              # anchor 1 of run 1 has no buffers
+    holed = (kk.kk.TableBatch * 2)(arr[0], kk.kk.TableBatch(ctypes.pointer(models[1]._cfg), 3, hole))
+    assert call(tabs=holed) == kk.KK_ERR_INVALID_ARGUMENT
+    hole[1] = kk.Cache(fake(60, 4).value, fake(61).value)              # codes not 16-byte aligned
+    assert call(tabs=holed) == kk.KK_ERR_INVALID_ARGUMENT
 
 
 def test_status_strings(kk):
