@@ -388,6 +388,27 @@ def test_mixed_table_fixture_is_reproducible_and_valid():
     assert 0.2 <= inh / 48 <= 0.45
 
 
+def test_hetero_tables_fixture_is_reproducible_and_valid():
+    import importlib.util
+    here = os.path.dirname(os.path.abspath(__file__))
+    spec = importlib.util.spec_from_file_location("mk", os.path.join(here, "golden", "make_table_14b_mixed.py"))
+    mk = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mk)
+    fixture = json.load(open(os.path.join(here, "golden", "tables_14b_hetero.json")))
+    single = json.load(open(os.path.join(here, "golden", "table_14b_mixed.json")))
+    assert [x["seed"] for x in fixture["tables"]] == list(mk.HETERO_SEEDS)
+    assert fixture["tables"][0]["table"] == single["table"]
+    full = 48 * ((512 + 64) * 16 + 32)
+    seen = set()
+    for x in fixture["tables"]:
+        t, draws, bits = mk.freeze(x["seed"])
+        assert (t, draws, bits) == (x["table"], x["draws"], x["bits_per_token"])
+        assert abs(bits / (full / 4) - 1) <= 0.01
+        ko.resolve_table([ko.Layer(a, d, b, 1.0) for a, d, b in t], 512)    # a valid table
+        seen.add(json.dumps(t))
+    assert len(seen) == 4                                                   # four different tables
+
+
 def test_eviction_positions():
     s = synth.gen_scores(4, 0, 65536)
     pos = synth.keep_positions(s, 8192)
