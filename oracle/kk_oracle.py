@@ -38,6 +38,14 @@ Readings where the pages are silent (each is listed in the design doc):
 * Absorbed-MLA attention per head h: z_t = sm_scale * (q_lat[:d] . c_t[:d] +
   q_rope . k^R_t) on the dequantized cache, softmax over the cached tokens,
   o = sum_t p_t c_t[:d].  An empty cache gives o = 0.
+* Latent epilogue (the MLA value path after attention; the pages name the
+  shared latent and its truncation, section "Three Non-Eviction Compression
+  Axes", item 2, but not the projections): head h's value is its block of
+  the value up-projection W_UV [H * d_v, r] applied to o restricted to the
+  kept coordinates, v_h = W_UV[h*d_v:(h+1)*d_v, :d] o_h, and the layer output
+  is y = W_O [v_1; ...; v_H] with W_O [D, H * d_v].  Because attention is
+  linear in the values, this equals attention over the per-token values
+  W_UV[h] c_t[:d] (the non-absorbed form), which pins it.
 
 Floating point: the quantizer runs in numpy float32 (its decisions are
 defined in fp32); dequantization and attention run in float64.
@@ -219,6 +227,26 @@ def decode_layer(q_lat: np.ndarray, q_rope: np.ndarray, packed: np.ndarray, scal
     xhat = dequantize_rows(codes, scales[:seq_len])
     qv = np.concatenate([np.asarray(q_lat, np.float64)[:, :d], np.asarray(q_rope, np.float64)], axis=1)
     return attend(qv, xhat, d, sm_scale)
+
+
+def latent_epilogue(o_lat: np.ndarray, w_uv: np.ndarray, w_o: np.ndarray, d_v: int):
+    """Value up-projection and output projection of one layer.
+
+    o_lat [B, H, d] (attention output in the kept latent coordinates),
+    w_uv [H * d_v, r] with r >= d (columns d.. are not used), w_o [D, H * d_v].
+    Returns (v [B, H, d_v], y [B, D]) in float64:
+      v[b, h, j] = sum_{i<d} w_uv[h*d_v + j, i] * o_lat[b, h, i]
+      y[b, n]    = sum_{h, j} w_o[n, h*d_v + j] * v[b, h, j]
+    """
+    o = np.asarray(o_lat, np.float64)
+    bsz, heads, d = o.shape
+    wu = np.asarray(w_uv, np.float64)
+    wo = np.asarray(w_o, np.float64)
+    v = np.empty((bsz, heads, d_v), np.float64)
+    for h in range(heads):
+        v[:, h, :] = o[:, h, :] @ wu[h * d_v:(h + 1) * d_v, :d].T
+    y = v.reshape(bsz, heads * d_v) @ wo.T
+    return v, y
 
 
 def partial_state(qv, xhat, d, sm_scale):

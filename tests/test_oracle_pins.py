@@ -362,6 +362,71 @@ def test_table_rules():
 
 
 # ----------------------------------------------------------------------------
+# latent epilogue (value up-projection, output projection)
+# ----------------------------------------------------------------------------
+
+def test_epilogue_identity_blocks_and_permutation():
+    """W_UV blocks that copy the kept coordinates (d_v = d) give v = o exactly;
+    a permutation W_O then reorders the concatenated heads."""
+    rng = np.random.default_rng(3)
+    B, H, d, r = 2, 3, 8, 12
+    o = rng.standard_normal((B, H, d))
+    w_uv = rng.standard_normal((H * d, r))          # columns >= d are never read
+    for h in range(H):
+        w_uv[h * d:(h + 1) * d, :d] = np.eye(d)
+    perm = rng.permutation(H * d)
+    w_o = np.eye(H * d)[perm]
+    v, y = ko.latent_epilogue(o, w_uv, w_o, d)
+    assert np.array_equal(v, o)
+    assert np.array_equal(y, o.reshape(B, H * d)[:, perm])
+
+
+def test_epilogue_ignores_columns_past_the_kept_width():
+    rng = np.random.default_rng(4)
+    B, H, d, r, dv, D = 2, 2, 8, 16, 5, 7
+    o = rng.standard_normal((B, H, d))
+    w_uv = rng.standard_normal((H * dv, r))
+    w_o = rng.standard_normal((D, H * dv))
+    v1, y1 = ko.latent_epilogue(o, w_uv, w_o, dv)
+    w_uv[:, d:] = rng.standard_normal((H * dv, r - d)) * 1e6
+    v2, y2 = ko.latent_epilogue(o, w_uv, w_o, dv)
+    assert np.array_equal(v1, v2) and np.array_equal(y1, y2)
+
+
+def test_epilogue_after_absorbed_decode_equals_attention_over_projected_values():
+    """Linearity of attention in its values: decoding in the latent space and
+    then projecting (the absorbed form) equals attention whose values are the
+    per-token projections W_UV[h] c_t[:d] (the non-absorbed form), softmax
+    taken here with scipy, then W_O."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(5)
+    H, d, r, dr, dv, D, T, bits = 3, 16, 24, 8, 6, 10, 40, 8
+    lat = rng.standard_normal((T, r)).astype(np.float32)
+    rope = rng.standard_normal((T, dr)).astype(np.float32)
+    q_lat = rng.standard_normal((H, r))
+    q_rope = rng.standard_normal((H, dr))
+    w_uv = rng.standard_normal((H * dv, r)) / np.sqrt(r)
+    w_o = rng.standard_normal((D, H * dv)) / np.sqrt(H * dv)
+    sm = 0.3
+    packed, scales, _ = ko.write_cache(lat, rope, d, bits)
+    o = ko.decode_layer(q_lat, q_rope, packed, scales, d, dr, bits, sm, T)
+    v, y = ko.latent_epilogue(o[None], w_uv, w_o, dv)
+    xhat = ko.dequantize_rows(ko.unpack_rows(packed, bits, d + dr), scales)
+    keys = xhat                                                       # [c[:d] || k^R]
+    y_ref = np.zeros(D)
+    vs = []
+    for h in range(H):
+        qh = np.concatenate([q_lat[h, :d], q_rope[h]])
+        p = softmax(sm * (keys @ qh))
+        vals = xhat[:, :d] @ w_uv[h * dv:(h + 1) * dv, :d].T           # [T, dv] per-token values
+        vh = p @ vals
+        vs.append(vh)
+        y_ref += w_o[:, h * dv:(h + 1) * dv] @ vh
+    np.testing.assert_allclose(v[0], np.stack(vs), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(y[0], y_ref, rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
 # fixtures and generators
 # ----------------------------------------------------------------------------
 
