@@ -51,6 +51,17 @@ def algorithmic_bytes(kk, w):
     return cache + q + out, cache
 
 
+def epilogue_bytes(w, d_v, d_model):
+    """Per step: W_UV blocks on the kept coordinates + W_O (bf16), o_lat read, v written and read, y written."""
+    H = w.n_heads
+    tot = 0
+    for l in range(w.n_layers):
+        d = w.d_eff(l)
+        tot += H * d_v * d * 2 + d_model * H * d_v * 2
+        tot += w.batch * H * d * 4 + 2 * w.batch * H * d_v * 4 + w.batch * d_model * 4
+    return tot
+
+
 def useful_flops(w):
     """Q.K and P.V multiply-adds per step: B*T*(2H(d+d_R) + 2Hd) per layer."""
     return sum(w.batch * w.seq_len * (2 * w.n_heads * (w.d_eff(l) + w.d_rope) + 2 * w.n_heads * w.d_eff(l))
@@ -172,6 +183,9 @@ def main():
                     help="time kk_append_decode (write each sequence's newest token into every anchor, then decode)")
     ap.add_argument("--hetero", action="store_true",
                     help="time kk_multi_decode_attn on the heterogeneous 14B batch (four tables, 8 sequences each)")
+    ap.add_argument("--epilogue", action="store_true",
+                    help="time kk_latent_epilogue (W_UV per head, then W_O; 14B shapes d_v = 128, d_model = 5120) "
+                         "on the decode output")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run 3 device-to-device copies of this size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -203,8 +217,8 @@ def main():
         sys.exit(1)
     t_setup = time.perf_counter()
     if args.hetero:
-        if args.append:
-            print("--append and --hetero are separate steps", file=sys.stderr)
+        if args.append or args.epilogue:
+            print("--hetero times the decode step alone", file=sys.stderr)
             sys.exit(2)
         runs_w = synth.hetero_workloads()
         w = runs_w[0]
@@ -231,6 +245,17 @@ def main():
         seq_lens = torch.full((w.batch,), w.seq_len, dtype=torch.int32, device="cuda")
         dec = kk.Decoder(model, caches, w.batch, w.seq_len, w.seq_len, split_tokens=args.split_tokens)
         step = lambda: dec(ql, qr, seq_lens)
+    if args.epilogue and args.append:
+        print("--epilogue and --append are separate steps", file=sys.stderr)
+        sys.exit(2)
+    if args.epilogue:
+        d_v, d_model = 128, 5120
+        dec(ql, qr, seq_lens)
+        wts = [synth.gen_epilogue_weights(w.wid, l, w.n_heads, d_v, w.r, d_model, "cuda") for l in range(w.n_layers)]
+        w_uv, w_o = [a for a, _ in wts], [b for _, b in wts]
+        v_buf = torch.empty(w.n_layers, w.batch, w.n_heads * d_v, dtype=torch.float32, device="cuda")
+        y_buf = torch.empty(w.n_layers, w.batch, d_model, dtype=torch.float32, device="cuda")
+        step = lambda: kk.latent_epilogue(model, w.batch, dec.out, w_uv, w_o, v_buf, y_buf)
     if args.append:
         # the newest token of each sequence (row seq_len - 1) is rewritten from seeded rows every step
         g = torch.Generator(device="cuda").manual_seed(1234)
@@ -270,8 +295,12 @@ def main():
 
     U = sum(algorithmic_bytes(kk, rw)[0] for rw in runs_w)
     flops = sum(useful_flops(rw) for rw in runs_w)
+    if args.epilogue:
+        U = epilogue_bytes(w, d_v, d_model)
+        flops = sum(2 * w.batch * w.n_heads * d_v * w.d_eff(l) + 2 * w.batch * d_model * w.n_heads * d_v
+                    for l in range(w.n_layers))
     achieved = U / (mean_dev_ms * 1e-3) / 1e9
-    name = "14b_hetero_4tables" if args.hetero else w.name
+    name = "14b_hetero_4tables" if args.hetero else (w.name + "_epilogue" if args.epilogue else w.name)
     batch = sum(rw.batch for rw in runs_w)
     traffic = stored_traffic(name)
     print(f"[bench] device ms/step mean {mean_dev_ms:.4f} p10 {dev_ms[len(dev_ms) // 10]:.4f} "
@@ -280,7 +309,7 @@ def main():
           file=sys.stderr, flush=True)
 
     cpu = None
-    if not args.no_cpu_baseline and not args.hetero:
+    if not args.no_cpu_baseline and not args.hetero and not args.epilogue:
         cpu = cpu_baseline(w, args.cpu_budget)
 
     anchors = [len(rw.anchors()) for rw in runs_w]
@@ -304,9 +333,11 @@ def main():
                    "bits_per_token": bits_tok if args.hetero else bits_tok[0],
                    "q_dtype": str(w.q_dtype).replace("torch.", ""),
                    "split_tokens": args.split_tokens or "auto", "parallelism": "none (one GPU)",
-                   "step": ("append + decode" if args.append else
+                   "step": ("latent epilogue (W_UV per head, W_O; d_v 128, d_model 5120)" if args.epilogue else
+                            "append + decode" if args.append else
                             "heterogeneous decode (4 tables x 8 sequences)" if args.hetero else "decode")},
-        "roofline": {"bound": "hbm", "kernel": ("append_kernel + " if args.append else
+        "roofline": {"bound": "hbm", "kernel": "epilogue: gemm_kernel (W_UV) + gemm_kernel (W_O)" if args.epilogue else
+                     ("append_kernel + " if args.append else
                                                 "store_kernel (plan upload) + " if args.hetero else "") +
                      "decode step: decode_kernel + merge_kernel",
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",

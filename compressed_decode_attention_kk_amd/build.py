@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkk.so")
-SOURCES = ["kk_host.cpp", "kk_write.hip", "kk_decode.hip"]
+SOURCES = ["kk_host.cpp", "kk_write.hip", "kk_decode.hip", "kk_epilogue.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

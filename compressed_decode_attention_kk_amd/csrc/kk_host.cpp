@@ -584,6 +584,65 @@ kk_status kk_append_decode(const kk_model_cfg* cfg, const kk_cache* caches, int3
   return kk::launch_decode(P.args, P.launch, stream) == hipSuccess ? KK_OK : KK_ERR_DEVICE;
 }
 
+kk_status kk_latent_epilogue(const kk_model_cfg* cfg, int32_t batch, int32_t d_v, int32_t d_model,
+                             const float* o_lat, const void* const* w_uv, const void* const* w_o, float* v, float* y,
+                             hipStream_t stream) {
+  kk_status st = check_model(cfg);
+  if (st != KK_OK) return st;
+  if (batch < 1 || d_v < 8 || d_model < 8 || d_v % 8 || d_model % 8) return KK_ERR_INVALID_ARGUMENT;
+  if (!o_lat || !w_uv || !w_o || !v || !y) return KK_ERR_INVALID_ARGUMENT;
+  if (!aligned(o_lat, 16) || !aligned(v, 16) || !aligned(y, 16)) return KK_ERR_INVALID_ARGUMENT;
+  const int L = cfg->n_layers, H = cfg->n_heads;
+  for (int l = 0; l < L; ++l) {
+    if (!w_uv[l] || !w_o[l] || !aligned(w_uv[l], 16) || !aligned(w_o[l], 16)) return KK_ERR_INVALID_ARGUMENT;
+  }
+  const int64_t hv = (int64_t)H * d_v;
+  const int64_t waves1 = (int64_t)L * H * ((d_v + 63) / 64), waves2 = (int64_t)L * ((d_model + 63) / 64);
+  if (waves1 > 0x7ffffff || waves2 > 0x7ffffff || hv > 0x7fffffff) return KK_ERR_UNSUPPORTED;
+  kk::EpiArgs up, out;
+  std::memset(&up, 0, sizeof(up));
+  std::memset(&out, 0, sizeof(out));
+  up.n_probs = out.n_probs = L;
+  up.batch = out.batch = batch;
+  int64_t off = 0;
+  for (int l = 0; l < L; ++l) {
+    const int d = cfg->layers[cfg->layers[l].anchor].d;
+    float* vl = v + (int64_t)l * batch * hv;
+    kk::GemmProblem& p = up.p[l];              // v_h = W_UV[h][:, :d] o_h
+    p.x = o_lat + off;
+    p.ldx = (int64_t)H * d;
+    p.x_hs = d;
+    p.w = static_cast<const uint16_t*>(w_uv[l]);
+    p.ldw = cfg->r;
+    p.w_hs = (int64_t)d_v * cfg->r;
+    p.y = vl;
+    p.ldy = hv;
+    p.y_hs = d_v;
+    p.n = d_v;
+    p.k = d;
+    p.heads = H;
+    p.n_tiles = (d_v + 63) / 64;
+    p.wave_base = up.total_waves;
+    up.total_waves += p.heads * p.n_tiles;
+    kk::GemmProblem& q = out.p[l];             // y = W_O [v_1; ...; v_H]
+    q.x = vl;
+    q.ldx = hv;
+    q.w = static_cast<const uint16_t*>(w_o[l]);
+    q.ldw = hv;
+    q.y = y + (int64_t)l * batch * d_model;
+    q.ldy = d_model;
+    q.n = d_model;
+    q.k = (int32_t)hv;
+    q.heads = 1;
+    q.n_tiles = (d_model + 255) / 256;             // 256-row workgroups
+    q.wave_base = out.total_waves;
+    out.total_waves += q.n_tiles;
+    off += (int64_t)batch * H * d;
+  }
+  if (kk::launch_epilogue_gemm(up, stream) != hipSuccess) return KK_ERR_DEVICE;
+  return kk::launch_epilogue_gemm_wide(out, stream) == hipSuccess ? KK_OK : KK_ERR_DEVICE;
+}
+
 const char* kk_status_string(kk_status s) {
   switch (s) {
     case KK_OK: return "ok";

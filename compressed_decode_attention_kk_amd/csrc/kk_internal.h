@@ -113,6 +113,30 @@ struct AppendArgs {
   AppendAnchor anchors[kMaxLayers];
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+// Latent epilogue: batched skinny products Y[b][n] = sum_k X[b][k] W[n][k]
+// (X fp32 [batch][ldx], W bf16 [N][ldw], Y fp32 [batch][ldy]), one problem
+// per layer, `heads` copies per problem at the given element strides.  Each
+// wave computes 64 rows n of one copy for the whole batch.
+struct GemmProblem {
+  const float* x;
+  const uint16_t* w;
+  float* y;
+  int64_t ldx, ldw, ldy;
+  int64_t x_hs, w_hs, y_hs;      // strides between the heads' copies
+  int32_t n, k, heads;
+  int32_t n_tiles;               // ceil(n / 64)
+  int32_t wave_base;             // first wave of this problem
+};
+struct EpiArgs {
+  int32_t n_probs, total_waves, batch, pad_;
+  GemmProblem p[kMaxLayers];
+};
+hipError_t launch_epilogue_gemm(const EpiArgs& a, hipStream_t stream);
+// Single-copy problems (heads == 1): workgroups of 256 rows sharing the
+// activations through LDS; wave_base / total_waves count workgroups
+// (n_tiles = ceil(n / 256)).
+hipError_t launch_epilogue_gemm_wide(const EpiArgs& a, hipStream_t stream);
+
 // One decode launch covers every work item of the step (all bit widths).
 struct DecodeLaunch {
   int items;

@@ -83,11 +83,15 @@ def lib():
                                            ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
                                            ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                            ctypes.c_size_t, ctypes.c_void_p]
+        L.kk_latent_epilogue.argtypes = [ctypes.POINTER(ModelCfg), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
+                                         ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]
         L.kk_status_string.restype = ctypes.c_char_p
         L.kk_status_string.argtypes = [ctypes.c_int]
         for name in ("kk_validate_model", "kk_cache_bytes", "kk_out_offsets", "kk_quantize_write",
                      "kk_decode_workspace_bytes", "kk_decode_attn", "kk_append_decode", "kk_multi_out_offsets",
-                     "kk_multi_decode_workspace_bytes", "kk_multi_decode_attn"):
+                     "kk_multi_decode_workspace_bytes", "kk_multi_decode_attn", "kk_latent_epilogue"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -321,3 +325,30 @@ class MultiDecoder:
         k = run * self.n_layers + l
         return self.out[self.offsets[k]:self.offsets[k + 1]].view(self.batches[run], self.n_heads,
                                                                    self.models[run].d_eff(l))
+
+
+def latent_epilogue(model: Model, batch: int, o_lat: torch.Tensor, w_uv, w_o, v: torch.Tensor, y: torch.Tensor,
+                    stream=None):
+    """kk_latent_epilogue: per-head value up-projection (W_UV on the kept
+    latent coordinates) and output projection W_O for every layer.
+
+    o_lat: the decode output (packed float32); w_uv: per layer bf16
+    [n_heads * d_v, r]; w_o: per layer bf16 [d_model, n_heads * d_v];
+    v: float32 [n_layers, batch, n_heads * d_v]; y: float32 [n_layers, batch, d_model].
+    """
+    L = model.n_layers
+    assert len(w_uv) == L and len(w_o) == L
+    d_model, hv = w_o[0].shape
+    d_v = hv // model.n_heads
+    for a, b in zip(w_uv, w_o):
+        assert a.dtype == torch.bfloat16 and b.dtype == torch.bfloat16 and a.is_contiguous() and b.is_contiguous()
+        assert tuple(a.shape) == (hv, model.r) and tuple(b.shape) == (d_model, hv)
+    assert o_lat.dtype == torch.float32 and o_lat.is_contiguous()
+    assert tuple(v.shape) == (L, batch, hv) and v.dtype == torch.float32 and v.is_contiguous()
+    assert tuple(y.shape) == (L, batch, d_model) and y.dtype == torch.float32 and y.is_contiguous()
+    pu = (ctypes.c_void_p * L)(*[t.data_ptr() for t in w_uv])
+    po = (ctypes.c_void_p * L)(*[t.data_ptr() for t in w_o])
+    st = lib().kk_latent_epilogue(model.cfg, batch, d_v, d_model, _ptr(o_lat), pu, po, _ptr(v), _ptr(y),
+                                  _stream(stream))
+    _check(st, "kk_latent_epilogue")
+    return v, y

@@ -250,6 +250,36 @@ kk_status kk_multi_decode_attn(const kk_table_batch* tables, int32_t n_tables, i
                                float* out, int32_t split_tokens, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* ---- Latent epilogue ---------------------------------------------------------
+ * Absorbed-MLA decode returns each head's output in the latent space (a
+ * weighted sum of the cached latents c^KV, truncated to the d_eff kept
+ * coordinates: KV-Kaizen summary page, "Three Non-Eviction Compression
+ * Axes", rank item).  The epilogue maps it to the model's output: head h's
+ * value is its block of the value up-projection on the kept coordinates, and
+ * the output projection mixes the heads.  For every layer l, sequence s:
+ *   v[l,s,h,j] = sum_{i < d_eff(l)} W_UV[l][h*d_v + j][i] * o_lat[l,s,h,i]
+ *   y[l,s,n]   = sum_{h, j} W_O[l][n][h*d_v + j] * v[l,s,h,j]
+ * Every layer has its own weights (inheriting layers share a cache, not
+ * weights).
+ *
+ * o_lat : device float32, packed as kk_out_offsets (the kk_decode_attn output).
+ * w_uv  : host array [n_layers] of device bf16 pointers; layer l's is
+ *         [n_heads * d_v][r] row-major (the full up-projection; columns
+ *         d_eff(l) .. r-1 are not read).  16-byte aligned.
+ * w_o   : host array [n_layers] of device bf16 pointers; layer l's is
+ *         [d_model][n_heads * d_v] row-major.  16-byte aligned.
+ * v     : device float32 [n_layers][batch][n_heads * d_v] (written: the
+ *         per-head values).
+ * y     : device float32 [n_layers][batch][d_model] (written).
+ * d_v, d_model: multiples of 8.
+ * Arithmetic: the bf16 weights are used exactly; each fp32 activation enters
+ * as the sum of two bf16 parts (16 significant bits); products accumulate in
+ * fp32.  Two launches on `stream` (up-projection of all layers, then output
+ * projection of all layers); no workspace. */
+kk_status kk_latent_epilogue(const kk_model_cfg* cfg, int32_t batch, int32_t d_v, int32_t d_model,
+                             const float* o_lat, const void* const* w_uv, const void* const* w_o, float* v, float* y,
+                             hipStream_t stream);
+
 /* Static description of a status code. */
 const char* kk_status_string(kk_status status);
 

@@ -24,7 +24,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-KIND_LATENT, KIND_ROPE, KIND_QLAT, KIND_QROPE, KIND_SCORES = 0, 1, 2, 3, 4
+KIND_LATENT, KIND_ROPE, KIND_QLAT, KIND_QROPE, KIND_SCORES, KIND_WUV, KIND_WO = 0, 1, 2, 3, 4, 5, 6
 
 GOLDEN_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "tests", "golden")
 
@@ -61,6 +61,16 @@ def gen_q(workload: int, layer: int, kind: int, shape, width: int, dtype, device
     g = _gen(device, seed_for(workload, layer, kind))
     x = torch.randn(*shape, width, generator=g, device=device, dtype=torch.float32)
     return x.to(dtype)
+
+
+def gen_epilogue_weights(workload: int, layer: int, n_heads: int, d_v: int, r: int, d_model: int, device="cpu"):
+    """Synthetic projection weights of one layer, rounded to bf16:
+    W_UV [n_heads * d_v, r] ~ N(0, 1/r), W_O [d_model, n_heads * d_v] ~ N(0, 1/(n_heads * d_v))."""
+    g = _gen(device, seed_for(workload, layer, KIND_WUV))
+    w_uv = torch.randn(n_heads * d_v, r, generator=g, device=device, dtype=torch.float32) / math.sqrt(r)
+    g = _gen(device, seed_for(workload, layer, KIND_WO))
+    w_o = torch.randn(d_model, n_heads * d_v, generator=g, device=device, dtype=torch.float32) / math.sqrt(n_heads * d_v)
+    return w_uv.to(torch.bfloat16), w_o.to(torch.bfloat16)
 
 
 def gen_scores(workload: int, seq: int, n: int, device="cpu") -> torch.Tensor:

@@ -35,7 +35,7 @@ def test_header_declares_the_entry_points():
     for n in ("kk_quantize_write", "kk_decode_attn", "kk_decode_workspace_bytes", "kk_cache_bytes",
               "kk_out_offsets", "kk_validate_model", "kk_row_stride_bytes", "kk_status_string",
               "kk_append_decode", "kk_multi_out_offsets", "kk_multi_decode_workspace_bytes",
-              "kk_multi_decode_attn"):
+              "kk_multi_decode_attn", "kk_latent_epilogue"):
         assert n in names
 
 
@@ -321,6 +321,30 @@ def test_multi_decode_rejects_bad_arguments_before_launch(kk):
     assert call(tabs=holed) == kk.KK_ERR_INVALID_ARGUMENT
     hole[1] = kk.Cache(fake(60, 4).value, fake(61).value)              # codes not 16-byte aligned
     assert call(tabs=holed) == kk.KK_ERR_INVALID_ARGUMENT
+
+
+def test_latent_epilogue_rejects_bad_arguments_before_launch(kk):
+    L = kk.lib()
+    m = table([[0, 128, 4], [0, 0, 0], [2, 64, 8]], r=128, dr=32, heads=16, kk=kk)
+    fake = _Fake()
+    wu = (ctypes.c_void_p * 3)(fake(10).value, fake(11).value, fake(12).value)
+    wo = (ctypes.c_void_p * 3)(fake(13).value, fake(14).value, fake(15).value)
+
+    def call(batch=4, d_v=64, d_model=256, o=None, u=wu, w=wo, v=None, y=None):
+        return L.kk_latent_epilogue(m.cfg, batch, d_v, d_model, o or fake(1), u, w, v or fake(2), y or fake(3), None)
+
+    assert call(batch=0) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(d_v=60) == kk.KK_ERR_INVALID_ARGUMENT                  # d_v not a multiple of 8
+    assert call(d_model=100) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(o=fake(1, 4)) == kk.KK_ERR_INVALID_ARGUMENT            # o_lat not 16-byte aligned
+    assert call(y=fake(3, 8)) == kk.KK_ERR_INVALID_ARGUMENT
+    assert call(u=None) == kk.KK_ERR_INVALID_ARGUMENT
+    hole = (ctypes.c_void_p * 3)(fake(10).value, None, fake(12).value)  # every layer needs its own weights
+    assert call(u=hole) == kk.KK_ERR_INVALID_ARGUMENT
+    mis = (ctypes.c_void_p * 3)(fake(13).value, fake(14, 2).value, fake(15).value)
+    assert call(w=mis) == kk.KK_ERR_INVALID_ARGUMENT
+    bad = table([[0, 100, 4]], r=128, dr=32, heads=16, kk=kk)           # d not a multiple of 16
+    assert L.kk_latent_epilogue(bad.cfg, 4, 64, 256, fake(1), wu, wo, fake(2), fake(3), None) != kk.KK_OK
 
 
 def test_status_strings(kk):
