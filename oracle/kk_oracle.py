@@ -47,6 +47,15 @@ Readings where the pages are silent (each is listed in the design doc):
   linear in the values, this equals attention over the per-token values
   W_UV[h] c_t[:d] (the non-absorbed form), which pins it.
 
+* Non-MLA variant (precision and depth on a grouped-query cache; the
+  configuration of the "Precision + depth" rows of Table 1 and the KVK 4x
+  row of Table 2): an anchor layer caches keys K and values V per KV head,
+  [n_kv, d_h] each per token, at b bits; inheriting layers read it.  One
+  scale per token covers everything the anchor stores for that token (K and
+  V of all KV heads, as for the MLA row).  Query head h reads KV head
+  h // (H / n_kv): z_t = sm_scale * q_h . K_t, o_h = sum_t softmax(z)_t V_t.
+  The cost of a (b) action is 2 * n_kv * d_h * b bits per token.
+
 Floating point: the quantizer runs in numpy float32 (its decisions are
 defined in fp32); dequantization and attention run in float64.
 """
@@ -247,6 +256,56 @@ def latent_epilogue(o_lat: np.ndarray, w_uv: np.ndarray, w_o: np.ndarray, d_v: i
         v[:, h, :] = o[:, h, :] @ wu[h * d_v:(h + 1) * d_v, :d].T
     y = v.reshape(bsz, heads * d_v) @ wo.T
     return v, y
+
+
+def gqa_write_cache(k: np.ndarray, v: np.ndarray, bits: int):
+    """Quantize one anchor layer of a grouped-query cache.
+
+    k, v [N, n_kv, d_h] (float32 or exactly-widened bf16).  One scale per
+    token over all of that token's K and V values.  Returns (codes_k, codes_v
+    int32 [N, n_kv, d_h], scales float32 [N])."""
+    k = np.asarray(k, np.float32)
+    v = np.asarray(v, np.float32)
+    n, nkv, dh = k.shape
+    codes, scales = quantize_rows(np.concatenate([k.reshape(n, -1), v.reshape(n, -1)], axis=1), bits)
+    return codes[:, :nkv * dh].reshape(n, nkv, dh), codes[:, nkv * dh:].reshape(n, nkv, dh), scales
+
+
+def gqa_pack_kv_rows(codes_k: np.ndarray, codes_v: np.ndarray, bits: int) -> np.ndarray:
+    """The library's row layout: per (token, KV head) one packed row of
+    2 d_h fields, values first then keys, [N, n_kv, stride] uint8."""
+    n, nkv, dh = codes_k.shape
+    rows = np.concatenate([codes_v, codes_k], axis=2).reshape(n * nkv, 2 * dh)
+    return pack_rows(rows, bits).reshape(n, nkv, -1)
+
+
+def gqa_decode_layer(q: np.ndarray, codes_k: np.ndarray, codes_v: np.ndarray, scales: np.ndarray,
+                     sm_scale: float, seq_len: int) -> np.ndarray:
+    """Grouped-query decode for one layer and one sequence: q [H, d_h];
+    codes [T, n_kv, d_h] with scales [T].  Returns o [H, d_h] (float64)."""
+    q = np.asarray(q, np.float64)
+    h_total, dh = q.shape
+    nkv = codes_k.shape[1]
+    group = h_total // nkv
+    sc = np.asarray(scales[:seq_len], np.float64)[:, None]
+    out = np.zeros((h_total, dh), np.float64)
+    if seq_len == 0:
+        return out
+    for g in range(nkv):
+        kh = codes_k[:seq_len, g, :].astype(np.float64) * sc
+        vh = codes_v[:seq_len, g, :].astype(np.float64) * sc
+        for j in range(group):
+            h = g * group + j
+            z = float(sm_scale) * (kh @ q[h])
+            w = np.exp(z - z.max())
+            out[h] = (w @ vh) / w.sum()
+    return out
+
+
+def gqa_table_bits_per_token(layers: list[Layer], n_kv: int, d_head: int, scale_bits: int = SCALE_BITS) -> int:
+    """Stored bits per token of a grouped-query table: per anchor
+    2 * n_kv * d_h * b + one scale."""
+    return sum(2 * n_kv * d_head * lay.bits + scale_bits for l, lay in enumerate(layers) if lay.anchor == l)
 
 
 def partial_state(qv, xhat, d, sm_scale):

@@ -427,6 +427,89 @@ def test_epilogue_after_absorbed_decode_equals_attention_over_projected_values()
 
 
 # ----------------------------------------------------------------------------
+# grouped-query (non-MLA) variant: precision + depth
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("bits", [2, 4, 8, 16])
+def test_gqa_decode_matches_sdpa_with_grouped_heads(bits):
+    """Against torch's fp64 scaled_dot_product_attention with each KV head
+    repeated for its query group, on the dequantized cache."""
+    rng = np.random.default_rng(20 + bits)
+    T, nkv, G, dh = 37, 2, 3, 16
+    k = rng.standard_normal((T, nkv, dh)).astype(np.float32) * 2
+    v = rng.standard_normal((T, nkv, dh)).astype(np.float32)
+    q = rng.standard_normal((nkv * G, dh))
+    ck, cv, sc = ko.gqa_write_cache(k, v, bits)
+    sm = 0.2
+    o = ko.gqa_decode_layer(q, ck, cv, sc, sm, T)
+    kh = torch.from_numpy(ck.astype(np.float64) * sc.astype(np.float64)[:, None, None])
+    vh = torch.from_numpy(cv.astype(np.float64) * sc.astype(np.float64)[:, None, None])
+    kq = kh.permute(1, 0, 2).repeat_interleave(G, dim=0)            # [H, T, dh]
+    vq = vh.permute(1, 0, 2).repeat_interleave(G, dim=0)
+    ref = torch.nn.functional.scaled_dot_product_attention(torch.from_numpy(q)[:, None, :], kq, vq, scale=sm)
+    np.testing.assert_allclose(o, ref[:, 0, :].numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_gqa_one_scale_per_token_over_keys_and_values():
+    rng = np.random.default_rng(31)
+    T, nkv, dh, bits = 9, 3, 8, 4
+    k = rng.standard_normal((T, nkv, dh)).astype(np.float32)
+    v = rng.standard_normal((T, nkv, dh)).astype(np.float32) * 0.1
+    v[4, 2, 5] = 9.0                                                 # the token's largest value is a V entry
+    k[6] = 0
+    v[6] = 0                                                         # an all-zero token
+    ck, cv, sc = ko.gqa_write_cache(k, v, bits)
+    qm = ko.qmax(bits)
+    for t in range(T):
+        amax = max(np.abs(k[t]).max(), np.abs(v[t]).max())
+        assert sc[t] == np.float32(amax) / np.float32(qm)
+        if amax > 0:
+            assert max(np.abs(ck[t]).max(), np.abs(cv[t]).max()) == qm
+    assert cv[4, 2, 5] == qm and sc[6] == 0 and not ck[6].any() and not cv[6].any()
+
+
+def test_gqa_rows_hold_values_then_keys_and_reduce_to_latent_attention():
+    """The library's row per (token, KV head) is [V codes || K codes]; with
+    the query [0 || q_h] and values = the first d_h fields, the latent
+    attention of the MLA path computes the grouped-query output."""
+    rng = np.random.default_rng(32)
+    T, nkv, G, dh, bits = 21, 2, 2, 16, 8
+    k = rng.standard_normal((T, nkv, dh)).astype(np.float32)
+    v = rng.standard_normal((T, nkv, dh)).astype(np.float32)
+    q = rng.standard_normal((nkv * G, dh))
+    ck, cv, sc = ko.gqa_write_cache(k, v, bits)
+    rows = ko.gqa_pack_kv_rows(ck, cv, bits)
+    o = ko.gqa_decode_layer(q, ck, cv, sc, 0.3, T)
+    for g in range(nkv):
+        codes = ko.unpack_rows(rows[:, g, :], bits, 2 * dh)
+        assert np.array_equal(codes[:, :dh], cv[:, g]) and np.array_equal(codes[:, dh:], ck[:, g])
+        xhat = ko.dequantize_rows(codes, sc)
+        qv = np.concatenate([np.zeros((G, dh)), q[g * G:(g + 1) * G]], axis=1)
+        np.testing.assert_allclose(ko.attend(qv, xhat, dh, 0.3), o[g * G:(g + 1) * G], rtol=1e-12, atol=1e-12)
+
+
+def test_gqa_accounting_and_table_fixture():
+    import importlib.util
+    here = os.path.dirname(os.path.abspath(__file__))
+    # C0 of the 14B shape: 48 * 2 * 8 * 128 * 16 bits = 192 KiB per token
+    assert ko.c0_bits(48, 8, 128) == 192 * 1024 * 8
+    # 8-bit anchors on every other layer: 2x from precision times 2x from depth
+    half = [ko.Layer(l if l % 2 == 0 else l - 1, 128, 8, 1.0) for l in range(48)]
+    assert abs(ko.c0_bits(48, 8, 128) / ko.gqa_table_bits_per_token(half, 8, 128) - 4) < 0.01
+    spec = importlib.util.spec_from_file_location("mkg", os.path.join(here, "golden", "make_table_14b_gqa.py"))
+    mk = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mk)
+    fixture = json.load(open(os.path.join(here, "golden", "table_14b_gqa.json")))
+    t, draws, bits = mk.freeze()
+    assert (t, draws, bits) == (fixture["table"], fixture["draws"], fixture["bits_per_token"])
+    assert abs(bits / (ko.c0_bits(48, 8, 128) / 4) - 1) <= 0.01
+    for l, (a, d, b) in enumerate(t):
+        assert a <= l and t[a][0] == a
+        if a == l:
+            assert d == 128 and b in (2, 4, 8, 16)
+
+
+# ----------------------------------------------------------------------------
 # fixtures and generators
 # ----------------------------------------------------------------------------
 
