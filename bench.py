@@ -62,6 +62,15 @@ def epilogue_bytes(w, d_v, d_model):
     return tot
 
 
+def gqa_bytes(kk, w):
+    """Per step: each anchor's codes of every KV head plus one scale per token,
+    the queries read and the fp32 outputs written."""
+    qsize = 4 if str(w.q_dtype) == "torch.float32" else 2
+    cache = sum(w.batch * w.seq_len * (w.n_kv_heads * kk.row_stride_bytes(w.d_head, w.d_head, w.layers[a].bits) + 4)
+                for a in w.anchors())
+    return cache + w.n_layers * w.batch * w.n_q_heads * w.d_head * (qsize + 4)
+
+
 def useful_flops(w):
     """Q.K and P.V multiply-adds per step: B*T*(2H(d+d_R) + 2Hd) per layer."""
     return sum(w.batch * w.seq_len * (2 * w.n_heads * (w.d_eff(l) + w.d_rope) + 2 * w.n_heads * w.d_eff(l))
@@ -186,6 +195,9 @@ def main():
     ap.add_argument("--epilogue", action="store_true",
                     help="time kk_latent_epilogue (W_UV per head, then W_O; 14B shapes d_v = 128, d_model = 5120) "
                          "on the decode output")
+    ap.add_argument("--gqa", action="store_true",
+                    help="time kk_gqa_decode_attn: the grouped-query 14B model (40 query / 8 KV heads of 128) with "
+                         "the frozen 4x precision + depth table, 16 sequences x 16384 tokens")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run 3 device-to-device copies of this size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -216,7 +228,20 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     t_setup = time.perf_counter()
-    if args.hetero:
+    if args.gqa and (args.hetero or args.append or args.epilogue):
+        print("--gqa times the grouped-query decode step alone", file=sys.stderr)
+        sys.exit(2)
+    if args.gqa:
+        from synth.device import build_gqa_caches
+        w = synth.gqa_workload()
+        runs_w = []
+        gm = kk.GqaModel(w.layers, w.n_q_heads, w.n_kv_heads, w.d_head)
+        gcaches = build_gqa_caches(kk, gm, w)
+        gq = synth.gqa_queries(w, "cuda")
+        seq_lens = torch.full((w.batch,), w.seq_len, dtype=torch.int32, device="cuda")
+        dec = kk.GqaDecoder(gm, gcaches, w.batch, w.seq_len, w.seq_len, split_tokens=args.split_tokens)
+        step = lambda: dec(gq, seq_lens)
+    elif args.hetero:
         if args.append or args.epilogue:
             print("--hetero times the decode step alone", file=sys.stderr)
             sys.exit(2)
@@ -295,13 +320,16 @@ def main():
 
     U = sum(algorithmic_bytes(kk, rw)[0] for rw in runs_w)
     flops = sum(useful_flops(rw) for rw in runs_w)
+    if args.gqa:
+        U = gqa_bytes(kk, w)
+        flops = w.n_layers * w.batch * w.seq_len * w.n_q_heads * 4 * w.d_head
     if args.epilogue:
         U = epilogue_bytes(w, d_v, d_model)
         flops = sum(2 * w.batch * w.n_heads * d_v * w.d_eff(l) + 2 * w.batch * d_model * w.n_heads * d_v
                     for l in range(w.n_layers))
     achieved = U / (mean_dev_ms * 1e-3) / 1e9
     name = "14b_hetero_4tables" if args.hetero else (w.name + "_epilogue" if args.epilogue else w.name)
-    batch = sum(rw.batch for rw in runs_w)
+    batch = w.batch if args.gqa else sum(rw.batch for rw in runs_w)
     traffic = stored_traffic(name)
     print(f"[bench] device ms/step mean {mean_dev_ms:.4f} p10 {dev_ms[len(dev_ms) // 10]:.4f} "
           f"p90 {dev_ms[(9 * len(dev_ms)) // 10]:.4f}; wall ms/step {ms_per_step:.4f}; U {U / 1e9:.3f} GB; "
@@ -309,11 +337,15 @@ def main():
           file=sys.stderr, flush=True)
 
     cpu = None
-    if not args.no_cpu_baseline and not args.hetero and not args.epilogue:
+    if not args.no_cpu_baseline and not args.hetero and not args.epilogue and not args.gqa:
         cpu = cpu_baseline(w, args.cpu_budget)
 
-    anchors = [len(rw.anchors()) for rw in runs_w]
-    bits_tok = [sum((rw.layers[a].d + rw.d_rope) * rw.layers[a].bits + 32 for a in rw.anchors()) for rw in runs_w]
+    if args.gqa:
+        anchors = [len(w.anchors())]
+        bits_tok = [sum(2 * w.n_kv_heads * w.d_head * w.layers[a].bits + 32 for a in w.anchors())]
+    else:
+        anchors = [len(rw.anchors()) for rw in runs_w]
+        bits_tok = [sum((rw.layers[a].d + rw.d_rope) * rw.layers[a].bits + 32 for a in rw.anchors()) for rw in runs_w]
     line = {
         "metric": "compressed decode-attn layer*tokens/s",
         "value": w.n_layers * batch / (ms_per_step * 1e-3),
@@ -327,13 +359,15 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": name, "layers": w.n_layers, "heads": w.n_heads, "batch": batch,
-                   "cached_tokens": w.seq_len, "r": w.r, "d_rope": w.d_rope,
+        "config": {"workload": name, "layers": w.n_layers, "heads": w.n_q_heads if args.gqa else w.n_heads,
+                   "batch": batch, "cached_tokens": w.seq_len,
+                   **({"kv_heads": w.n_kv_heads, "d_head": w.d_head} if args.gqa else {"r": w.r, "d_rope": w.d_rope}),
                    "anchors": anchors if args.hetero else anchors[0],
                    "bits_per_token": bits_tok if args.hetero else bits_tok[0],
                    "q_dtype": str(w.q_dtype).replace("torch.", ""),
                    "split_tokens": args.split_tokens or "auto", "parallelism": "none (one GPU)",
-                   "step": ("latent epilogue (W_UV per head, W_O; d_v 128, d_model 5120)" if args.epilogue else
+                   "step": ("grouped-query decode (precision + depth)" if args.gqa else
+                            "latent epilogue (W_UV per head, W_O; d_v 128, d_model 5120)" if args.epilogue else
                             "append + decode" if args.append else
                             "heterogeneous decode (4 tables x 8 sequences)" if args.hetero else "decode")},
         "roofline": {"bound": "hbm", "kernel": "epilogue: gemm_kernel (W_UV) + gemm_kernel (W_O)" if args.epilogue else

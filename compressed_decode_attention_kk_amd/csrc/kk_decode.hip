@@ -306,7 +306,9 @@ __device__ inline h4 cvt_i16x4(u2 w) {
 // one barrier per stage (P.V first, so that after its rescale branch the two
 // halves form one region the compiler can interleave); P', the rescale factors
 // and the flags are double buffered by tile parity.
-template <int BITS, int RB>
+// GQA: grouped-query rows [V || K] (values first; Q.K skips the value
+// chunks, the first half of the row) and sequence s reading seq_lens[s / n_kv].
+template <int BITS, int RB, bool GQA>
 __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char* lds) {
   constexpr int TB = tile_blocks<BITS>();
   constexpr int TILE = 16 * TB;
@@ -329,7 +331,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   const int nrows = min(E.chunk_rows, E.row_end - r0);
 
   // token range of this split
-  int len = A.seq_lens[E.seq_base + s];
+  int len = A.seq_lens[GQA ? (E.seq_base + s) / A.seq_div : E.seq_base + s];
   len = len < 0 ? 0 : (len > A.t_cap ? A.t_cap : len);
   const int tps = ((len + E.splits - 1) / E.splits + kTile - 1) / kTile * kTile;
   const int t0 = ksplit * tps;
@@ -441,7 +443,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
 #pragma unroll
       for (int c = 0; c < kMaxChunks64; ++c) {
         const int f0 = 64 * c + 16 * g;
-        ok[c] = row_ok && f0 < K;
+        ok[c] = row_ok && f0 < K && (!GQA || c >= E.qk_c0);   // grouped-query: value chunks hold no keys
         lat[c] = !ok[c] || f0 < d;
         off[c] = !ok[c] ? 0 : f0 < d ? qrow * A.r + f0 : qrow * A.d_rope + (f0 - d);
       }
@@ -662,8 +664,8 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           // The chunk count is a compile-time constant in each case below, so every
           // LDS read of the tile is straight-line code the scheduler can hoist
           // ahead of the MFMAs that consume it.
-          auto qk_chunks = [&](auto nc) {
-            constexpr int NC = decltype(nc)::value;
+          auto qk_chunks = [&](auto c0, auto nc) {
+            constexpr int C0 = decltype(c0)::value, NC = decltype(nc)::value;
             // the scales are read with the codes, not after the MFMAs
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) scv[tb] = *(const f4*)(sc + 16 * tb + 4 * g);
@@ -673,7 +675,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
 #pragma unroll
               for (int k = 0; k < NACC; ++k) acc[tb][k] = i4{0, 0, 0, 0};
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
+            for (int c = C0; c < NC; ++c) {
               const int fbyte = (64 * c + 16 * g) * BITS / 8;   // first byte of this lane's 16 features
 #pragma unroll
               for (int tb = 0; tb < TB; ++tb) {
@@ -712,16 +714,24 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
                   sqv[tb][j] = (float)(128 * acc[tb][0][j] + acc[tb][1][j]);
               }
           };
-          switch (KC) {
-            case 1: qk_chunks(std::integral_constant<int, 1>{}); break;
-            case 2: qk_chunks(std::integral_constant<int, 2>{}); break;
-            case 3: qk_chunks(std::integral_constant<int, 3>{}); break;
-            case 4: qk_chunks(std::integral_constant<int, 4>{}); break;
-            case 5: qk_chunks(std::integral_constant<int, 5>{}); break;
-            case 6: qk_chunks(std::integral_constant<int, 6>{}); break;
-            case 7: qk_chunks(std::integral_constant<int, 7>{}); break;
-            case 8: qk_chunks(std::integral_constant<int, 8>{}); break;
-            default: qk_chunks(std::integral_constant<int, kMaxChunks64>{}); break;
+          using Z = std::integral_constant<int, 0>;
+          if constexpr (GQA) {
+            if (KC == 2)                      // d_h = 64: [V 64 || K 64]
+              qk_chunks(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
+            else                              // d_h = 128: [V 128 || K 128]
+              qk_chunks(std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{});
+          } else {
+            switch (KC) {
+              case 1: qk_chunks(Z{}, std::integral_constant<int, 1>{}); break;
+              case 2: qk_chunks(Z{}, std::integral_constant<int, 2>{}); break;
+              case 3: qk_chunks(Z{}, std::integral_constant<int, 3>{}); break;
+              case 4: qk_chunks(Z{}, std::integral_constant<int, 4>{}); break;
+              case 5: qk_chunks(Z{}, std::integral_constant<int, 5>{}); break;
+              case 6: qk_chunks(Z{}, std::integral_constant<int, 6>{}); break;
+              case 7: qk_chunks(Z{}, std::integral_constant<int, 7>{}); break;
+              case 8: qk_chunks(Z{}, std::integral_constant<int, 8>{}); break;
+              default: qk_chunks(Z{}, std::integral_constant<int, kMaxChunks64>{}); break;
+            }
           }
 
           // ---- online softmax for these rows ----
@@ -905,7 +915,7 @@ __device__ inline KArgs& kernel_args() {
 // One launch covers the items of every bit width, interleaved by the host so
 // that each CU runs a mix of bandwidth-bound (wide codes) and arithmetic-bound
 // (narrow codes) items; the bit width is uniform per workgroup.
-template <int RB>
+template <int RB, bool GQA>
 __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   KArgs& A = kernel_args();
@@ -929,10 +939,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs) {
   }
   const int s = j / E.splits, ks = j - s * E.splits;
   switch (E.bits) {
-    case 2: run_item<2, RB>(A, E, s, ks, chunk, lds); break;
-    case 4: run_item<4, RB>(A, E, s, ks, chunk, lds); break;
-    case 8: run_item<8, RB>(A, E, s, ks, chunk, lds); break;
-    default: run_item<16, RB>(A, E, s, ks, chunk, lds); break;
+    case 2: run_item<2, RB, GQA>(A, E, s, ks, chunk, lds); break;
+    case 4: run_item<4, RB, GQA>(A, E, s, ks, chunk, lds); break;
+    case 8: run_item<8, RB, GQA>(A, E, s, ks, chunk, lds); break;
+    default: run_item<16, RB, GQA>(A, E, s, ks, chunk, lds); break;
   }
 }
 
@@ -1031,11 +1041,12 @@ __global__ void __launch_bounds__(256) store_kernel(StoreArgs) {
   for (int i = threadIdx.x; i < a.n; i += 256) a.dst[i] = a.w[i];
 }
 
-template <int RB>
+template <int RB, bool GQA>
 hipError_t launch_one(const DecodeArgs& a, int n, int lds, hipStream_t stream) {
-  hipError_t e = hipFuncSetAttribute((const void*)decode_kernel<RB>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  hipError_t e =
+      hipFuncSetAttribute((const void*)decode_kernel<RB, GQA>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_kernel<RB>), dim3(n), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((decode_kernel<RB, GQA>), dim3(n), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -1058,11 +1069,17 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t
   static_assert(sizeof(DecodeArgs) < 7600, "kernel argument block too large");
   if (L.items > 0) {
     hipError_t e;
-    switch (L.row_blocks) {
-      case 1: e = launch_one<1>(a, L.items, L.lds_bytes, stream); break;
-      case 2: e = launch_one<2>(a, L.items, L.lds_bytes, stream); break;
-      case 3: e = launch_one<3>(a, L.items, L.lds_bytes, stream); break;
-      default: e = launch_one<4>(a, L.items, L.lds_bytes, stream); break;
+    if (L.grouped) {                  // grouped-query rows: <= 32 per KV head, <= 2 row blocks
+      if (L.row_blocks > 2) return hipErrorInvalidValue;
+      e = L.row_blocks == 1 ? launch_one<1, true>(a, L.items, L.lds_bytes, stream)
+                            : launch_one<2, true>(a, L.items, L.lds_bytes, stream);
+    } else {
+      switch (L.row_blocks) {
+        case 1: e = launch_one<1, false>(a, L.items, L.lds_bytes, stream); break;
+        case 2: e = launch_one<2, false>(a, L.items, L.lds_bytes, stream); break;
+        case 3: e = launch_one<3, false>(a, L.items, L.lds_bytes, stream); break;
+        default: e = launch_one<4, false>(a, L.items, L.lds_bytes, stream); break;
+      }
     }
     if (e != hipSuccess) return e;
   }

@@ -59,6 +59,7 @@ struct TableRef {
   int n_seq, seq_base;      // sequences [seq_base, seq_base + n_seq) of the batch
   int layer_base;           // first slot of the table's layers in the layer array
   int64_t out_base;         // float offset of the table's output block
+  int qk_c0 = 0;            // first Q.K chunk of a row (grouped-query rows skip their values)
 };
 
 struct Plan {
@@ -139,6 +140,7 @@ kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_to
         E.e.layer_base = T.layer_base;
         E.e.seq_base = T.seq_base;
         E.e.n_seq = T.n_seq;
+        E.e.qk_c0 = (int8_t)T.qk_c0;
         E.anchor = a;
         E.table = (int)ti;
         E.cost_tile = tile_cost(E.e.bits, E.e.d);
@@ -233,7 +235,7 @@ kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_to
       ws += (int64_t)e.nrc * e.n_seq * e.splits * kk::partial_slot_floats(e.d);
       merges += (int64_t)e.nrc * e.n_seq;
     }
-    e.nbuf = (int16_t)kk::decode_nbuf(e.row_stride, e.d + c0->d_rope, e.bits, RB);
+    e.nbuf = (int8_t)kk::decode_nbuf(e.row_stride, e.d + c0->d_rope, e.bits, RB);
     Lc.lds_bytes = std::max(Lc.lds_bytes, kk::decode_lds_bytes(e.row_stride, e.d + c0->d_rope, e.bits, RB));
     if (Lc.lds_bytes > 160 * 1024 / kk::decode_wg_per_cu(0)) return KK_ERR_UNSUPPORTED;
     P.ents[i] = e;
@@ -391,6 +393,7 @@ kk_status prepare_decode(const kk_model_cfg* cfg, const kk_cache* caches, int32_
   A.d_rope = cfg->d_rope;
   A.t_cap = t_cap;
   A.q_is_f32 = q_dtype == KK_DTYPE_F32;
+  A.seq_div = 1;
   return KK_OK;
 }
 }  // namespace
@@ -528,6 +531,7 @@ kk_status kk_multi_decode_attn(const kk_table_batch* tables, int32_t n_tables, i
   A.d_rope = tabs[0].cfg->d_rope;
   A.t_cap = t_cap;
   A.q_is_f32 = q_dtype == KK_DTYPE_F32;
+  A.seq_div = 1;
   if (A.n_entries == 0 || P.launch.items == 0) return KK_OK;
   if (kk::launch_store(reinterpret_cast<uint32_t*>(ws + m.plan_off), img.data(), (int64_t)img.size(), stream) !=
       hipSuccess)
@@ -582,6 +586,156 @@ kk_status kk_append_decode(const kk_model_cfg* cfg, const kk_cache* caches, int3
   }
   if (kk::launch_append(a, stream) != hipSuccess) return KK_ERR_DEVICE;
   return kk::launch_decode(P.args, P.launch, stream) == hipSuccess ? KK_OK : KK_ERR_DEVICE;
+}
+
+namespace {
+// Grouped-query tables run on the latent decode path: each (sequence, KV
+// head) is one sequence of rows [V_g || K_g] (values = the first d_h fields,
+// keys = the d_h fields after them, which alone enter Q.K), and its G = H /
+// n_kv query heads are the rows of an item.
+struct GqaModel {
+  std::vector<kk_layer_cfg> layers;
+  kk_model_cfg cfg;
+};
+kk_status gqa_model(const kk_gqa_cfg* c, GqaModel& m) {
+  if (!c || !c->layers) return KK_ERR_INVALID_ARGUMENT;
+  if (c->n_layers < 1 || c->n_q_heads < 1 || c->n_kv_heads < 1 || c->d_head < 1) return KK_ERR_INVALID_ARGUMENT;
+  if (c->n_q_heads % c->n_kv_heads) return KK_ERR_INVALID_ARGUMENT;
+  if (c->d_head != 64 && c->d_head != 128) return KK_ERR_UNSUPPORTED;
+  if (c->n_q_heads / c->n_kv_heads > 32) return KK_ERR_UNSUPPORTED;   // query rows of one KV head: <= 2 row blocks
+  if (c->n_layers > KK_MAX_LAYERS) return KK_ERR_UNSUPPORTED;
+  m.layers.resize(c->n_layers);
+  for (int l = 0; l < c->n_layers; ++l) {
+    m.layers[l] = c->layers[l];
+    if (c->layers[l].anchor == l) m.layers[l].d = c->d_head;   // the cache keeps every key and value coordinate
+  }
+  m.cfg.n_layers = c->n_layers;
+  m.cfg.n_heads = c->n_q_heads / c->n_kv_heads;
+  m.cfg.r = c->d_head;
+  m.cfg.d_rope = c->d_head;
+  m.cfg.layers = m.layers.data();
+  return check_model(&m.cfg);
+}
+}  // namespace
+
+kk_status kk_gqa_cache_bytes(const kk_gqa_cfg* cfg, int32_t layer, int32_t batch, int32_t t_cap, size_t* codes_bytes,
+                             size_t* scales_bytes) {
+  GqaModel m;
+  const kk_status st = gqa_model(cfg, m);
+  if (st != KK_OK) return st;
+  if (layer < 0 || layer >= cfg->n_layers || cfg->layers[layer].anchor != layer) return KK_ERR_INVALID_ARGUMENT;
+  if (batch < 1 || t_cap < 1 || !codes_bytes || !scales_bytes) return KK_ERR_INVALID_ARGUMENT;
+  const size_t rows = (size_t)batch * cfg->n_kv_heads * (size_t)t_cap;
+  *codes_bytes = rows * stride_of(cfg->d_head, cfg->d_head, cfg->layers[layer].bits);
+  *scales_bytes = rows * sizeof(float);
+  return KK_OK;
+}
+
+kk_status kk_gqa_quantize_write(const kk_gqa_cfg* cfg, int32_t layer, const void* k, const void* v, kk_dtype src_dtype,
+                                int64_t n_src, int32_t n_tokens, const int32_t* src_index, const int64_t* dst_slot,
+                                kk_cache dst, int32_t batch, int32_t t_cap, hipStream_t stream) {
+  GqaModel m;
+  const kk_status st = gqa_model(cfg, m);
+  if (st != KK_OK) return st;
+  if (layer < 0 || layer >= cfg->n_layers || cfg->layers[layer].anchor != layer) return KK_ERR_INVALID_ARGUMENT;
+  if (src_dtype != KK_DTYPE_F32 && src_dtype != KK_DTYPE_BF16) return KK_ERR_INVALID_ARGUMENT;
+  if (n_tokens < 0 || n_src < 0 || batch < 1 || t_cap < 1) return KK_ERR_INVALID_ARGUMENT;
+  if (n_tokens == 0) return KK_OK;
+  const size_t ea = src_dtype == KK_DTYPE_F32 ? 4 : 2;
+  if (!k || !v || !dst_slot || !dst.codes || !dst.scales) return KK_ERR_INVALID_ARGUMENT;
+  if (!aligned(k, ea) || !aligned(v, ea) || !aligned(dst_slot, 8) || (src_index && !aligned(src_index, 4)))
+    return KK_ERR_INVALID_ARGUMENT;
+  if (!aligned(dst.codes, 16) || !aligned(dst.scales, 16)) return KK_ERR_INVALID_ARGUMENT;
+  kk::GqaWriteArgs a;
+  a.k = k;
+  a.v = v;
+  a.src_index = src_index;
+  a.dst_slot = dst_slot;
+  a.codes = dst.codes;
+  a.scales = dst.scales;
+  a.n_src = n_src;
+  a.n_slots = (int64_t)batch * t_cap;
+  a.n_tokens = n_tokens;
+  a.n_kv = cfg->n_kv_heads;
+  a.d_head = cfg->d_head;
+  a.bits = cfg->layers[layer].bits;
+  a.row_stride = (int32_t)stride_of(cfg->d_head, cfg->d_head, a.bits);
+  a.t_cap = t_cap;
+  a.src_bf16 = src_dtype == KK_DTYPE_BF16;
+  return kk::launch_gqa_write(a, stream) == hipSuccess ? KK_OK : KK_ERR_DEVICE;
+}
+
+kk_status kk_gqa_decode_workspace_bytes(const kk_gqa_cfg* cfg, int32_t batch, int32_t max_seq_len,
+                                        int32_t split_tokens, size_t* bytes) {
+  GqaModel m;
+  kk_status st = gqa_model(cfg, m);
+  if (st != KK_OK) return st;
+  if (batch < 1 || max_seq_len < 0 || split_tokens < 0 || split_tokens % kk::kTile || !bytes)
+    return KK_ERR_INVALID_ARGUMENT;
+  if ((int64_t)batch * cfg->n_kv_heads > 0x7fffffff) return KK_ERR_UNSUPPORTED;
+  Plan P;
+  std::vector<TableRef> tabs{TableRef{&m.cfg, nullptr, batch * cfg->n_kv_heads, 0, 0, 0, cfg->d_head / 64}};
+  st = make_plan(tabs, max_seq_len, split_tokens, P);
+  if (st != KK_OK) return st;
+  if (P.ents.size() > (size_t)kk::kMaxEntries) return KK_ERR_UNSUPPORTED;
+  *bytes = (size_t)P.ws_floats * sizeof(float);
+  return KK_OK;
+}
+
+kk_status kk_gqa_decode_attn(const kk_gqa_cfg* cfg, const kk_cache* caches, int32_t batch, int32_t t_cap,
+                             const int32_t* seq_lens, int32_t max_seq_len, const void* q, kk_dtype q_dtype, float* out,
+                             int32_t split_tokens, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  GqaModel m;
+  kk_status st = gqa_model(cfg, m);
+  if (st != KK_OK) return st;
+  if (!caches || batch < 1 || t_cap < 1 || max_seq_len < 0 || max_seq_len > t_cap) return KK_ERR_INVALID_ARGUMENT;
+  if (split_tokens < 0 || split_tokens % kk::kTile) return KK_ERR_INVALID_ARGUMENT;
+  if (q_dtype != KK_DTYPE_F32 && q_dtype != KK_DTYPE_BF16) return KK_ERR_INVALID_ARGUMENT;
+  if (!seq_lens || !q || !out || !aligned(seq_lens, 4) || !aligned(q, 16) || !aligned(out, 16))
+    return KK_ERR_INVALID_ARGUMENT;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    if (cfg->layers[l].anchor != l) continue;
+    if (!caches[l].codes || !caches[l].scales) return KK_ERR_INVALID_ARGUMENT;
+    if (!aligned(caches[l].codes, 16) || !aligned(caches[l].scales, 16)) return KK_ERR_INVALID_ARGUMENT;
+  }
+  const int64_t nseq = (int64_t)batch * cfg->n_kv_heads;
+  if (nseq > 0x7fffffff || (int64_t)cfg->n_layers * batch * cfg->n_q_heads > ((int64_t)1 << 31))
+    return KK_ERR_UNSUPPORTED;
+  Plan P;
+  std::vector<TableRef> tabs{TableRef{&m.cfg, caches, (int)nseq, 0, 0, 0, cfg->d_head / 64}};
+  st = make_plan(tabs, max_seq_len, split_tokens, P);
+  if (st != KK_OK) return st;
+  if (P.ents.size() > (size_t)kk::kMaxEntries) return KK_ERR_UNSUPPORTED;
+  const size_t need = (size_t)P.ws_floats * sizeof(float);
+  if (need > 0) {
+    if (!workspace || !aligned(workspace, 256)) return KK_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < need) return KK_ERR_WORKSPACE_TOO_SMALL;
+  }
+  kk::DecodeArgs& A = P.args;
+  std::memset(&A, 0, sizeof(A));
+  for (size_t i = 0; i < P.group_layers.size(); ++i) A.group_layers[i] = P.group_layers[i];
+  for (size_t i = 0; i < P.layers.size(); ++i) A.layers[i] = P.layers[i];
+  for (size_t i = 0; i < P.ents.size(); ++i) {
+    A.entries[i] = P.ents[i];
+    A.entries[i].codes = caches[P.entry_anchor[i]].codes;
+    A.entries[i].scales = caches[P.entry_anchor[i]].scales;
+  }
+  A.n_entries = (int32_t)P.ents.size();
+  A.total_items = P.launch.items;
+  A.q_lat = q;                 // the value chunks are skipped: never read as queries
+  A.q_rope = q;                // [L][B][n_kv * G][d_h] = [L][B * n_kv][G][d_h]
+  A.out = out;                 // [L][B * n_kv][G][d_h] = [L][B][H][d_h]
+  A.ws = static_cast<float*>(workspace);
+  A.seq_lens = seq_lens;
+  A.batch = (int32_t)nseq;
+  A.heads = m.cfg.n_heads;
+  A.r = m.cfg.r;
+  A.d_rope = m.cfg.d_rope;
+  A.t_cap = t_cap;
+  A.q_is_f32 = q_dtype == KK_DTYPE_F32;
+  A.seq_div = cfg->n_kv_heads;
+  P.launch.grouped = true;
+  return kk::launch_decode(A, P.launch, stream) == hipSuccess ? KK_OK : KK_ERR_DEVICE;
 }
 
 kk_status kk_latent_epilogue(const kk_model_cfg* cfg, int32_t batch, int32_t d_v, int32_t d_model,

@@ -51,7 +51,10 @@ struct EntryArg {
   int16_t d, bits;
   int16_t nrc, chunk_rows;
   int16_t splits;
-  int16_t nbuf;          // LDS tile buffers of this entry (nbuf - 1 tiles in flight)
+  int8_t nbuf;           // LDS tile buffers of this entry (nbuf - 1 tiles in flight)
+  int8_t qk_c0;          // first 64-field chunk of the row that enters Q.K (the
+                         // fields before it are values only: grouped-query rows
+                         // [V || K]); 0 for latent rows
 };
 
 // The entry, layer and group-layer arrays sit in the launch arguments for one
@@ -72,6 +75,7 @@ struct DecodeArgs {
   int32_t batch, heads, r, d_rope, t_cap;
   int32_t n_entries, total_items;
   int32_t q_is_f32;
+  int32_t seq_div;                    // sequence s reads seq_lens[s / seq_div] (grouped-query: n_kv)
   uint16_t group_layers[kMaxLayers];  // layers ordered by group
   LayerArg layers[kMaxLayers];
   EntryArg entries[kMaxEntries];
@@ -97,6 +101,20 @@ struct WriteArgs {
 };
 
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream);
+
+// Grouped-query writer: one scale per token over its K and V of every KV
+// head; row (seq * n_kv + g) * t_cap + pos holds [V_g || K_g].
+struct GqaWriteArgs {
+  const void* k;             // [n_src][n_kv][d_h]
+  const void* v;
+  const int32_t* src_index;
+  const int64_t* dst_slot;   // seq * t_cap + pos
+  uint8_t* codes;
+  float* scales;
+  int64_t n_src, n_slots;
+  int32_t n_tokens, n_kv, d_head, bits, row_stride, t_cap, src_bf16;
+};
+hipError_t launch_gqa_write(const GqaWriteArgs& a, hipStream_t stream);
 
 // Append of one token per sequence to every anchor cache (see kk_append_decode).
 struct AppendAnchor {
@@ -143,6 +161,7 @@ struct DecodeLaunch {
   int lds_bytes;         // dynamic LDS per workgroup: the largest entry's need
   int row_blocks;        // 16-row MFMA blocks per item (1..4), uniform for the step
   int merge_blocks;
+  bool grouped = false;  // grouped-query rows [V || K] (row_blocks <= 2)
 };
 
 int decode_nbuf(int row_stride, int K, int bits, int row_blocks);

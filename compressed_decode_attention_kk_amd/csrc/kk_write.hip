@@ -29,10 +29,13 @@ __device__ inline float load_src(const void* p, int64_t idx, int bf16) {
 
 // Quantizes one token (the wave's 64 lanes) from its source rows and packs it
 // into `row` with its scale at *scale_out.  The source rows hold the latent
-// (first d used) and the RoPE key (d_rope), fp32 or bf16.
+// (first d used) and the RoPE key (d_rope), fp32 or bf16.  amax_in >= 0 gives
+// the absmax the scale is taken from (a token whose scale covers more than
+// this row); otherwise it is the row's own.
 template <int BITS>
 __device__ inline void quantize_token(const void* lat_row, const void* rope_row, int bf16, int d, int d_rope,
-                                      int row_stride, uint8_t* row, float* scale_out, int lane) {
+                                      int row_stride, uint8_t* row, float* scale_out, int lane,
+                                      float amax_in = -1.0f) {
   constexpr int kFields = 32 / BITS;              // fields per 32-bit word
   constexpr int kMaxWords = (640 * BITS / 32 + 63) / 64;   // words per lane (K <= 640)
   const int K = d + d_rope;
@@ -53,6 +56,7 @@ __device__ inline void quantize_token(const void* lat_row, const void* rope_row,
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if (amax_in >= 0.0f) amax = amax_in;
 
   const float qmax = (float)((1 << (BITS - 1)) - 1);
   const float scale = __fdiv_rn(amax, qmax);
@@ -123,7 +127,48 @@ __global__ void __launch_bounds__(256) append_kernel(AppendArgs a) {
   }
 }
 
+// Grouped-query write: one wave per token.  The absmax runs over the token's
+// K and V of every KV head (one scale per token), then each KV head's row
+// [V_g || K_g] is packed like a latent row with values first.
+template <int BITS>
+__global__ void __launch_bounds__(256) gqa_write_kernel(GqaWriteArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= a.n_tokens) return;
+  const int64_t src = a.src_index ? (int64_t)a.src_index[tok] : tok;
+  const int64_t slot = a.dst_slot[tok];
+  if (src < 0 || src >= a.n_src || slot < 0 || slot >= a.n_slots) return;
+  const int64_t per = (int64_t)a.n_kv * a.d_head;
+  const int64_t base = src * per;
+  float amax = 0.0f;
+  for (int64_t j = lane; j < per; j += 64)
+    amax = fmaxf(amax, fmaxf(fabsf(load_src(a.k, base + j, a.src_bf16)), fabsf(load_src(a.v, base + j, a.src_bf16))));
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const int64_t seq = slot / a.t_cap, pos = slot - seq * a.t_cap;
+  const size_t es = a.src_bf16 ? 2 : 4;
+  for (int g = 0; g < a.n_kv; ++g) {
+    const int64_t r = (seq * a.n_kv + g) * a.t_cap + pos;
+    const int64_t so = (base + (int64_t)g * a.d_head) * es;
+    quantize_token<BITS>((const char*)a.v + so, (const char*)a.k + so, a.src_bf16, a.d_head, a.d_head, a.row_stride,
+                         a.codes + r * a.row_stride, a.scales + r, lane, amax);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_gqa_write(const GqaWriteArgs& a, hipStream_t stream) {
+  if (a.n_tokens <= 0) return hipSuccess;
+  dim3 grid((unsigned)((a.n_tokens + 3) / 4)), block(256);
+  switch (a.bits) {
+    case 2: hipLaunchKernelGGL(gqa_write_kernel<2>, grid, block, 0, stream, a); break;
+    case 4: hipLaunchKernelGGL(gqa_write_kernel<4>, grid, block, 0, stream, a); break;
+    case 8: hipLaunchKernelGGL(gqa_write_kernel<8>, grid, block, 0, stream, a); break;
+    case 16: hipLaunchKernelGGL(gqa_write_kernel<16>, grid, block, 0, stream, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_write(const WriteArgs& a, hipStream_t stream) {
   if (a.n_tokens <= 0) return hipSuccess;

@@ -41,6 +41,11 @@ class Cache(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
+class GqaCfg(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("d_head", ctypes.c_int32), ("layers", ctypes.POINTER(LayerCfg))]
+
+
 class TableBatch(ctypes.Structure):
     _fields_ = [("cfg", ctypes.POINTER(ModelCfg)), ("batch", ctypes.c_int32), ("caches", ctypes.POINTER(Cache))]
 
@@ -87,11 +92,24 @@ def lib():
                                          ctypes.c_void_p, ctypes.POINTER(ctypes.c_void_p),
                                          ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_void_p,
                                          ctypes.c_void_p]
+        L.kk_gqa_cache_bytes.argtypes = [ctypes.POINTER(GqaCfg), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+        L.kk_gqa_quantize_write.argtypes = [ctypes.POINTER(GqaCfg), ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                            ctypes.c_void_p, Cache, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+        L.kk_gqa_decode_workspace_bytes.argtypes = [ctypes.POINTER(GqaCfg), ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.kk_gqa_decode_attn.argtypes = [ctypes.POINTER(GqaCfg), ctypes.POINTER(Cache), ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int,
+                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
+                                         ctypes.c_void_p]
         L.kk_status_string.restype = ctypes.c_char_p
         L.kk_status_string.argtypes = [ctypes.c_int]
         for name in ("kk_validate_model", "kk_cache_bytes", "kk_out_offsets", "kk_quantize_write",
                      "kk_decode_workspace_bytes", "kk_decode_attn", "kk_append_decode", "kk_multi_out_offsets",
-                     "kk_multi_decode_workspace_bytes", "kk_multi_decode_attn", "kk_latent_epilogue"):
+                     "kk_multi_decode_workspace_bytes", "kk_multi_decode_attn", "kk_latent_epilogue",
+                     "kk_gqa_cache_bytes", "kk_gqa_quantize_write", "kk_gqa_decode_workspace_bytes",
+                     "kk_gqa_decode_attn"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -352,3 +370,82 @@ def latent_epilogue(model: Model, batch: int, o_lat: torch.Tensor, w_uv, w_o, v:
                                   _stream(stream))
     _check(st, "kk_latent_epilogue")
     return v, y
+
+
+class GqaModel:
+    """Per-layer table of a grouped-query model (a kk_gqa_cfg): precision and
+    depth; each anchor caches all d_head key and value coordinates."""
+
+    def __init__(self, layers, n_q_heads: int, n_kv_heads: int, d_head: int):
+        self.layers = [LayerSpec(int(l.anchor), int(l.d), int(l.bits), float(l.sm_scale)) for l in layers]
+        self.n_layers, self.n_q_heads, self.n_kv_heads, self.d_head = (len(self.layers), int(n_q_heads),
+                                                                        int(n_kv_heads), int(d_head))
+        self._arr = (LayerCfg * self.n_layers)(*[LayerCfg(l.anchor, l.d, l.bits, l.sm_scale) for l in self.layers])
+        self._cfg = GqaCfg(self.n_layers, self.n_q_heads, self.n_kv_heads, self.d_head, self._arr)
+
+    @property
+    def cfg(self):
+        return ctypes.byref(self._cfg)
+
+    def anchors(self):
+        return [l for l, s in enumerate(self.layers) if s.anchor == l]
+
+
+def gqa_alloc_cache(model: GqaModel, layer: int, batch: int, t_cap: int, device="cuda"):
+    """(codes uint8 [B, n_kv, T_cap, stride], scales f32 [B, n_kv, T_cap]) of one anchor."""
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().kk_gqa_cache_bytes(model.cfg, layer, batch, t_cap, ctypes.byref(cb), ctypes.byref(sb)),
+           "kk_gqa_cache_bytes")
+    rows = batch * model.n_kv_heads * t_cap
+    codes = torch.empty((batch, model.n_kv_heads, t_cap, cb.value // rows), dtype=torch.uint8, device=device)
+    scales = torch.empty((batch, model.n_kv_heads, t_cap), dtype=torch.float32, device=device)
+    return codes, scales
+
+
+def gqa_quantize_write(model: GqaModel, layer: int, k: torch.Tensor, v: torch.Tensor, codes: torch.Tensor,
+                       scales: torch.Tensor, dst_slot: torch.Tensor, src_index: torch.Tensor | None = None,
+                       stream=None):
+    """Quantize K and V source rows [n_src, n_kv, d_head] into anchor `layer` at
+    slots dst_slot (seq * t_cap + position, int64)."""
+    assert k.shape == v.shape and k.dtype == v.dtype and k.is_contiguous() and v.is_contiguous()
+    assert tuple(k.shape[1:]) == (model.n_kv_heads, model.d_head)
+    assert dst_slot.dtype == torch.int64 and dst_slot.is_contiguous()
+    if src_index is not None:
+        assert src_index.dtype == torch.int32 and src_index.is_contiguous() and src_index.numel() == dst_slot.numel()
+    batch, _, t_cap = scales.shape
+    st = lib().kk_gqa_quantize_write(model.cfg, layer, _ptr(k), _ptr(v), _dtype_code(k.dtype), k.shape[0],
+                                     dst_slot.numel(), _ptr(src_index), _ptr(dst_slot),
+                                     Cache(codes.data_ptr(), scales.data_ptr()), batch, t_cap, _stream(stream))
+    _check(st, "kk_gqa_quantize_write")
+
+
+class GqaDecoder:
+    """kk_gqa_decode_attn for repeated steps: out [n_layers, batch, n_q_heads, d_head]."""
+
+    def __init__(self, model: GqaModel, caches: dict, batch: int, t_cap: int, max_seq_len: int,
+                 split_tokens: int = 0, device="cuda"):
+        self.model, self.batch, self.t_cap, self.max_seq_len = model, batch, t_cap, max_seq_len
+        self.split_tokens = split_tokens
+        self.caches = caches
+        self._ctab = (Cache * model.n_layers)()
+        for l in model.anchors():
+            c, s = caches[l]
+            self._ctab[l] = Cache(c.data_ptr(), s.data_ptr())
+        self.out = torch.empty(model.n_layers, batch, model.n_q_heads, model.d_head, dtype=torch.float32,
+                               device=device)
+        wb = ctypes.c_size_t()
+        _check(lib().kk_gqa_decode_workspace_bytes(model.cfg, batch, max_seq_len, split_tokens, ctypes.byref(wb)),
+               "kk_gqa_decode_workspace_bytes")
+        self.ws_bytes = wb.value
+        self.workspace = torch.empty(max(self.ws_bytes, 256) // 4 + 64, dtype=torch.float32, device=device)
+
+    def __call__(self, q: torch.Tensor, seq_lens: torch.Tensor, stream=None):
+        m = self.model
+        assert q.is_contiguous() and tuple(q.shape) == (m.n_layers, self.batch, m.n_q_heads, m.d_head)
+        assert seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.numel() == self.batch
+        wptr = (self.workspace.data_ptr() + 255) // 256 * 256
+        st = lib().kk_gqa_decode_attn(m.cfg, self._ctab, self.batch, self.t_cap, _ptr(seq_lens), self.max_seq_len,
+                                      _ptr(q), _dtype_code(q.dtype), _ptr(self.out), self.split_tokens,
+                                      ctypes.c_void_p(wptr), self.ws_bytes, _stream(stream))
+        _check(st, "kk_gqa_decode_attn")
+        return self.out

@@ -250,6 +250,61 @@ kk_status kk_multi_decode_attn(const kk_table_batch* tables, int32_t n_tables, i
                                float* out, int32_t split_tokens, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* ---- Grouped-query (non-MLA) cache: precision + depth --------------------------
+ * The same per-layer table on a model without a latent: an anchor caches its
+ * keys K and values V per KV head at b bits, later layers may inherit an
+ * anchor's cache; there is no rank axis (KV-Kaizen summary page: the "Precision
+ * (non-MLA)", "Depth (non-MLA)" and "Precision + depth" rows of Table 1, the
+ * KVK 4x row of Table 2; the non-MLA cost C0 = L * 2 * n_kv * d_h * 16 bits of
+ * "Action Space and Cost Model").
+ *
+ * Layout (one anchor): codes uint8 [batch][n_kv][t_cap][row_stride], one row
+ * per (sequence, KV head, token) holding 2 d_h fields, the head's values then
+ * its keys ([V_g || K_g], fields packed as for the latent cache, b = 16 as two
+ * byte planes); row_stride = kk_row_stride_bytes(d_h, d_h, b).  scales float32
+ * [batch][n_kv][t_cap]: one scale per token over its K and V of every KV head
+ * (amax / qmax, as for the latent cache), repeated for each KV head's row.
+ *
+ * Decode, for layer l with anchor a, sequence s, query head h and its KV head
+ * g = h / (n_q_heads / n_kv_heads), over t < len_s:
+ *   z_t = sm_scale_l * q[l,s,h,:] . K_a[s,g,t,:],  out[l,s,h,:] = sum_t softmax(z)_t V_a[s,g,t,:]
+ * (dequantized codes).  Keys are cached after RoPE. */
+typedef struct {
+  int32_t n_layers;             /* 1 .. KK_MAX_LAYERS */
+  int32_t n_q_heads;            /* H, a multiple of n_kv_heads */
+  int32_t n_kv_heads;           /* n_kv */
+  int32_t d_head;               /* d_h: 64 or 128 */
+  const kk_layer_cfg* layers;   /* host [n_layers]: anchor, bits and sm_scale as for
+                                   kk_layer_cfg; d is ignored (every coordinate kept) */
+} kk_gqa_cfg;
+
+/* Bytes of anchor `layer`'s codes and scales for [batch][n_kv][t_cap]. */
+kk_status kk_gqa_cache_bytes(const kk_gqa_cfg* cfg, int32_t layer, int32_t batch, int32_t t_cap,
+                             size_t* codes_bytes, size_t* scales_bytes);
+
+/* Quantize-and-pack write of anchor `layer`: token i reads k and v row
+ * src_index[i] (nullable: identity), each [n_src][n_kv][d_h] contiguous
+ * `src_dtype` (4-byte aligned for f32), and writes position dst_slot[i] =
+ * seq * t_cap + pos of every KV head.  Out-of-range tokens are skipped; two
+ * tokens writing one slot race. */
+kk_status kk_gqa_quantize_write(const kk_gqa_cfg* cfg, int32_t layer, const void* k, const void* v,
+                                kk_dtype src_dtype, int64_t n_src, int32_t n_tokens, const int32_t* src_index,
+                                const int64_t* dst_slot, kk_cache dst, int32_t batch, int32_t t_cap,
+                                hipStream_t stream);
+
+/* Workspace bytes of kk_gqa_decode_attn (0 when no sequence is split). */
+kk_status kk_gqa_decode_workspace_bytes(const kk_gqa_cfg* cfg, int32_t batch, int32_t max_seq_len,
+                                        int32_t split_tokens, size_t* bytes);
+
+/* One decode step of every layer.
+ * q   : device [n_layers][batch][n_q_heads][d_h], q_dtype, 16-byte aligned.
+ * out : device float32 [n_layers][batch][n_q_heads][d_h].
+ * caches, seq_lens, max_seq_len, split_tokens, workspace: as for kk_decode_attn. */
+kk_status kk_gqa_decode_attn(const kk_gqa_cfg* cfg, const kk_cache* caches, int32_t batch, int32_t t_cap,
+                             const int32_t* seq_lens, int32_t max_seq_len, const void* q, kk_dtype q_dtype,
+                             float* out, int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
 /* ---- Latent epilogue ---------------------------------------------------------
  * Absorbed-MLA decode returns each head's output in the latent space (a
  * weighted sum of the cached latents c^KV, truncated to the d_eff kept

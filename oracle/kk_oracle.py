@@ -267,7 +267,7 @@ def gqa_write_cache(k: np.ndarray, v: np.ndarray, bits: int):
     k = np.asarray(k, np.float32)
     v = np.asarray(v, np.float32)
     n, nkv, dh = k.shape
-    codes, scales = quantize_rows(np.concatenate([k.reshape(n, -1), v.reshape(n, -1)], axis=1), bits)
+    codes, scales = quantize_rows(np.concatenate([k.reshape(n, nkv * dh), v.reshape(n, nkv * dh)], axis=1), bits)
     return codes[:, :nkv * dh].reshape(n, nkv, dh), codes[:, nkv * dh:].reshape(n, nkv, dh), scales
 
 
@@ -276,7 +276,8 @@ def gqa_pack_kv_rows(codes_k: np.ndarray, codes_v: np.ndarray, bits: int) -> np.
     2 d_h fields, values first then keys, [N, n_kv, stride] uint8."""
     n, nkv, dh = codes_k.shape
     rows = np.concatenate([codes_v, codes_k], axis=2).reshape(n * nkv, 2 * dh)
-    return pack_rows(rows, bits).reshape(n, nkv, -1)
+    packed = pack_rows(rows, bits)
+    return packed.reshape(n, nkv, packed.shape[1])
 
 
 def gqa_decode_layer(q: np.ndarray, codes_k: np.ndarray, codes_v: np.ndarray, scales: np.ndarray,

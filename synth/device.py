@@ -41,3 +41,23 @@ def build_caches(kk, model, w: gen.Workload, t_cap: int | None = None, device="c
             del lat, rope
         caches[a] = (codes, scales)
     return caches
+
+
+def build_gqa_caches(kk, model, w: gen.GqaWorkload, t_cap: int | None = None, device="cuda", seq_lens=None):
+    """{anchor: (codes, scales)} of a grouped-query workload through the
+    library writer; rows t < seq_lens[s] of sequence s are written."""
+    t_cap = t_cap or w.seq_len
+    lens = [w.seq_len] * w.batch if seq_lens is None else [int(x) for x in seq_lens]
+    caches = {}
+    for a in w.anchors():
+        codes, scales = kk.gqa_alloc_cache(model, a, w.batch, t_cap, device)
+        codes.zero_()
+        scales.zero_()
+        k, v = gen.gqa_source(w, a, device)
+        for s in range(w.batch):
+            n = lens[s]
+            dst = s * t_cap + torch.arange(n, device=device, dtype=torch.int64)
+            kk.gqa_quantize_write(model, a, k[s, :n].contiguous(), v[s, :n].contiguous(), codes, scales, dst)
+        del k, v
+        caches[a] = (codes, scales)
+    return caches

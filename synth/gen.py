@@ -24,7 +24,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-KIND_LATENT, KIND_ROPE, KIND_QLAT, KIND_QROPE, KIND_SCORES, KIND_WUV, KIND_WO = 0, 1, 2, 3, 4, 5, 6
+KIND_LATENT, KIND_ROPE, KIND_QLAT, KIND_QROPE, KIND_SCORES, KIND_WUV, KIND_WO, KIND_K, KIND_V, KIND_Q = range(10)
 
 GOLDEN_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "tests", "golden")
 
@@ -160,6 +160,74 @@ def workload(wid: int) -> Workload:
         return Workload(4, "14b_mixed_4x_evict8", 48, 40, 8, 8192, 512, 64, torch.bfloat16,
                         layers_from_table(mixed_table_14b(), 64), nominal_context=65536)
     raise ValueError(wid)
+
+
+@dataclass
+class GqaWorkload:
+    """A grouped-query (non-MLA) model with a precision + depth table."""
+    wid: int
+    name: str
+    n_layers: int
+    n_q_heads: int
+    n_kv_heads: int
+    d_head: int
+    batch: int
+    seq_len: int
+    q_dtype: torch.dtype
+    layers: list = field(default_factory=list)
+
+    def anchors(self):
+        return [l for l, s in enumerate(self.layers) if s.anchor == l]
+
+    def bits_eff(self, l):
+        return self.layers[self.layers[l].anchor].bits
+
+
+GQA_WID = 9
+
+
+def gqa_layers_from_table(table, d_head):
+    """table rows [anchor, d, bits]; softmax scale 1/sqrt(d_head) for every layer."""
+    sm = 1.0 / math.sqrt(d_head)
+    return [LayerSpec(int(a), int(d_head) if a == l else 0, int(b), sm) for l, (a, _, b) in enumerate(table)]
+
+
+def gqa_table_14b():
+    with open(os.path.join(GOLDEN_DIR, "table_14b_gqa.json")) as f:
+        return json.load(f)["table"]
+
+
+def gqa_workload(batch: int = 16, seq_len: int = 16384) -> GqaWorkload:
+    """Qwen2.5-14B-shaped grouped-query model (48 layers, 40 query heads, 8 KV
+    heads of 128) with the frozen 4x precision + depth table, at the 16k
+    context of the long-context evaluation."""
+    return GqaWorkload(GQA_WID, "14b_gqa_4x", 48, 40, 8, 128, batch, seq_len, torch.bfloat16,
+                       gqa_layers_from_table(gqa_table_14b(), 128))
+
+
+def small_gqa_workload(wid: int, table, n_q_heads: int, n_kv_heads: int, d_head: int, batch: int, seq_len: int,
+                       q_dtype=torch.bfloat16) -> GqaWorkload:
+    return GqaWorkload(wid, "small_gqa", len(table), n_q_heads, n_kv_heads, d_head, batch, seq_len, q_dtype,
+                       gqa_layers_from_table(table, d_head))
+
+
+def gqa_source(w: GqaWorkload, layer: int, device="cpu"):
+    """K and V source rows of one anchor layer, float32 [B, T, n_kv, d_head], both N(0, 1)."""
+    shape = (w.batch, w.seq_len, w.n_kv_heads, w.d_head)
+    g = _gen(device, seed_for(w.wid, layer, KIND_K))
+    k = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    g = _gen(device, seed_for(w.wid, layer, KIND_V))
+    v = torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+    return k, v
+
+
+def gqa_queries(w: GqaWorkload, device="cpu"):
+    """q [L, B, H, d_head] ~ N(0, 1) in the workload's q dtype."""
+    qs = []
+    for l in range(w.n_layers):
+        g = _gen(device, seed_for(w.wid, l, KIND_Q))
+        qs.append(torch.randn(w.batch, w.n_q_heads, w.d_head, generator=g, device=device).to(w.q_dtype))
+    return torch.stack(qs)
 
 
 HETERO_WID = 5   # data seeds of run k of the heterogeneous batch: workload HETERO_WID + k

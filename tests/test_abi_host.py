@@ -35,7 +35,8 @@ def test_header_declares_the_entry_points():
     for n in ("kk_quantize_write", "kk_decode_attn", "kk_decode_workspace_bytes", "kk_cache_bytes",
               "kk_out_offsets", "kk_validate_model", "kk_row_stride_bytes", "kk_status_string",
               "kk_append_decode", "kk_multi_out_offsets", "kk_multi_decode_workspace_bytes",
-              "kk_multi_decode_attn", "kk_latent_epilogue"):
+              "kk_multi_decode_attn", "kk_latent_epilogue", "kk_gqa_cache_bytes", "kk_gqa_quantize_write",
+              "kk_gqa_decode_workspace_bytes", "kk_gqa_decode_attn"):
         assert n in names
 
 
@@ -345,6 +346,73 @@ def test_latent_epilogue_rejects_bad_arguments_before_launch(kk):
     assert call(w=mis) == kk.KK_ERR_INVALID_ARGUMENT
     bad = table([[0, 100, 4]], r=128, dr=32, heads=16, kk=kk)           # d not a multiple of 16
     assert L.kk_latent_epilogue(bad.cfg, 4, 64, 256, fake(1), wu, wo, fake(2), fake(3), None) != kk.KK_OK
+
+
+def gqa(kk, rows, nq=8, nkv=2, dh=128):
+    layers = [kk.LayerSpec(a, d, b, 0.1) for a, d, b in rows]
+    return kk.GqaModel(layers, nq, nkv, dh)
+
+
+def test_gqa_sizes_and_rules(kk):
+    L = kk.lib()
+    m = gqa(kk, [[0, 0, 4], [0, 0, 0], [2, 0, 16]])
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.kk_gqa_cache_bytes(m.cfg, 2, 3, 100, ctypes.byref(cb), ctypes.byref(sb)) == kk.KK_OK
+    assert cb.value == 3 * 2 * 100 * ko.row_stride(256, 16) and sb.value == 3 * 2 * 100 * 4
+    assert L.kk_gqa_cache_bytes(m.cfg, 1, 3, 100, ctypes.byref(cb), ctypes.byref(sb)) == kk.KK_ERR_INVALID_ARGUMENT
+    ws = ctypes.c_size_t()
+    assert L.kk_gqa_decode_workspace_bytes(m.cfg, 3, 1024, 1024, ctypes.byref(ws)) == kk.KK_OK and ws.value == 0
+    assert L.kk_gqa_decode_workspace_bytes(m.cfg, 3, 1024, 64, ctypes.byref(ws)) == kk.KK_OK and ws.value > 0
+    assert status_gqa(kk, gqa(kk, [[0, 0, 4]], nq=6, nkv=4)) == kk.KK_ERR_INVALID_ARGUMENT     # H % n_kv != 0
+    assert status_gqa(kk, gqa(kk, [[0, 0, 4]], dh=96)) == kk.KK_ERR_UNSUPPORTED                # d_h 64 or 128
+    assert status_gqa(kk, gqa(kk, [[0, 0, 4]], nq=66, nkv=1)) == kk.KK_ERR_UNSUPPORTED         # > 32 per KV head
+    assert status_gqa(kk, gqa(kk, [[0, 0, 3]])) == kk.KK_ERR_INVALID_ARGUMENT                  # bits
+    assert status_gqa(kk, gqa(kk, [[1, 0, 0]])) == kk.KK_ERR_INVALID_ARGUMENT                  # layer 0 inherits
+
+
+def status_gqa(kk, m):
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    return kk.lib().kk_gqa_cache_bytes(m.cfg, 0, 1, 16, ctypes.byref(cb), ctypes.byref(sb))
+
+
+def test_gqa_calls_reject_bad_arguments_before_launch(kk):
+    L = kk.lib()
+    m = gqa(kk, [[0, 0, 4], [0, 0, 0], [2, 0, 8]])
+    fake = _Fake()
+    caches = (kk.Cache * 3)()
+    caches[0] = kk.Cache(fake(1).value, fake(2).value)
+    caches[2] = kk.Cache(fake(3).value, fake(4).value)
+    need = ctypes.c_size_t()
+    assert L.kk_gqa_decode_workspace_bytes(m.cfg, 4, 1024, 64, ctypes.byref(need)) == kk.KK_OK
+    need = need.value
+
+    def dec(**kw):
+        a = dict(caches=caches, max_len=1024, q=fake(6), out=fake(8), split=64, ws=fake(9), ws_bytes=need,
+                 q_dtype=kk.KK_DTYPE_BF16)
+        a.update(kw)
+        return L.kk_gqa_decode_attn(m.cfg, a["caches"], 4, 1024, fake(5), a["max_len"], a["q"], a["q_dtype"],
+                                    a["out"], a["split"], a["ws"], a["ws_bytes"], None)
+
+    assert dec(ws_bytes=need - 1) == kk.KK_ERR_WORKSPACE_TOO_SMALL
+    assert dec(ws=fake(9, 32)) == kk.KK_ERR_INVALID_ARGUMENT
+    assert dec(q=fake(6, 8)) == kk.KK_ERR_INVALID_ARGUMENT
+    assert dec(max_len=1025) == kk.KK_ERR_INVALID_ARGUMENT
+    assert dec(split=40) == kk.KK_ERR_INVALID_ARGUMENT
+    assert dec(q_dtype=5) == kk.KK_ERR_INVALID_ARGUMENT
+    bad = (kk.Cache * 3)()
+    bad[0] = caches[0]
+    assert dec(caches=bad) == kk.KK_ERR_INVALID_ARGUMENT
+
+    def wr(layer=0, dtype=kk.KK_DTYPE_F32, k=None, n_tok=4, codes=None):
+        c = kk.Cache(codes if codes is not None else fake(1).value, fake(2).value)
+        return L.kk_gqa_quantize_write(m.cfg, layer, k or fake(10), fake(11), dtype, 4, n_tok, None, fake(12), c, 4,
+                                       1024, None)
+
+    assert wr(layer=1) == kk.KK_ERR_INVALID_ARGUMENT
+    assert wr(dtype=2) == kk.KK_ERR_INVALID_ARGUMENT
+    assert wr(k=fake(10, 2)) == kk.KK_ERR_INVALID_ARGUMENT
+    assert wr(codes=fake(1, 4).value) == kk.KK_ERR_INVALID_ARGUMENT
+    assert wr(n_tok=0) == kk.KK_OK
 
 
 def test_status_strings(kk):
