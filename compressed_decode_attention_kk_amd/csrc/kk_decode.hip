@@ -286,10 +286,15 @@ static_assert(tile_blocks<16>() == 1 && tile_blocks<8>() == 2, "tile_blocks and 
 
 // P.V output units (32 features) per wave.  Q.K waves take a few units; the
 // waves without Q.K rows take the rest, so that no wave idles while Q.K runs.
-template <int RB>
-constexpr int qk_units_max() { return RB >= kWaves ? 4 : 3; }
-template <int RB>
-constexpr int pv_units_max() { return RB == 3 ? 7 : 5; }
+// Grouped-query rows have d = d_h <= 128 (4 units): none on the Q.K waves, at
+// most 2 per other wave.
+template <int RB, bool GQA = false>
+constexpr int qk_units_max() { return GQA ? 1 : RB >= kWaves ? 4 : 3; }
+template <int RB, bool GQA = false>
+constexpr int pv_units_max() { return GQA ? 2 : RB == 3 ? 7 : 5; }
+// 64-field chunks of a row that enter Q.K (grouped-query rows: K = 2 d_h <= 256)
+template <bool GQA>
+constexpr int max_chunks() { return GQA ? 4 : (kMaxK + 63) / 64; }
 
 __device__ inline f4 mfma_f16_k16(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
 
@@ -311,6 +316,7 @@ __device__ inline h4 cvt_i16x4(u2 w) {
 template <int BITS, int RB, bool GQA>
 __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char* lds) {
   constexpr int TB = tile_blocks<BITS>();
+  constexpr int kMaxC = max_chunks<GQA>();
   constexpr int TILE = 16 * TB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, n = lane & 15;
@@ -393,8 +399,8 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
     ucount = max(0, min(per, NU - ubase));
   } else {
     const int npv = kWaves - RB;
-    int uq = max((NU * 3) / 16, (NU - npv * pv_units_max<RB>() + RB - 1) / RB);
-    uq = min(max(uq, 0), qk_units_max<RB>());
+    int uq = max((NU * 3) / 16, (NU - npv * pv_units_max<RB, GQA>() + RB - 1) / RB);
+    uq = min(max(uq, 0), qk_units_max<RB, GQA>());
     const int rest = NU - RB * uq;
     const int per = (rest + npv - 1) / npv;
     if (wave < RB) {
@@ -418,7 +424,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
 
     // ---- q as two int8 limbs of a 14-bit fixed-point number per row ------------------
     // chunk c, lane (g, n): row 16*wave + n, features 64c + 16g + qk_slot_feature(i).
-    i4 qh[QKW ? kMaxChunks64 : 1], ql[QKW ? kMaxChunks64 : 1];
+    i4 qh[QKW ? kMaxC : 1], ql[QKW ? kMaxC : 1];
     float rowf = 1.0f;
     int qbias = 0;
     if constexpr (QKW) {
@@ -429,7 +435,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
         my_head = gr % A.heads;
       }
       int qsum = 0;                               // sum of the fixed-point q of this row
-      float qv[kMaxChunks64][16];
+      float qv[kMaxC][16];
       float mx = 0.0f;
       // The loads of every chunk are issued before any of them is used, so the
       // query costs one memory round trip: a chunk outside the row or past K
@@ -437,41 +443,41 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       const bool row_ok = my_layer >= 0;
       const int64_t qrow =
           row_ok ? ((int64_t)(my_layer - E.layer_base) * A.batch + E.seq_base + s) * A.heads + my_head : 0;
-      bool ok[kMaxChunks64];
-      int64_t off[kMaxChunks64];
-      bool lat[kMaxChunks64];
+      bool ok[kMaxC];
+      int64_t off[kMaxC];
+      bool lat[kMaxC];
 #pragma unroll
-      for (int c = 0; c < kMaxChunks64; ++c) {
+      for (int c = 0; c < kMaxC; ++c) {
         const int f0 = 64 * c + 16 * g;
         ok[c] = row_ok && f0 < K && (!GQA || c >= E.qk_c0);   // grouped-query: value chunks hold no keys
         lat[c] = !ok[c] || f0 < d;
         off[c] = !ok[c] ? 0 : f0 < d ? qrow * A.r + f0 : qrow * A.d_rope + (f0 - d);
       }
-      float x[kMaxChunks64][16];
+      float x[kMaxC][16];
       if (A.q_is_f32) {
-        f4 raw[kMaxChunks64][4];
+        f4 raw[kMaxC][4];
 #pragma unroll
-        for (int c = 0; c < kMaxChunks64; ++c) {
+        for (int c = 0; c < kMaxC; ++c) {
           const f4* p = (const f4*)((const float*)(lat[c] ? A.q_lat : A.q_rope) + off[c]);
 #pragma unroll
           for (int v = 0; v < 4; ++v) raw[c][v] = p[v];
         }
 #pragma unroll
-        for (int c = 0; c < kMaxChunks64; ++c)
+        for (int c = 0; c < kMaxC; ++c)
 #pragma unroll
           for (int v = 0; v < 4; ++v)
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[c][4 * v + i] = raw[c][v][i];
       } else {
-        u4 raw[kMaxChunks64][2];
+        u4 raw[kMaxC][2];
 #pragma unroll
-        for (int c = 0; c < kMaxChunks64; ++c) {
+        for (int c = 0; c < kMaxC; ++c) {
           const u4* p = (const u4*)((const uint16_t*)(lat[c] ? A.q_lat : A.q_rope) + off[c]);
 #pragma unroll
           for (int v = 0; v < 2; ++v) raw[c][v] = p[v];
         }
 #pragma unroll
-        for (int c = 0; c < kMaxChunks64; ++c)
+        for (int c = 0; c < kMaxC; ++c)
 #pragma unroll
           for (int v = 0; v < 2; ++v)
 #pragma unroll
@@ -481,7 +487,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
             }
       }
 #pragma unroll
-      for (int c = 0; c < kMaxChunks64; ++c)
+      for (int c = 0; c < kMaxC; ++c)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float xi = ok[c] ? x[c][qk_slot_feature<BITS>(i)] : 0.0f;
@@ -496,7 +502,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       const float sm = my_layer >= 0 ? layer_at(A, my_layer).sm_scale : 0.0f;
       const float pre = ldexpf(sm < 0.0f ? -1.0f : 1.0f, kQFrac - e);
 #pragma unroll
-      for (int c = 0; c < kMaxChunks64; ++c) {
+      for (int c = 0; c < kMaxC; ++c) {
         uint32_t hw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -730,7 +736,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
               case 6: qk_chunks(Z{}, std::integral_constant<int, 6>{}); break;
               case 7: qk_chunks(Z{}, std::integral_constant<int, 7>{}); break;
               case 8: qk_chunks(Z{}, std::integral_constant<int, 8>{}); break;
-              default: qk_chunks(Z{}, std::integral_constant<int, kMaxChunks64>{}); break;
+              default: qk_chunks(Z{}, std::integral_constant<int, kMaxC>{}); break;
             }
           }
 
@@ -889,9 +895,9 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   };
 
   if (RB >= kWaves || wave < RB)
-    pipeline(std::true_type{}, std::integral_constant<int, qk_units_max<RB>()>{});
+    pipeline(std::true_type{}, std::integral_constant<int, qk_units_max<RB, GQA>()>{});
   else
-    pipeline(std::false_type{}, std::integral_constant<int, pv_units_max<RB>()>{});
+    pipeline(std::false_type{}, std::integral_constant<int, pv_units_max<RB, GQA>()>{});
 }
 
 // Last entry whose first decode block (merge: first merge block) is <= blk;
@@ -916,7 +922,7 @@ __device__ inline KArgs& kernel_args() {
 // that each CU runs a mix of bandwidth-bound (wide codes) and arithmetic-bound
 // (narrow codes) items; the bit width is uniform per workgroup.
 template <int RB, bool GQA>
-__global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeArgs) {
+__global__ void __launch_bounds__(kThreads, GQA ? 4 : 2) decode_kernel(DecodeArgs) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   KArgs& A = kernel_args();
   const int item = blockIdx.x;
@@ -1054,14 +1060,14 @@ hipError_t launch_one(const DecodeArgs& a, int n, int lds, hipStream_t stream) {
 
 // Tile buffers per workgroup: as many as fit in the workgroup's share of the
 // 160 KB LDS, 3 to 12 (two tiles are in use, the rest in flight).
-int decode_nbuf(int row_stride, int K, int bits, int rb) {
-  const int budget = 160 * 1024 / decode_wg_per_cu(bits) - pbuf_bytes(rb, tile_blocks_of(bits)) - kMiscBytes;
+int decode_nbuf(int row_stride, int K, int bits, int rb, bool grouped) {
+  const int budget = 160 * 1024 / decode_wg_per_cu(grouped) - pbuf_bytes(rb, tile_blocks_of(bits)) - kMiscBytes;
   const int n = budget / tilebuf_bytes(row_stride, K, bits);
   return n < 3 ? 3 : (n > 12 ? 12 : n);
 }
 
-int decode_lds_bytes(int row_stride, int K, int bits, int rb) {
-  return decode_nbuf(row_stride, K, bits, rb) * tilebuf_bytes(row_stride, K, bits) +
+int decode_lds_bytes(int row_stride, int K, int bits, int rb, bool grouped) {
+  return decode_nbuf(row_stride, K, bits, rb, grouped) * tilebuf_bytes(row_stride, K, bits) +
          pbuf_bytes(rb, tile_blocks_of(bits)) + kMiscBytes;
 }
 

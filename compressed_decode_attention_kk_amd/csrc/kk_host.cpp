@@ -155,7 +155,8 @@ kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_to
   const int max_tiles = std::max(1, (max_len + kk::kTile - 1) / kk::kTile);
   int64_t total_cost = 0;
   for (auto& E : ents) total_cost += E.cost_tile * max_tiles * E.e.nrc * E.e.n_seq;
-  const int64_t slots = (int64_t)kk::kCUs * kk::decode_wg_per_cu(0);
+  const bool grouped = tabs[0].qk_c0 > 0;
+  const int64_t slots = (int64_t)kk::kCUs * kk::decode_wg_per_cu(grouped);
   auto split_of = [&](const Ent& E, int waves) {
     const int64_t target = std::max<int64_t>(1, total_cost / (waves * slots));
     int64_t sp;
@@ -235,9 +236,9 @@ kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_to
       ws += (int64_t)e.nrc * e.n_seq * e.splits * kk::partial_slot_floats(e.d);
       merges += (int64_t)e.nrc * e.n_seq;
     }
-    e.nbuf = (int8_t)kk::decode_nbuf(e.row_stride, e.d + c0->d_rope, e.bits, RB);
-    Lc.lds_bytes = std::max(Lc.lds_bytes, kk::decode_lds_bytes(e.row_stride, e.d + c0->d_rope, e.bits, RB));
-    if (Lc.lds_bytes > 160 * 1024 / kk::decode_wg_per_cu(0)) return KK_ERR_UNSUPPORTED;
+    e.nbuf = (int8_t)kk::decode_nbuf(e.row_stride, e.d + c0->d_rope, e.bits, RB, grouped);
+    Lc.lds_bytes = std::max(Lc.lds_bytes, kk::decode_lds_bytes(e.row_stride, e.d + c0->d_rope, e.bits, RB, grouped));
+    if (Lc.lds_bytes > 160 * 1024 / kk::decode_wg_per_cu(grouped)) return KK_ERR_UNSUPPORTED;
     P.ents[i] = e;
     P.entry_anchor[i] = ents[i].anchor;
     P.entry_table[i] = ents[i].table;

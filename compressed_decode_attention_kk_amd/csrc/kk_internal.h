@@ -17,9 +17,10 @@ constexpr int kMaxK = 576;           // d + d_R (the ABI limit)
 constexpr int kMaxEntries = 88;      // group entries held in the launch arguments
 constexpr int kMaxLayers = 64;
 constexpr int kCUs = 256;
-// Decode workgroups per CU (the same for every bit width: a second workgroup
-// hides the per-item and per-tile fixed latencies of the first).
-constexpr int decode_wg_per_cu(int) { return 2; }
+// Decode workgroups per CU: two for latent rows (a second workgroup hides the
+// per-item and per-tile fixed latencies of the first); four for the leaner
+// grouped-query instantiation, whose items carry few rows and bytes per stage.
+constexpr int decode_wg_per_cu(bool grouped) { return grouped ? 4 : 2; }
 constexpr float kLazyRescale = 8.0f; // log2 headroom before the running max is moved
 
 // One layer of one table: softmax scale, kept width of its anchor and the
@@ -164,8 +165,8 @@ struct DecodeLaunch {
   bool grouped = false;  // grouped-query rows [V || K] (row_blocks <= 2)
 };
 
-int decode_nbuf(int row_stride, int K, int bits, int row_blocks);
-int decode_lds_bytes(int row_stride, int K, int bits, int row_blocks);
+int decode_nbuf(int row_stride, int K, int bits, int row_blocks, bool grouped);
+int decode_lds_bytes(int row_stride, int K, int bits, int row_blocks, bool grouped);
 hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t stream);
 
 // Copies `words` 32-bit words from host memory to device memory `dst` by
