@@ -27,7 +27,6 @@ It is reported as null when the kernel sources have changed since.
 from __future__ import annotations
 
 import argparse
-import glob
 import hashlib
 import json
 import math
@@ -77,11 +76,16 @@ def useful_flops(w):
                for l in range(w.n_layers))
 
 
+# sources the decode step is built from (its kernels, launch descriptors and planner)
+DECODE_SOURCES = ("kk_decode.hip", "kk_internal.h", "kk_host.cpp")
+
+
 def kernel_source_digest():
     h = hashlib.sha256()
-    for p in sorted(glob.glob(os.path.join(ROOT, "compressed_decode_attention_kk_amd", "csrc", "*"))):
+    for name in DECODE_SOURCES:
+        p = os.path.join(ROOT, "compressed_decode_attention_kk_amd", "csrc", name)
         with open(p, "rb") as f:
-            h.update(os.path.basename(p).encode() + b"\0" + f.read())
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
