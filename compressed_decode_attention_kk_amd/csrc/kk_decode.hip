@@ -413,7 +413,8 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   }
 
   float m_run = -INFINITY, l_lane = 0.0f;     // softmax state of row 16*wave + n (Q.K waves)
-  int Ecur = -1000;                            // scales so far are <= 2^(Ecur + headroom)
+  constexpr int kNoScale = -1000;              // E before an item's first tile
+  int Ecur = kNoScale;                         // scales so far are <= 2^(Ecur + headroom)
 
   // The stage loop of one wave role.  QKW: this wave owns Q.K rows; UMAX: its
   // largest unit count (each role is register-allocated for its own arrays).
@@ -777,7 +778,9 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           }
           smax = max_xor_16_32(smax);
           tmax = max_xor_16_32(tmax) * rowf;
-          const bool raise_e = smax > ldexpf(1.0f, Ecur + kScaleHeadroom);   // wave-uniform
+          // The first tile always sets E (a tile of all-zero tokens, scale 0,
+          // gives E = 0, so that its exponentials stay finite and count in l).
+          const bool raise_e = smax > ldexpf(1.0f, Ecur + kScaleHeadroom) || Ecur == kNoScale;   // wave-uniform
           const bool upd = __any(tmax > m_run + kLazyRescale) || raise_e;    // wave-uniform
           const int par = tq & 1;
           if (upd) {

@@ -262,6 +262,49 @@ def test_outliers_and_zero_tokens(kk):
         check_layer_seq(w, dec, caches, ql, qr, l, 0, 200, src)
 
 
+def test_zero_tokens_at_item_start_and_all_zero_sequences(kk):
+    """Tokens whose stored values are all zero have scale 0 and score 0; they
+    still weigh in the softmax.  Sequence 0 is all zero tokens (the output is
+    0), sequence 1 starts with 40 of them (the first tile of an item is all
+    zero), sequence 2 has them at the end; every bit width, with and without
+    splits."""
+    table = [[0, 128, 2], [1, 128, 4], [2, 128, 8], [3, 128, 16], [3, 0, 0]]
+    w = synth.small_workload(17, 5, 16, 3, 300, 128, 32, table)
+    model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    caches, src = {}, {}
+    for a in w.anchors():
+        lat = torch.randn(3, 300, 128, generator=g, device="cuda")
+        rope = torch.randn(3, 300, 32, generator=g, device="cuda")
+        lat[0] = 0
+        rope[0] = 0
+        lat[1, :40] = 0
+        rope[1, :40] = 0
+        lat[2, 250:] = 0
+        rope[2, 250:] = 0
+        codes, scales = kk.alloc_cache(model, a, 3, 300)
+        for s_ in range(3):
+            kk.quantize_write(model, a, lat[s_].contiguous(), rope[s_].contiguous(), codes, scales,
+                              s_ * 300 + torch.arange(300, device="cuda"))
+        caches[a] = (codes, scales)
+        src[a] = [(lat[s_].cpu().numpy(), rope[s_].cpu().numpy()) for s_ in range(3)]
+    ql, qr = synth.queries(w, "cuda")
+    sl = torch.full((3,), 300, dtype=torch.int32, device="cuda")
+    for st in (0, 64):
+        dec = kk.Decoder(model, caches, 3, 300, 300, split_tokens=st)
+        dec(ql, qr, sl)
+        torch.cuda.synchronize()
+        assert torch.isfinite(dec.out).all(), f"split {st}: non-finite output"
+        for s_ in range(3):
+            for l in range(w.n_layers):
+                a = w.layers[l].anchor
+                if s_ == 0:
+                    assert torch.all(dec.layer_out(l)[0] == 0)
+                    continue
+                check_layer_seq(w, dec, caches, ql, qr, l, s_, 300, {a: src[a][s_]})
+
+
 def test_b16_full_rank_matches_unquantized_attention(kk):
     table = [[0, 256, 16]]
     w = synth.small_workload(15, 1, 28, 2, 2048, 256, 64, table)
