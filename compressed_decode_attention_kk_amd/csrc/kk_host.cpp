@@ -1,6 +1,7 @@
 // Host side of the C ABI: validation, per-layer table resolution, the work
-// plan of one decode step, and kernel launches.  Nothing here allocates,
-// synchronizes or keeps state between calls.
+// plan of one decode step, and kernel launches.  Nothing here allocates
+// device memory, synchronizes or keeps state between calls (plans live in
+// host memory local to the call).
 //
 // Table semantics follow the KV-Kaizen summary page (picx.dev): "Action Space
 // and Cost Model" (actions {inherit} U {(d, b)}, b in {2, 4, 8, 16}) and

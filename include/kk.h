@@ -21,8 +21,9 @@
  *
  * Conventions shared by every entry point
  *   - All device pointers are HIP device allocations owned by the caller.
- *     The library never allocates, frees or synchronizes, and keeps no
- *     mutable global state; calls are thread-safe.
+ *     The library never allocates or frees device memory, never
+ *     synchronizes, and keeps no mutable global state (planning uses host
+ *     memory local to the call); calls are thread-safe.
  *   - Every call validates its arguments on the host before enqueueing
  *     anything; a non-KK_OK status means nothing was enqueued.
  *   - Work is enqueued on the caller's stream and returns asynchronously;
