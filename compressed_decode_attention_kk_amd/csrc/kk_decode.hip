@@ -289,7 +289,7 @@ static_assert(tile_blocks<16>() == 1 && tile_blocks<8>() == 2, "tile_blocks and 
 // Grouped-query rows have d = d_h <= 128 (4 units): none on the Q.K waves, at
 // most 2 per other wave.
 template <int RB, bool GQA = false>
-constexpr int qk_units_max() { return GQA ? 1 : RB >= kWaves ? 4 : 3; }
+constexpr int qk_units_max() { return GQA ? 1 : 3; }
 template <int RB, bool GQA = false>
 constexpr int pv_units_max() { return GQA ? 2 : RB == 3 ? 7 : 5; }
 // 64-field chunks of a row that enter Q.K (grouped-query rows: K = 2 d_h <= 256)
@@ -393,11 +393,8 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   // ---- P.V output units of this wave ---------------------------------------------
   const int NU = (d + 31) >> 5;
   int ubase, ucount;
-  if (RB >= kWaves) {
-    const int per = (NU + kWaves - 1) / kWaves;
-    ubase = wave * per;
-    ucount = max(0, min(per, NU - ubase));
-  } else {
+  static_assert(RB < kWaves, "at least one wave without Q.K rows");
+  {
     const int npv = kWaves - RB;
     int uq = max((NU * 3) / 16, (NU - npv * pv_units_max<RB, GQA>() + RB - 1) / RB);
     uq = min(max(uq, 0), qk_units_max<RB, GQA>());
@@ -413,8 +410,11 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   }
 
   float m_run = -INFINITY, l_lane = 0.0f;     // softmax state of row 16*wave + n (Q.K waves)
-  constexpr int kNoScale = -1000;              // E before an item's first tile
-  int Ecur = kNoScale;                         // scales so far are <= 2^(Ecur + headroom)
+  // E before an item's first tile: any scale above 2^-94 raises it there; a
+  // first tile of all-zero tokens (scale 0) keeps it, and its exponentials,
+  // at most 2^100 each, stay finite in P' (= 0) and in l (< 2^114 over 8192
+  // tokens); a later raise rescales both like any other.
+  int Ecur = -100;                             // scales so far are <= 2^(Ecur + headroom)
 
   // The stage loop of one wave role.  QKW: this wave owns Q.K rows; UMAX: its
   // largest unit count (each role is register-allocated for its own arrays).
@@ -778,9 +778,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           }
           smax = max_xor_16_32(smax);
           tmax = max_xor_16_32(tmax) * rowf;
-          // The first tile always sets E (a tile of all-zero tokens, scale 0,
-          // gives E = 0, so that its exponentials stay finite and count in l).
-          const bool raise_e = smax > ldexpf(1.0f, Ecur + kScaleHeadroom) || Ecur == kNoScale;   // wave-uniform
+          const bool raise_e = smax > ldexpf(1.0f, Ecur + kScaleHeadroom);   // wave-uniform
           const bool upd = __any(tmax > m_run + kLazyRescale) || raise_e;    // wave-uniform
           const int par = tq & 1;
           if (upd) {
@@ -897,7 +895,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
     }
   };
 
-  if (RB >= kWaves || wave < RB)
+  if (wave < RB)
     pipeline(std::true_type{}, std::integral_constant<int, qk_units_max<RB, GQA>()>{});
   else
     pipeline(std::false_type{}, std::integral_constant<int, pv_units_max<RB, GQA>()>{});
@@ -1087,7 +1085,7 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t
         case 1: e = launch_one<1, false>(a, L.items, L.lds_bytes, stream); break;
         case 2: e = launch_one<2, false>(a, L.items, L.lds_bytes, stream); break;
         case 3: e = launch_one<3, false>(a, L.items, L.lds_bytes, stream); break;
-        default: e = launch_one<4, false>(a, L.items, L.lds_bytes, stream); break;
+        default: return hipErrorInvalidValue;   // at most kMaxRowBlocks (3) row blocks
       }
     }
     if (e != hipSuccess) return e;

@@ -102,10 +102,13 @@ kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_to
     int key_num, key_den;  // position of the entry in its bit width's order
   };
   std::vector<Ent> ents;
-  // Row chunks: RB blocks of 16 rows per item, RB fixed by the head count; when
-  // a layer's heads fit in one item, chunks hold whole layers (least padding).
-  const int RB = std::min(4, (std::min(H, 64) + 15) / 16);
-  const int chunk_rows = H <= 64 ? H * ((16 * RB) / H) : 64;
+  // Row chunks: RB <= 3 blocks of 16 rows per item, RB fixed by the head
+  // count; when a layer's heads fit in one item, chunks hold whole layers
+  // (least padding), otherwise 48-row chunks run across layer boundaries.
+  // (Four row blocks need more registers than a wave has: with their spills,
+  // 64- and 128-head tables ran 1.1-2x slower than with 48-row chunks.)
+  const int RB = std::min(kk::kMaxRowBlocks, (std::min(H, 64) + 15) / 16);
+  const int chunk_rows = H <= 16 * RB ? H * ((16 * RB) / H) : 16 * RB;
   const int kEntryRows = 8 * chunk_rows;
   P.launch.row_blocks = RB;
   for (size_t ti = 0; ti < tabs.size(); ++ti) {

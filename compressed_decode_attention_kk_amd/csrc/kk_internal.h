@@ -11,7 +11,7 @@ namespace kk {
 constexpr int kWaves = 4;            // waves per workgroup (256 threads)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;            // token granularity of splits (tiles are 32 or 16 tokens)
-constexpr int kMaxRowBlocks = 4;     // 16-row MFMA blocks per work item (<= 64 query rows)
+constexpr int kMaxRowBlocks = 3;     // 16-row MFMA blocks per work item (<= 48 query rows)
 constexpr int kMaxMergeSplits = 64;  // token splits of one sequence
 constexpr int kMaxK = 576;           // d + d_R (the ABI limit)
 constexpr int kMaxEntries = 88;      // group entries held in the launch arguments
@@ -160,7 +160,7 @@ hipError_t launch_epilogue_gemm_wide(const EpiArgs& a, hipStream_t stream);
 struct DecodeLaunch {
   int items;
   int lds_bytes;         // dynamic LDS per workgroup: the largest entry's need
-  int row_blocks;        // 16-row MFMA blocks per item (1..4), uniform for the step
+  int row_blocks;        // 16-row MFMA blocks per item (1..3), uniform for the step
   int merge_blocks;
   bool grouped = false;  // grouped-query rows [V || K] (row_blocks <= 2)
 };

@@ -155,8 +155,9 @@ def test_inheritor_equals_one_layer_call_on_anchor_cache(kk):
 
 @pytest.mark.parametrize("heads", [64, 100, 128])
 def test_many_heads_row_chunks(kk, heads):
-    """64 heads: four 16-row blocks per item; 100 and 128 heads: 64-row chunks
-    that cross layer boundaries inside an inheriting group."""
+    """More heads than one item's 48 rows: 48-row chunks that cross layer
+    boundaries inside an inheriting group (64 heads: 48 + 16 rows per layer;
+    100 and 128 heads: chunks straddling layers of a 3-layer group)."""
     table = [[0, 256, 4], [0, 0, 0], [2, 128, 16], [3, 192, 8], [3, 0, 0], [3, 0, 0]]
     w = synth.small_workload(16, len(table), heads, 2, 300, 256, 64, table)
     lens = [300, 77]
@@ -230,6 +231,35 @@ def test_append_then_attend(kk):
         for l in range(w.n_layers):
             worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, after[s], src))
     print(f"append then attend: worst err ratio {worst:.2e}")
+
+
+def test_append_then_attend_full_size_sampled(kk):
+    """The 14B mixed table at full size in the configuration bench.py --append
+    times: caches hold 8191 tokens, kk_append_decode writes token 8191 of
+    every sequence into every anchor and decodes over 8192; the new rows are
+    bit-exact and sampled outputs match the oracle over the full context."""
+    w = synth.workload(3)
+    model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+    T = w.seq_len
+    caches = build_caches(kk, model, w, T, seq_lens=[T - 1] * w.batch)
+    new_lat = torch.zeros(w.n_layers, w.batch, w.r, dtype=torch.float32, device="cuda")
+    new_rope = torch.zeros(w.n_layers, w.batch, w.d_rope, dtype=torch.float32, device="cuda")
+    for a in w.anchors():
+        lat, rope, _ = synth.source_rows(w, a, "cuda")
+        new_lat[a] = lat[:, T - 1]
+        new_rope[a] = rope[:, T - 1]
+        del lat, rope
+    ql, qr = synth.queries(w, "cuda")
+    sl = torch.full((w.batch,), T, dtype=torch.int32, device="cuda")
+    dec = kk.Decoder(model, caches, w.batch, T, T)
+    dec.append(new_lat, new_rope, ql, qr, sl)
+    torch.cuda.synchronize()
+    picks = [next(l for l in range(w.n_layers) if w.bits_eff(l) == b) for b in (2, 4, 8, 16)]
+    worst = 0.0
+    for i, l in enumerate(picks):
+        s_ = 0 if i % 2 == 0 else w.batch - 1
+        worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s_, T))
+    print(f"append full size: worst err ratio {worst:.2e}")
 
 
 def test_outliers_and_zero_tokens(kk):
