@@ -119,6 +119,27 @@ def test_edge_lengths_and_empty(kk):
                 check_layer_seq(w, dec, caches, ql, qr, l, s, lens[s], src)
 
 
+def test_max_seq_len_is_a_hint_and_lengths_clamp(kk):
+    """max_seq_len only sets the split count: with a hint below the real
+    lengths (or 0) every token is still attended; seq_lens above t_cap are
+    clamped to t_cap (the caches hold t_cap rows)."""
+    table = [[0, 64, 8], [0, 0, 0], [2, 96, 16], [3, 64, 2]]
+    w = synth.small_workload(18, 4, 16, 3, 256, 128, 32, table)
+    model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+    caches = build_caches(kk, model, w, 256)
+    ql, qr = synth.queries(w, "cuda")
+    lens = [256, 200, 1000]                         # the last one clamps to t_cap = 256
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    for hint in (0, 64, 256):
+        dec = kk.Decoder(model, caches, 3, 256, hint)
+        dec(ql, qr, sl)
+        torch.cuda.synchronize()
+        for s_ in range(3):
+            src = {a: source_cpu(w, a, s_) for a in w.anchors()}
+            for l in range(w.n_layers):
+                check_layer_seq(w, dec, caches, ql, qr, l, s_, min(lens[s_], 256), src)
+
+
 def test_deterministic_and_split_invariant(kk):
     w = synth.small_workload(12, len(MIXED_SMALL), 40, 2, 700, 256, 32, MIXED_SMALL)
     model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
