@@ -286,15 +286,18 @@ static_assert(tile_blocks<16>() == 1 && tile_blocks<8>() == 2, "tile_blocks and 
 
 // P.V output units (32 features) per wave.  Q.K waves take a few units; the
 // waves without Q.K rows take the rest, so that no wave idles while Q.K runs.
-// Grouped-query rows have d = d_h <= 128 (4 units): none on the Q.K waves, at
-// most 2 per other wave.
-template <int RB, bool GQA = false>
-constexpr int qk_units_max() { return GQA ? 1 : 3; }
-template <int RB, bool GQA = false>
-constexpr int pv_units_max() { return GQA ? 2 : RB == 3 ? 7 : 5; }
-// 64-field chunks of a row that enter Q.K (grouped-query rows: K = 2 d_h <= 256)
-template <bool GQA>
-constexpr int max_chunks() { return GQA ? 4 : (kMaxK + 63) / 64; }
+// Kernel variants (register budgets): kFull, any row; kLean, rows with K <= 320
+// and d <= 256 in items of at most 2 row blocks (3 workgroups per CU);
+// kGqa, grouped-query rows [V || K] with d = d_h <= 128 (4 workgroups per
+// CU).  Lean and grouped-query rows have at most 8 and 4 output units.  (A
+// lean 3-row-block item spills: it is left to the full variant.)
+template <int RB, int V>
+constexpr int qk_units_max() { return V == kGqa ? 1 : V == kLean ? 2 : 3; }
+template <int RB, int V>
+constexpr int pv_units_max() { return V == kGqa ? 2 : V == kLean ? 4 : RB == 3 ? 7 : 5; }
+// 64-field chunks of a row that enter Q.K
+template <int V>
+constexpr int max_chunks() { return V == kGqa ? 4 : V == kLean ? 5 : (kMaxK + 63) / 64; }
 
 __device__ inline f4 mfma_f16_k16(h4 a, h4 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0); }
 
@@ -313,10 +316,11 @@ __device__ inline h4 cvt_i16x4(u2 w) {
 // and the flags are double buffered by tile parity.
 // GQA: grouped-query rows [V || K] (values first; Q.K skips the value
 // chunks, the first half of the row) and sequence s reading seq_lens[s / n_kv].
-template <int BITS, int RB, bool GQA>
+template <int BITS, int RB, int V>
 __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit, int chunk, char* lds) {
   constexpr int TB = tile_blocks<BITS>();
-  constexpr int kMaxC = max_chunks<GQA>();
+  constexpr int kMaxC = max_chunks<V>();
+  constexpr bool GQA = V == kGqa;
   constexpr int TILE = 16 * TB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, n = lane & 15;
@@ -396,8 +400,8 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   static_assert(RB < kWaves, "at least one wave without Q.K rows");
   {
     const int npv = kWaves - RB;
-    int uq = max((NU * 3) / 16, (NU - npv * pv_units_max<RB, GQA>() + RB - 1) / RB);
-    uq = min(max(uq, 0), qk_units_max<RB, GQA>());
+    int uq = max((NU * 3) / 16, (NU - npv * pv_units_max<RB, V>() + RB - 1) / RB);
+    uq = min(max(uq, 0), qk_units_max<RB, V>());
     const int rest = NU - RB * uq;
     const int per = (rest + npv - 1) / npv;
     if (wave < RB) {
@@ -733,10 +737,10 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
               case 2: qk_chunks(Z{}, std::integral_constant<int, 2>{}); break;
               case 3: qk_chunks(Z{}, std::integral_constant<int, 3>{}); break;
               case 4: qk_chunks(Z{}, std::integral_constant<int, 4>{}); break;
-              case 5: qk_chunks(Z{}, std::integral_constant<int, 5>{}); break;
-              case 6: qk_chunks(Z{}, std::integral_constant<int, 6>{}); break;
-              case 7: qk_chunks(Z{}, std::integral_constant<int, 7>{}); break;
-              case 8: qk_chunks(Z{}, std::integral_constant<int, 8>{}); break;
+              case 5: if constexpr (kMaxC >= 5) qk_chunks(Z{}, std::integral_constant<int, 5>{}); break;
+              case 6: if constexpr (kMaxC >= 6) qk_chunks(Z{}, std::integral_constant<int, 6>{}); break;
+              case 7: if constexpr (kMaxC >= 7) qk_chunks(Z{}, std::integral_constant<int, 7>{}); break;
+              case 8: if constexpr (kMaxC >= 8) qk_chunks(Z{}, std::integral_constant<int, 8>{}); break;
               default: qk_chunks(Z{}, std::integral_constant<int, kMaxC>{}); break;
             }
           }
@@ -896,9 +900,9 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   };
 
   if (wave < RB)
-    pipeline(std::true_type{}, std::integral_constant<int, qk_units_max<RB, GQA>()>{});
+    pipeline(std::true_type{}, std::integral_constant<int, qk_units_max<RB, V>()>{});
   else
-    pipeline(std::false_type{}, std::integral_constant<int, pv_units_max<RB, GQA>()>{});
+    pipeline(std::false_type{}, std::integral_constant<int, pv_units_max<RB, V>()>{});
 }
 
 // Last entry whose first decode block (merge: first merge block) is <= blk;
@@ -922,8 +926,8 @@ __device__ inline KArgs& kernel_args() {
 // One launch covers the items of every bit width, interleaved by the host so
 // that each CU runs a mix of bandwidth-bound (wide codes) and arithmetic-bound
 // (narrow codes) items; the bit width is uniform per workgroup.
-template <int RB, bool GQA>
-__global__ void __launch_bounds__(kThreads, GQA ? 4 : 2) decode_kernel(DecodeArgs) {
+template <int RB, int V>
+__global__ void __launch_bounds__(kThreads, decode_wg_per_cu(V)) decode_kernel(DecodeArgs) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   KArgs& A = kernel_args();
   const int item = blockIdx.x;
@@ -946,10 +950,10 @@ __global__ void __launch_bounds__(kThreads, GQA ? 4 : 2) decode_kernel(DecodeArg
   }
   const int s = j / E.splits, ks = j - s * E.splits;
   switch (E.bits) {
-    case 2: run_item<2, RB, GQA>(A, E, s, ks, chunk, lds); break;
-    case 4: run_item<4, RB, GQA>(A, E, s, ks, chunk, lds); break;
-    case 8: run_item<8, RB, GQA>(A, E, s, ks, chunk, lds); break;
-    default: run_item<16, RB, GQA>(A, E, s, ks, chunk, lds); break;
+    case 2: run_item<2, RB, V>(A, E, s, ks, chunk, lds); break;
+    case 4: run_item<4, RB, V>(A, E, s, ks, chunk, lds); break;
+    case 8: run_item<8, RB, V>(A, E, s, ks, chunk, lds); break;
+    default: run_item<16, RB, V>(A, E, s, ks, chunk, lds); break;
   }
 }
 
@@ -1048,12 +1052,12 @@ __global__ void __launch_bounds__(256) store_kernel(StoreArgs) {
   for (int i = threadIdx.x; i < a.n; i += 256) a.dst[i] = a.w[i];
 }
 
-template <int RB, bool GQA>
+template <int RB, int V>
 hipError_t launch_one(const DecodeArgs& a, int n, int lds, hipStream_t stream) {
   hipError_t e =
-      hipFuncSetAttribute((const void*)decode_kernel<RB, GQA>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      hipFuncSetAttribute((const void*)decode_kernel<RB, V>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((decode_kernel<RB, GQA>), dim3(n), dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((decode_kernel<RB, V>), dim3(n), dim3(kThreads), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -1061,14 +1065,14 @@ hipError_t launch_one(const DecodeArgs& a, int n, int lds, hipStream_t stream) {
 
 // Tile buffers per workgroup: as many as fit in the workgroup's share of the
 // 160 KB LDS, 3 to 12 (two tiles are in use, the rest in flight).
-int decode_nbuf(int row_stride, int K, int bits, int rb, bool grouped) {
-  const int budget = 160 * 1024 / decode_wg_per_cu(grouped) - pbuf_bytes(rb, tile_blocks_of(bits)) - kMiscBytes;
+int decode_nbuf(int row_stride, int K, int bits, int rb, int variant) {
+  const int budget = 160 * 1024 / decode_wg_per_cu(variant) - pbuf_bytes(rb, tile_blocks_of(bits)) - kMiscBytes;
   const int n = budget / tilebuf_bytes(row_stride, K, bits);
   return n < 3 ? 3 : (n > 12 ? 12 : n);
 }
 
-int decode_lds_bytes(int row_stride, int K, int bits, int rb, bool grouped) {
-  return decode_nbuf(row_stride, K, bits, rb, grouped) * tilebuf_bytes(row_stride, K, bits) +
+int decode_lds_bytes(int row_stride, int K, int bits, int rb, int variant) {
+  return decode_nbuf(row_stride, K, bits, rb, variant) * tilebuf_bytes(row_stride, K, bits) +
          pbuf_bytes(rb, tile_blocks_of(bits)) + kMiscBytes;
 }
 
@@ -1076,15 +1080,19 @@ hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t
   static_assert(sizeof(DecodeArgs) < 7600, "kernel argument block too large");
   if (L.items > 0) {
     hipError_t e;
-    if (L.grouped) {                  // grouped-query rows: <= 32 per KV head, <= 2 row blocks
+    if (L.variant == kGqa) {          // grouped-query rows: <= 32 per KV head, <= 2 row blocks
       if (L.row_blocks > 2) return hipErrorInvalidValue;
-      e = L.row_blocks == 1 ? launch_one<1, true>(a, L.items, L.lds_bytes, stream)
-                            : launch_one<2, true>(a, L.items, L.lds_bytes, stream);
+      e = L.row_blocks == 1 ? launch_one<1, kGqa>(a, L.items, L.lds_bytes, stream)
+                            : launch_one<2, kGqa>(a, L.items, L.lds_bytes, stream);
+    } else if (L.variant == kLean) {  // <= 2 row blocks
+      if (L.row_blocks > 2) return hipErrorInvalidValue;
+      e = L.row_blocks == 1 ? launch_one<1, kLean>(a, L.items, L.lds_bytes, stream)
+                            : launch_one<2, kLean>(a, L.items, L.lds_bytes, stream);
     } else {
       switch (L.row_blocks) {
-        case 1: e = launch_one<1, false>(a, L.items, L.lds_bytes, stream); break;
-        case 2: e = launch_one<2, false>(a, L.items, L.lds_bytes, stream); break;
-        case 3: e = launch_one<3, false>(a, L.items, L.lds_bytes, stream); break;
+        case 1: e = launch_one<1, kFull>(a, L.items, L.lds_bytes, stream); break;
+        case 2: e = launch_one<2, kFull>(a, L.items, L.lds_bytes, stream); break;
+        case 3: e = launch_one<3, kFull>(a, L.items, L.lds_bytes, stream); break;
         default: return hipErrorInvalidValue;   // at most kMaxRowBlocks (3) row blocks
       }
     }

@@ -159,8 +159,17 @@ kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_to
   const int max_tiles = std::max(1, (max_len + kk::kTile - 1) / kk::kTile);
   int64_t total_cost = 0;
   for (auto& E : ents) total_cost += E.cost_tile * max_tiles * E.e.nrc * E.e.n_seq;
-  const bool grouped = tabs[0].qk_c0 > 0;
-  const int64_t slots = (int64_t)kk::kCUs * kk::decode_wg_per_cu(grouped);
+  // kernel variant: grouped-query rows, or every anchor narrow enough for the
+  // lean register budget (items of <= 2 row blocks), or the full one
+  int variant = tabs[0].qk_c0 > 0 ? kk::kGqa : RB <= 2 ? kk::kLean : kk::kFull;
+  if (variant == kk::kLean)
+    for (auto& T : tabs)
+      for (int a = 0; a < L; ++a)
+        if (T.cfg->layers[a].anchor == a &&
+            (T.cfg->layers[a].d > kk::kLeanMaxD || T.cfg->layers[a].d + T.cfg->d_rope > kk::kLeanMaxK))
+          variant = kk::kFull;
+  P.launch.variant = variant;
+  const int64_t slots = (int64_t)kk::kCUs * kk::decode_wg_per_cu(variant);
   auto split_of = [&](const Ent& E, int waves) {
     const int64_t target = std::max<int64_t>(1, total_cost / (waves * slots));
     int64_t sp;
@@ -240,9 +249,9 @@ kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_to
       ws += (int64_t)e.nrc * e.n_seq * e.splits * kk::partial_slot_floats(e.d);
       merges += (int64_t)e.nrc * e.n_seq;
     }
-    e.nbuf = (int8_t)kk::decode_nbuf(e.row_stride, e.d + c0->d_rope, e.bits, RB, grouped);
-    Lc.lds_bytes = std::max(Lc.lds_bytes, kk::decode_lds_bytes(e.row_stride, e.d + c0->d_rope, e.bits, RB, grouped));
-    if (Lc.lds_bytes > 160 * 1024 / kk::decode_wg_per_cu(grouped)) return KK_ERR_UNSUPPORTED;
+    e.nbuf = (int8_t)kk::decode_nbuf(e.row_stride, e.d + c0->d_rope, e.bits, RB, variant);
+    Lc.lds_bytes = std::max(Lc.lds_bytes, kk::decode_lds_bytes(e.row_stride, e.d + c0->d_rope, e.bits, RB, variant));
+    if (Lc.lds_bytes > 160 * 1024 / kk::decode_wg_per_cu(variant)) return KK_ERR_UNSUPPORTED;
     P.ents[i] = e;
     P.entry_anchor[i] = ents[i].anchor;
     P.entry_table[i] = ents[i].table;
@@ -739,7 +748,6 @@ kk_status kk_gqa_decode_attn(const kk_gqa_cfg* cfg, const kk_cache* caches, int3
   A.t_cap = t_cap;
   A.q_is_f32 = q_dtype == KK_DTYPE_F32;
   A.seq_div = cfg->n_kv_heads;
-  P.launch.grouped = true;
   return kk::launch_decode(A, P.launch, stream) == hipSuccess ? KK_OK : KK_ERR_DEVICE;
 }
 

@@ -17,10 +17,14 @@ constexpr int kMaxK = 576;           // d + d_R (the ABI limit)
 constexpr int kMaxEntries = 88;      // group entries held in the launch arguments
 constexpr int kMaxLayers = 64;
 constexpr int kCUs = 256;
-// Decode workgroups per CU: two for latent rows (a second workgroup hides the
-// per-item and per-tile fixed latencies of the first); four for the leaner
-// grouped-query instantiation, whose items carry few rows and bytes per stage.
-constexpr int decode_wg_per_cu(bool grouped) { return grouped ? 4 : 2; }
+// Decode kernel variants (register budgets) and workgroups per CU: kFull, any
+// latent row (256 VGPRs: two workgroups, the second hides the fixed latencies
+// of the first); kLean, steps whose anchors all have d <= 256 and K = d + d_R
+// <= 320, in items of at most 2 row blocks (three); kGqa, grouped-query rows
+// (four).
+constexpr int kFull = 0, kLean = 1, kGqa = 2;
+constexpr int decode_wg_per_cu(int variant) { return variant == kGqa ? 4 : variant == kLean ? 3 : 2; }
+constexpr int kLeanMaxD = 256, kLeanMaxK = 320;
 constexpr float kLazyRescale = 8.0f; // log2 headroom before the running max is moved
 
 // One layer of one table: softmax scale, kept width of its anchor and the
@@ -162,11 +166,11 @@ struct DecodeLaunch {
   int lds_bytes;         // dynamic LDS per workgroup: the largest entry's need
   int row_blocks;        // 16-row MFMA blocks per item (1..3), uniform for the step
   int merge_blocks;
-  bool grouped = false;  // grouped-query rows [V || K] (row_blocks <= 2)
+  int variant = kFull;   // kernel variant (kGqa: row_blocks <= 2)
 };
 
-int decode_nbuf(int row_stride, int K, int bits, int row_blocks, bool grouped);
-int decode_lds_bytes(int row_stride, int K, int bits, int row_blocks, bool grouped);
+int decode_nbuf(int row_stride, int K, int bits, int row_blocks, int variant);
+int decode_lds_bytes(int row_stride, int K, int bits, int row_blocks, int variant);
 hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t stream);
 
 // Copies `words` 32-bit words from host memory to device memory `dst` by
