@@ -79,7 +79,8 @@ int bits_class(int bits) { return bits == 2 ? 0 : bits == 4 ? 1 : bits == 8 ? 2 
 // and 8-bit codes (fixed per-tile work dominates), up to 1.7x for 16-bit codes,
 // which stream 2-8x the bytes (measured on MI355X).
 int64_t tile_cost(int bits, int d) { return 10 + (bits == 16 ? (7 * d + 511) / 512 : 0); }
-constexpr int kItemWaves = 4;       // waves of items over the resident slots (mixed tables)
+constexpr int kItemWaves = 4;       // waves of items over the resident slots (mixed tables), at most
+constexpr int kMinItemTiles = 96;   // ... fewer when items would average fewer tiles than this
 constexpr int kMinSplitTiles = 8;   // no split shorter than 8 tiles (256 tokens)
 constexpr int64_t kTailPercent = 15;  // share of the work (last dispatched) cut twice as fine
 constexpr int64_t kItemOverhead = 40;   // per-item fixed cost (query setup, pipeline fill, stores)
@@ -180,10 +181,23 @@ kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_to
     return std::min<int64_t>(sp, kk::kMaxMergeSplits);
   };
   // Mixed tables: longest-first order leaves short items for the end, so few,
-  // long items are best (kItemWaves).  When every entry is alike, all items are
-  // equal and the last wave of items decides: pick the wave count whose items
-  // fill whole waves best, i.e. the least (waves of items) x (item time).
+  // long items are best: kItemWaves waves, or fewer (down to 2) while the
+  // average item would be shorter than kMinItemTiles (small batches, where the
+  // per-item fixed cost and the split merges would weigh more).  When every
+  // entry is alike, all items are equal and the last wave of items decides:
+  // pick the wave count whose items fill whole waves best, i.e. the least
+  // (waves of items) x (item time).
   int waves = kItemWaves;
+  if (split_tokens <= 0) {
+    for (; waves > 2; --waves) {
+      int64_t work = 0, pieces = 0;
+      for (auto& E : ents) {
+        work += (int64_t)E.e.nrc * E.e.n_seq * max_tiles;
+        pieces += (int64_t)E.e.nrc * E.e.n_seq * split_of(E, waves);
+      }
+      if (pieces == 0 || work >= kMinItemTiles * pieces) break;
+    }
+  }
   bool alike = split_tokens <= 0 && !ents.empty();
   for (auto& E : ents)
     alike = alike && E.e.bits == ents[0].e.bits && E.e.d == ents[0].e.d && E.e.nrc == ents[0].e.nrc;
