@@ -25,7 +25,7 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 bool valid_bits(int b) { return b == 2 || b == 4 || b == 8 || b == 16; }
 
 // Layer table rules.  INVALID: breaks the method's rules; UNSUPPORTED: outside
-// this build's limits.
+// this library's limits.
 kk_status check_model(const kk_model_cfg* c) {
   if (!c || !c->layers) return KK_ERR_INVALID_ARGUMENT;
   if (c->n_layers < 1 || c->n_heads < 1 || c->r < 1 || c->d_rope < 1) return KK_ERR_INVALID_ARGUMENT;
@@ -828,7 +828,7 @@ const char* kk_status_string(kk_status s) {
   switch (s) {
     case KK_OK: return "ok";
     case KK_ERR_INVALID_ARGUMENT: return "invalid argument";
-    case KK_ERR_UNSUPPORTED: return "unsupported by this build";
+    case KK_ERR_UNSUPPORTED: return "unsupported by this library";
     case KK_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case KK_ERR_DEVICE: return "device error";
   }

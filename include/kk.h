@@ -65,7 +65,7 @@ extern "C" {
 typedef enum {
   KK_OK = 0,
   KK_ERR_INVALID_ARGUMENT = 1,   /* a rule below is broken (null, misaligned, out of range) */
-  KK_ERR_UNSUPPORTED = 2,        /* valid for the method but outside this build's limits */
+  KK_ERR_UNSUPPORTED = 2,        /* valid for the method but outside this library's limits */
   KK_ERR_WORKSPACE_TOO_SMALL = 3,
   KK_ERR_DEVICE = 4              /* a HIP launch or query failed */
 } kk_status;
