@@ -18,7 +18,6 @@ LIB_PATH = os.path.join(_HERE, "libkk.so")
 
 KK_OK, KK_ERR_INVALID_ARGUMENT, KK_ERR_UNSUPPORTED, KK_ERR_WORKSPACE_TOO_SMALL, KK_ERR_DEVICE = range(5)
 KK_DTYPE_F32, KK_DTYPE_BF16 = 0, 1
-TILE = 32
 
 
 class KKError(RuntimeError):
@@ -124,6 +123,22 @@ def _check(status: int, what: str):
         raise KKError(status, what)
 
 
+def _require(cond, what: str):
+    """Argument check of the binding.  The library checks scalars and pointers
+    itself but cannot see tensor extents, so these checks guard its kernels
+    against short buffers; unlike assert they stay active under python -O."""
+    if not cond:
+        raise ValueError(what)
+
+
+def _tensor(t, name: str, dtype=None, contiguous=True):
+    _require(isinstance(t, torch.Tensor) and t.is_cuda, f"{name} must be a device tensor")
+    if dtype is not None:
+        _require(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    if contiguous:
+        _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
 def _ptr(t):
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
@@ -189,6 +204,26 @@ def out_offsets(model: Model, batch: int):
     return list(arr)
 
 
+def _check_cache(model: Model, layer: int, codes: torch.Tensor, scales: torch.Tensor, batch: int, t_cap: int):
+    """codes / scales are large enough for anchor `layer`'s cache of [batch][t_cap]."""
+    cb, sb = cache_bytes(model, layer, batch, t_cap)
+    _tensor(codes, f"codes of layer {layer}", torch.uint8)
+    _tensor(scales, f"scales of layer {layer}", torch.float32)
+    _require(codes.numel() >= cb and scales.numel() * 4 >= sb,
+             f"cache of layer {layer} must hold {cb} code bytes and {sb // 4} scales for batch {batch}, t_cap {t_cap}")
+
+
+def _cache_table(model: Model, caches: dict, batch: int, t_cap: int):
+    """kk_cache[n_layers] of the anchors' buffers (entries of inheritors stay NULL)."""
+    tab = (Cache * model.n_layers)()
+    for l in model.anchors():
+        _require(l in caches, f"no cache for anchor layer {l}")
+        c, s = caches[l]
+        _check_cache(model, l, c, s, batch, t_cap)
+        tab[l] = Cache(c.data_ptr(), s.data_ptr())
+    return tab
+
+
 def alloc_cache(model: Model, layer: int, batch: int, t_cap: int, device="cuda"):
     """Device buffers of one anchor cache: (codes uint8 [B, T_cap, stride], scales f32 [B, T_cap])."""
     cb, _ = cache_bytes(model, layer, batch, t_cap)
@@ -206,14 +241,21 @@ def quantize_write(model: Model, layer: int, latent: torch.Tensor, rope: torch.T
     dst_slot: int64 [n_tokens] (seq * t_cap + position); src_index: int32 [n_tokens] or None.
     codes/scales: the anchor's cache buffers [B, T_cap, stride] / [B, T_cap].
     """
-    assert latent.is_cuda and rope.is_cuda and codes.is_cuda and scales.is_cuda and dst_slot.is_cuda
-    assert latent.dim() == 2 and rope.dim() == 2 and latent.stride(1) == 1 and rope.stride(1) == 1
-    assert latent.dtype == rope.dtype and dst_slot.dtype == torch.int64 and dst_slot.is_contiguous()
-    assert codes.dtype == torch.uint8 and scales.dtype == torch.float32 and codes.is_contiguous() and scales.is_contiguous()
-    if src_index is not None:
-        assert src_index.dtype == torch.int32 and src_index.is_contiguous() and src_index.is_cuda
-        assert src_index.numel() == dst_slot.numel()
+    _tensor(latent, "latent", contiguous=False)
+    _tensor(rope, "rope", latent.dtype, contiguous=False)
+    _require(latent.dim() == 2 and rope.dim() == 2 and latent.stride(1) == 1 and rope.stride(1) == 1,
+             "latent and rope must be 2-D with unit column stride")
+    _require(rope.shape[0] == latent.shape[0], "latent and rope must have the same number of rows")
+    _require(latent.shape[1] >= model.d_eff(layer) and rope.shape[1] >= model.d_rope,
+             "latent needs >= d columns and rope >= d_rope columns")
+    _tensor(dst_slot, "dst_slot", torch.int64)
+    _tensor(scales, "scales", torch.float32)
+    _require(scales.dim() == 2, "scales must be [batch, t_cap]")
     batch, t_cap = scales.shape
+    _check_cache(model, layer, codes, scales, batch, t_cap)
+    if src_index is not None:
+        _tensor(src_index, "src_index", torch.int32)
+        _require(src_index.numel() == dst_slot.numel(), "src_index and dst_slot must have one entry per token")
     st = lib().kk_quantize_write(model.cfg, layer, _ptr(latent), _ptr(rope), _dtype_code(latent.dtype),
                                  latent.stride(0), rope.stride(0), latent.shape[0], dst_slot.numel(),
                                  _ptr(src_index), _ptr(dst_slot), Cache(codes.data_ptr(), scales.data_ptr()),
@@ -236,24 +278,18 @@ class Decoder:
         self.model, self.batch, self.t_cap, self.max_seq_len = model, batch, t_cap, max_seq_len
         self.split_tokens = split_tokens
         self.caches = caches
-        self._ctab = (Cache * model.n_layers)()
-        for l in range(model.n_layers):
-            if model.layers[l].anchor == l:
-                c, s = caches[l]
-                self._ctab[l] = Cache(c.data_ptr(), s.data_ptr())
+        self._ctab = _cache_table(model, caches, batch, t_cap)
         offs = out_offsets(model, batch)
         self.offsets = offs
         self.out = torch.empty(offs[-1], dtype=torch.float32, device=device)
         wb = workspace_bytes(model, batch, max_seq_len, split_tokens)
-        self.workspace = torch.empty(max(wb, 256) // 4 + 64, dtype=torch.float32, device=device)
+        self.workspace = _workspace(wb, device)
         self.ws_bytes = wb
 
     def __call__(self, q_lat: torch.Tensor, q_rope: torch.Tensor, seq_lens: torch.Tensor, stream=None):
         m = self.model
-        assert q_lat.is_contiguous() and q_rope.is_contiguous() and q_lat.dtype == q_rope.dtype
-        assert tuple(q_lat.shape) == (m.n_layers, self.batch, m.n_heads, m.r)
-        assert tuple(q_rope.shape) == (m.n_layers, self.batch, m.n_heads, m.d_rope)
-        assert seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.numel() == self.batch
+        _check_queries(q_lat, q_rope, m.n_layers, self.batch, m.n_heads, m.r, m.d_rope)
+        _check_lens(seq_lens, self.batch)
         ws = self.workspace
         wptr = (ws.data_ptr() + 255) // 256 * 256
         st = lib().kk_decode_attn(m.cfg, self._ctab, self.batch, self.t_cap, _ptr(seq_lens), self.max_seq_len,
@@ -268,13 +304,13 @@ class Decoder:
         every anchor cache, then decode over the extended caches.  new_latent
         [n_layers, batch, r] and new_rope [n_layers, batch, d_rope], one dtype."""
         m = self.model
-        assert new_latent.is_contiguous() and new_rope.is_contiguous() and new_latent.dtype == new_rope.dtype
-        assert tuple(new_latent.shape) == (m.n_layers, self.batch, m.r)
-        assert tuple(new_rope.shape) == (m.n_layers, self.batch, m.d_rope)
-        assert q_lat.is_contiguous() and q_rope.is_contiguous() and q_lat.dtype == q_rope.dtype
-        assert tuple(q_lat.shape) == (m.n_layers, self.batch, m.n_heads, m.r)
-        assert tuple(q_rope.shape) == (m.n_layers, self.batch, m.n_heads, m.d_rope)
-        assert seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.numel() == self.batch
+        _tensor(new_latent, "new_latent")
+        _tensor(new_rope, "new_rope", new_latent.dtype)
+        _require(tuple(new_latent.shape) == (m.n_layers, self.batch, m.r), "new_latent must be [n_layers, batch, r]")
+        _require(tuple(new_rope.shape) == (m.n_layers, self.batch, m.d_rope),
+                 "new_rope must be [n_layers, batch, d_rope]")
+        _check_queries(q_lat, q_rope, m.n_layers, self.batch, m.n_heads, m.r, m.d_rope)
+        _check_lens(seq_lens, self.batch)
         wptr = (self.workspace.data_ptr() + 255) // 256 * 256
         st = lib().kk_append_decode(m.cfg, self._ctab, self.batch, self.t_cap, _ptr(seq_lens), self.max_seq_len,
                                     _ptr(new_latent), _ptr(new_rope), _dtype_code(new_latent.dtype),
@@ -289,13 +325,22 @@ class Decoder:
         return self.out[self.offsets[l]:self.offsets[l + 1]].view(self.batch, m.n_heads, m.d_eff(l))
 
 
-def _cache_table(model: Model, caches: dict):
-    tab = (Cache * model.n_layers)()
-    for l in range(model.n_layers):
-        if model.layers[l].anchor == l:
-            c, s = caches[l]
-            tab[l] = Cache(c.data_ptr(), s.data_ptr())
-    return tab
+def _workspace(nbytes: int, device):
+    """Device buffer of >= nbytes from a 256-byte aligned address (see the callers' wptr)."""
+    return torch.empty((max(nbytes, 256) + 3) // 4 + 64, dtype=torch.float32, device=device)
+
+
+def _check_queries(q_lat, q_rope, n_layers, batch, n_heads, r, d_rope):
+    _tensor(q_lat, "q_lat")
+    _tensor(q_rope, "q_rope", q_lat.dtype)
+    _require(tuple(q_lat.shape) == (n_layers, batch, n_heads, r), "q_lat must be [n_layers, batch, n_heads, r]")
+    _require(tuple(q_rope.shape) == (n_layers, batch, n_heads, d_rope),
+             "q_rope must be [n_layers, batch, n_heads, d_rope]")
+
+
+def _check_lens(seq_lens, batch):
+    _tensor(seq_lens, "seq_lens", torch.int32)
+    _require(seq_lens.numel() == batch, f"seq_lens must have {batch} entries")
 
 
 class MultiDecoder:
@@ -311,7 +356,7 @@ class MultiDecoder:
         self.batches = [int(b) for _, _, b in self.runs]
         self.batch = sum(self.batches)
         self.t_cap, self.max_seq_len, self.split_tokens = t_cap, max_seq_len, split_tokens
-        self._ctabs = [_cache_table(m, c) if c is not None else None for m, c, _ in self.runs]
+        self._ctabs = [_cache_table(m, c, b, t_cap) if c is not None else None for m, c, b in self.runs]
         self._tabs = (TableBatch * len(self.runs))(*[
             TableBatch(ctypes.pointer(m._cfg), b, ctab if ctab is not None else None)
             for (m, _, b), ctab in zip(self.runs, self._ctabs)])
@@ -324,13 +369,12 @@ class MultiDecoder:
         _check(lib().kk_multi_decode_workspace_bytes(self._tabs, n, max_seq_len, split_tokens, ctypes.byref(wb)),
                "kk_multi_decode_workspace_bytes")
         self.ws_bytes = wb.value
-        self.workspace = torch.empty(self.ws_bytes // 4 + 64, dtype=torch.float32, device=device)
+        self.workspace = _workspace(self.ws_bytes, device)
 
     def __call__(self, q_lat: torch.Tensor, q_rope: torch.Tensor, seq_lens: torch.Tensor, stream=None):
-        assert q_lat.is_contiguous() and q_rope.is_contiguous() and q_lat.dtype == q_rope.dtype
-        assert tuple(q_lat.shape) == (self.n_layers, self.batch, self.n_heads, self.r)
-        assert tuple(q_rope.shape) == (self.n_layers, self.batch, self.n_heads, self.d_rope)
-        assert seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.numel() == self.batch
+        _require(all(c is not None for c in self._ctabs), "every run needs its caches to decode")
+        _check_queries(q_lat, q_rope, self.n_layers, self.batch, self.n_heads, self.r, self.d_rope)
+        _check_lens(seq_lens, self.batch)
         wptr = (self.workspace.data_ptr() + 255) // 256 * 256
         st = lib().kk_multi_decode_attn(self._tabs, len(self.runs), self.t_cap, _ptr(seq_lens), self.max_seq_len,
                                         _ptr(q_lat), _ptr(q_rope), _dtype_code(q_lat.dtype), _ptr(self.out),
@@ -355,15 +399,22 @@ def latent_epilogue(model: Model, batch: int, o_lat: torch.Tensor, w_uv, w_o, v:
     v: float32 [n_layers, batch, n_heads * d_v]; y: float32 [n_layers, batch, d_model].
     """
     L = model.n_layers
-    assert len(w_uv) == L and len(w_o) == L
+    _require(len(w_uv) == L and len(w_o) == L, "one W_UV and one W_O per layer")
+    _tensor(w_o[0], "w_o[0]", torch.bfloat16)
+    _require(w_o[0].dim() == 2 and w_o[0].shape[1] % model.n_heads == 0, "w_o must be [d_model, n_heads * d_v]")
     d_model, hv = w_o[0].shape
     d_v = hv // model.n_heads
-    for a, b in zip(w_uv, w_o):
-        assert a.dtype == torch.bfloat16 and b.dtype == torch.bfloat16 and a.is_contiguous() and b.is_contiguous()
-        assert tuple(a.shape) == (hv, model.r) and tuple(b.shape) == (d_model, hv)
-    assert o_lat.dtype == torch.float32 and o_lat.is_contiguous()
-    assert tuple(v.shape) == (L, batch, hv) and v.dtype == torch.float32 and v.is_contiguous()
-    assert tuple(y.shape) == (L, batch, d_model) and y.dtype == torch.float32 and y.is_contiguous()
+    for l, (a, b) in enumerate(zip(w_uv, w_o)):
+        _tensor(a, f"w_uv[{l}]", torch.bfloat16)
+        _tensor(b, f"w_o[{l}]", torch.bfloat16)
+        _require(tuple(a.shape) == (hv, model.r) and tuple(b.shape) == (d_model, hv),
+                 f"layer {l}: w_uv must be [n_heads * d_v, r] and w_o [d_model, n_heads * d_v]")
+    _tensor(o_lat, "o_lat", torch.float32)
+    _require(o_lat.numel() == out_offsets(model, batch)[-1], "o_lat must be the packed decode output")
+    _tensor(v, "v", torch.float32)
+    _tensor(y, "y", torch.float32)
+    _require(tuple(v.shape) == (L, batch, hv), "v must be [n_layers, batch, n_heads * d_v]")
+    _require(tuple(y.shape) == (L, batch, d_model), "y must be [n_layers, batch, d_model]")
     pu = (ctypes.c_void_p * L)(*[t.data_ptr() for t in w_uv])
     po = (ctypes.c_void_p * L)(*[t.data_ptr() for t in w_o])
     st = lib().kk_latent_epilogue(model.cfg, batch, d_v, d_model, _ptr(o_lat), pu, po, _ptr(v), _ptr(y),
@@ -391,6 +442,16 @@ class GqaModel:
         return [l for l, s in enumerate(self.layers) if s.anchor == l]
 
 
+def _check_gqa_cache(model: GqaModel, layer: int, codes, scales, batch: int, t_cap: int):
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().kk_gqa_cache_bytes(model.cfg, layer, batch, t_cap, ctypes.byref(cb), ctypes.byref(sb)),
+           "kk_gqa_cache_bytes")
+    _tensor(codes, f"codes of layer {layer}", torch.uint8)
+    _tensor(scales, f"scales of layer {layer}", torch.float32)
+    _require(codes.numel() >= cb.value and scales.numel() * 4 >= sb.value,
+             f"cache of layer {layer} must hold {cb.value} code bytes and {sb.value // 4} scales")
+
+
 def gqa_alloc_cache(model: GqaModel, layer: int, batch: int, t_cap: int, device="cuda"):
     """(codes uint8 [B, n_kv, T_cap, stride], scales f32 [B, n_kv, T_cap]) of one anchor."""
     cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
@@ -407,12 +468,18 @@ def gqa_quantize_write(model: GqaModel, layer: int, k: torch.Tensor, v: torch.Te
                        stream=None):
     """Quantize K and V source rows [n_src, n_kv, d_head] into anchor `layer` at
     slots dst_slot (seq * t_cap + position, int64)."""
-    assert k.shape == v.shape and k.dtype == v.dtype and k.is_contiguous() and v.is_contiguous()
-    assert tuple(k.shape[1:]) == (model.n_kv_heads, model.d_head)
-    assert dst_slot.dtype == torch.int64 and dst_slot.is_contiguous()
+    _tensor(k, "k")
+    _tensor(v, "v", k.dtype)
+    _require(k.shape == v.shape and k.dim() == 3 and tuple(k.shape[1:]) == (model.n_kv_heads, model.d_head),
+             "k and v must be [n_src, n_kv_heads, d_head]")
+    _tensor(dst_slot, "dst_slot", torch.int64)
     if src_index is not None:
-        assert src_index.dtype == torch.int32 and src_index.is_contiguous() and src_index.numel() == dst_slot.numel()
+        _tensor(src_index, "src_index", torch.int32)
+        _require(src_index.numel() == dst_slot.numel(), "src_index and dst_slot must have one entry per token")
+    _tensor(scales, "scales", torch.float32)
+    _require(scales.dim() == 3 and scales.shape[1] == model.n_kv_heads, "scales must be [batch, n_kv_heads, t_cap]")
     batch, _, t_cap = scales.shape
+    _check_gqa_cache(model, layer, codes, scales, batch, t_cap)
     st = lib().kk_gqa_quantize_write(model.cfg, layer, _ptr(k), _ptr(v), _dtype_code(k.dtype), k.shape[0],
                                      dst_slot.numel(), _ptr(src_index), _ptr(dst_slot),
                                      Cache(codes.data_ptr(), scales.data_ptr()), batch, t_cap, _stream(stream))
@@ -429,7 +496,9 @@ class GqaDecoder:
         self.caches = caches
         self._ctab = (Cache * model.n_layers)()
         for l in model.anchors():
+            _require(l in caches, f"no cache for anchor layer {l}")
             c, s = caches[l]
+            _check_gqa_cache(model, l, c, s, batch, t_cap)
             self._ctab[l] = Cache(c.data_ptr(), s.data_ptr())
         self.out = torch.empty(model.n_layers, batch, model.n_q_heads, model.d_head, dtype=torch.float32,
                                device=device)
@@ -437,12 +506,14 @@ class GqaDecoder:
         _check(lib().kk_gqa_decode_workspace_bytes(model.cfg, batch, max_seq_len, split_tokens, ctypes.byref(wb)),
                "kk_gqa_decode_workspace_bytes")
         self.ws_bytes = wb.value
-        self.workspace = torch.empty(max(self.ws_bytes, 256) // 4 + 64, dtype=torch.float32, device=device)
+        self.workspace = _workspace(self.ws_bytes, device)
 
     def __call__(self, q: torch.Tensor, seq_lens: torch.Tensor, stream=None):
         m = self.model
-        assert q.is_contiguous() and tuple(q.shape) == (m.n_layers, self.batch, m.n_q_heads, m.d_head)
-        assert seq_lens.dtype == torch.int32 and seq_lens.is_cuda and seq_lens.numel() == self.batch
+        _tensor(q, "q")
+        _require(tuple(q.shape) == (m.n_layers, self.batch, m.n_q_heads, m.d_head),
+                 "q must be [n_layers, batch, n_q_heads, d_head]")
+        _check_lens(seq_lens, self.batch)
         wptr = (self.workspace.data_ptr() + 255) // 256 * 256
         st = lib().kk_gqa_decode_attn(m.cfg, self._ctab, self.batch, self.t_cap, _ptr(seq_lens), self.max_seq_len,
                                       _ptr(q), _dtype_code(q.dtype), _ptr(self.out), self.split_tokens,

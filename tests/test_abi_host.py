@@ -53,6 +53,21 @@ def test_missing_library_fails_loudly(kk, monkeypatch):
         kk.kk.lib()
 
 
+def test_binding_refuses_host_tensors(kk):
+    """The binding takes device tensors only: a host tensor is refused with
+    ValueError before anything reaches the library (no CPU path)."""
+    import torch
+    m = kk.Model([kk.LayerSpec(0, 64, 8, 0.1)], 4, 64, 16)
+    lat, rope = torch.zeros(8, 64), torch.zeros(8, 16)
+    slots = torch.arange(8, dtype=torch.int64)
+    codes, scales = torch.zeros(2, 64, 80, dtype=torch.uint8), torch.zeros(2, 64)
+    with pytest.raises(ValueError, match="device tensor"):
+        kk.quantize_write(m, 0, lat, rope, codes, scales, slots)
+    g = kk.GqaModel([kk.LayerSpec(0, 0, 8, 0.1)], 4, 2, 64)
+    with pytest.raises(ValueError, match="device tensor"):
+        kk.gqa_quantize_write(g, 0, torch.zeros(8, 2, 64), torch.zeros(8, 2, 64), codes, scales, slots)
+
+
 @pytest.mark.parametrize("d,dr,bits", [(512, 64, 2), (512, 64, 4), (512, 64, 8), (512, 64, 16), (256, 64, 4),
                                        (32, 16, 8), (64, 16, 2), (96, 32, 2), (160, 64, 4), (16, 16, 2)])
 def test_row_stride_matches_oracle_layout(kk, d, dr, bits):
