@@ -361,7 +361,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16",
+        # the arithmetic of the step: fp16 P.V (the Q.K products are exact int8 x int8), bf16 epilogue
+        "dtype": "bf16" if args.epilogue else "f16",
         "data": "synthetic",
         "config": {"workload": name, "layers": w.n_layers, "heads": w.n_q_heads if args.gqa else w.n_heads,
                    "batch": batch, "cached_tokens": w.seq_len,
@@ -374,7 +375,7 @@ def main():
                             "latent epilogue (W_UV per head, W_O; d_v 128, d_model 5120)" if args.epilogue else
                             "append + decode" if args.append else
                             "heterogeneous decode (4 tables x 8 sequences)" if args.hetero else "decode")},
-        "roofline": {"bound": "hbm", "kernel": "epilogue: gemm_kernel (W_UV) + gemm_kernel (W_O)" if args.epilogue else
+        "roofline": {"bound": "hbm", "kernel": "epilogue: gemm_kernel (W_UV) + gemm_lds_kernel (W_O)" if args.epilogue else
                      ("append_kernel + " if args.append else
                                                 "store_kernel (plan upload) + " if args.hetero else "") +
                      "decode step: decode_kernel + merge_kernel",
