@@ -24,7 +24,7 @@ the picx.dev whiteboard summary, is the only one with method detail):
 * Decode reads the whole cache of every layer at every generated token
   (section "Background: The KV Cache Bottleneck").
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 
 * One scale covers the concatenation [c[:d] || k^R] of one anchor layer for
   one token; scale = amax / qmax in IEEE fp32 division, qmax = 2^(b-1) - 1,

@@ -1,6 +1,6 @@
 """Seeded generators and workload descriptions.
 
-Distributions (the workload recipe; see DESIGN.md "Input recipe"):
+Distributions (the workload recipe):
   * latent c^KV coordinate i (0-based) ~ N(0, variance 1 / (1 + i / 8)),
   * RoPE key k^R ~ N(0, 1),
   * q_lat, q_rope ~ N(0, 1); float32 in the tiny workload, rounded to bf16
