@@ -191,6 +191,36 @@ def test_many_heads_row_chunks(kk, heads):
     print(f"heads {heads}: worst err ratio {worst:.2e}")
 
 
+def limits_table():
+    """64 layers (the table limit) in four anchor groups of 20, 11, 10 and 23
+    layers; widths 448 and 256 with d_R = 128, so K = 576 (the K limit) for
+    the wide anchors; every bit width."""
+    table = [[0, 448, 4]] + [[0, 0, 0]] * 19
+    table += [[20, 448, 16]] + [[20, 0, 0]] * 10
+    table += [[31, 256, 2]] + [[31, 0, 0]] * 9
+    table += [[41, 448, 8]] + [[41, 0, 0]] * 22
+    assert len(table) == 64
+    return table
+
+
+@pytest.mark.parametrize("heads", [1, 3])
+def test_limits_64_layers_rope_128_k_576(kk, heads):
+    """The largest table and RoPE width: 64 layers, d_R = 128 with d = 448
+    (K = 576), r = 512 > d; one or three heads, so that a group's inheriting
+    layers fill 48-row chunks across layer boundaries (1 head: 20 layers in one
+    chunk; 3 heads: 69 rows of the last group in chunks of 48 + 21)."""
+    table = limits_table()
+    w = synth.small_workload(19, len(table), heads, 2, 100, 512, 128, table)
+    lens = [100, 33]
+    model, caches, dec, ql, qr = run_gpu(kk, w, seq_lens=lens, t_cap=128)
+    worst = 0.0
+    for s in range(w.batch):
+        src = {a: source_cpu(w, a, s) for a in w.anchors()}
+        for l in range(w.n_layers):
+            worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, lens[s], src))
+    print(f"limits, {heads} heads: worst err ratio {worst:.2e}")
+
+
 def test_softmax_scale_sign_zero_and_extremes(kk):
     """Per-layer softmax scales that are negative (the logits flip sign), zero
     (uniform weights), tiny, and large (close to an argmax), on ragged lengths
