@@ -38,6 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
+PEAK_MFMA_F16_TFLOPS = 2500.0     # dense fp16/bf16 MFMA, MI355X
 
 
 def algorithmic_bytes(kk, w):
@@ -144,6 +145,38 @@ def traffic_from(fetch_csv, write_csv, copy_mib, workload_name):
     return rec
 
 
+def copy_bandwidth(torch, mib: int = 1024, reps: int = 5) -> float:
+    """Measured device-to-device copy rate (GB/s, bytes read + written) on the
+    launch stream: the practical streaming ceiling the achieved rate is set
+    against besides the 8 TB/s peak."""
+    n = mib * 2 ** 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del src, dst
+    return 2 * n / (ms * 1e-3) / 1e9
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:                                      # pragma: no cover
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s: float):
     """The oracle (unchanged) on the host cores: decode of whole (layer, sequence)
     pairs of the same workload until the time budget is used."""
@@ -157,7 +190,8 @@ def cpu_baseline(w, budget_s: float):
     except Exception:                                    # pragma: no cover
         cores = os.cpu_count() or 1
     ql, qr = synth.queries(w, "cuda")
-    done, spent = 0, 0.0
+    done, spent, nbytes = 0, 0.0, 0
+    qsize = 4 if str(w.q_dtype) == "torch.float32" else 2
     pairs = [(l, s) for s in range(w.batch) for l in range(w.n_layers)]
     cache = {}
     for (l, s) in pairs:
@@ -176,9 +210,12 @@ def cpu_baseline(w, budget_s: float):
                         w.seq_len)
         spent += time.perf_counter() - t0
         done += 1
+        d = w.d_eff(l)
+        nbytes += (packed.nbytes + scales.nbytes + w.n_heads * (d + w.d_rope) * qsize + w.n_heads * d * 4)
         if spent >= budget_s:
             break
     return {"value": done / spent, "unit": "layer*tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "effective_gbps": nbytes / spent / 1e9,
             "sample": f"{done} (layer, sequence) decodes of the same workload (unpack, dequantize, fp64 attention "
                       f"over {w.seq_len} tokens, {w.n_heads} heads), {spent:.1f} s of CPU time"}
 
@@ -312,6 +349,8 @@ def main():
     mean_dev_ms = sum(dev_ms) / len(dev_ms)
     ms_per_step = wall * 1000.0 / args.steps
 
+    # (not in the counter runs, whose only large copies are the calibration ones)
+    copy_gbps = copy_bandwidth(torch) if args.calibration_copy_mib == 0 else None
     if args.calibration_copy_mib > 0:
         n = args.calibration_copy_mib * 2 ** 20
         src = torch.empty(n, dtype=torch.uint8, device="cuda")
@@ -382,7 +421,11 @@ def main():
                      "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_step": U, "device_ms_per_step": mean_dev_ms,
-                     "useful_tflops": flops / (mean_dev_ms * 1e-3) / 1e12},
+                     "device_ms_p10_p50_p90": [dev_ms[len(dev_ms) // 10], dev_ms[len(dev_ms) // 2],
+                                               dev_ms[(9 * len(dev_ms)) // 10]],
+                     "copy_gbps_measured": copy_gbps, "frac_of_copy": achieved / copy_gbps if copy_gbps else None,
+                     "useful_tflops": flops / (mean_dev_ms * 1e-3) / 1e12,
+                     "mfma_util_vs_2500_tflops": flops / (mean_dev_ms * 1e-3) / 1e12 / PEAK_MFMA_F16_TFLOPS},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
