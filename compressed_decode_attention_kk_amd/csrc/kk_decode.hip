@@ -1001,36 +1001,51 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs) {
     }
   }
   __syncthreads();
-  const int d4 = d >> 2;
-  // Each thread merges 4 output vectors at once: all partial loads of a split
-  // are issued before any store (the stores could alias them for the compiler).
-  constexpr int kMergeVec = 4;
-  const int total = nrows * d4;
+  // Each thread merges two 8-feature vectors per pass (16-byte loads) and
+  // issues the loads of kSplitBatch splits before using any of them; every
+  // output still sums its splits in order k = 0 .. S-1.
+  const int d8 = d >> 3;
+  constexpr int kMergeVec = 2;
+  constexpr int kSplitBatch = 4;
+  const int total = nrows * d8;
   for (int i0 = threadIdx.x; i0 < total; i0 += kMergeVec * 256) {
     int rl[kMergeVec], f[kMergeVec];
-    f4 acc[kMergeVec];
+    f4 acc[kMergeVec][2];
 #pragma unroll
     for (int j = 0; j < kMergeVec; ++j) {
       const int idx = min(i0 + 256 * j, total - 1);
-      rl[j] = idx / d4;
-      f[j] = (idx - rl[j] * d4) * 4;
-      acc[j] = f4{0.f, 0.f, 0.f, 0.f};
+      rl[j] = idx / d8;
+      f[j] = (idx - rl[j] * d8) * 8;
+      acc[j][0] = acc[j][1] = f4{0.f, 0.f, 0.f, 0.f};
     }
-    for (int k = 0; k < S; ++k) {
-      const _Float16* pk = (const _Float16*)(base + k * kstride);
-      h4 h[kMergeVec];
+    for (int k0 = 0; k0 < S; k0 += kSplitBatch) {
+      h8 h[kSplitBatch][kMergeVec];
 #pragma unroll
-      for (int j = 0; j < kMergeVec; ++j) h[j] = *(const h4*)(pk + (int64_t)rl[j] * d + f[j]);
+      for (int kb = 0; kb < kSplitBatch; ++kb) {
+        const _Float16* pk = (const _Float16*)(base + min(k0 + kb, S - 1) * kstride);
 #pragma unroll
-      for (int j = 0; j < kMergeVec; ++j)
-        acc[j] += f4{(float)h[j][0], (float)h[j][1], (float)h[j][2], (float)h[j][3]} * wgt[k][rl[j]];
+        for (int j = 0; j < kMergeVec; ++j) h[kb][j] = *(const h8*)(pk + (int64_t)rl[j] * d + f[j]);
+      }
+#pragma unroll
+      for (int kb = 0; kb < kSplitBatch; ++kb) {
+        if (k0 + kb < S) {
+#pragma unroll
+          for (int j = 0; j < kMergeVec; ++j) {
+            const float wk = wgt[k0 + kb][rl[j]];
+            acc[j][0] += f4{(float)h[kb][j][0], (float)h[kb][j][1], (float)h[kb][j][2], (float)h[kb][j][3]} * wk;
+            acc[j][1] += f4{(float)h[kb][j][4], (float)h[kb][j][5], (float)h[kb][j][6], (float)h[kb][j][7]} * wk;
+          }
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < kMergeVec; ++j) {
       if (i0 + 256 * j < total) {
         const int gr = r0 + rl[j];
         const int layer = group_layer_at(A, E.lay_begin + gr / A.heads), head = gr % A.heads;
-        *(f4*)(A.out + layer_at(A, layer).out_off + ((int64_t)s * A.heads + head) * d + f[j]) = acc[j];
+        float* dst = A.out + layer_at(A, layer).out_off + ((int64_t)s * A.heads + head) * d + f[j];
+        *(f4*)dst = acc[j][0];
+        *(f4*)(dst + 4) = acc[j][1];
       }
     }
   }
