@@ -11,7 +11,8 @@
 //
 // Work item = (chunk of <= 16*RB query rows of one anchor group, sequence,
 // token split).  A workgroup of 4 waves processes one item in tiles of 32
-// tokens (16 for b = 16), two workgroups per CU:
+// tokens (16 for b = 16), two to four workgroups per CU (by the register budget
+// of the kernel variant):
 //   1. the tile's packed rows and scales are copied HBM -> LDS with direct
 //      loads (global_load_lds), several tiles ahead (explicit vmcnt waits);
 //   2. Q.K on the integer MFMA: wave w < RB owns query rows 16w..16w+15.  The
