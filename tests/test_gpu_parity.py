@@ -221,6 +221,22 @@ def test_limits_64_layers_rope_128_k_576(kk, heads):
     print(f"limits, {heads} heads: worst err ratio {worst:.2e}")
 
 
+def test_fp32_queries_at_full_k(kk):
+    """fp32 queries (every chunk's query loaded in one round trip) at the
+    largest K = 512 + 64 with 40 heads (three row blocks), every bit width,
+    an inheriting layer; ragged lengths."""
+    table = [[0, 512, 16], [1, 512, 8], [2, 448, 4], [2, 0, 0], [4, 512, 2]]
+    w = synth.small_workload(21, len(table), 40, 2, 200, 512, 64, table, q_dtype=torch.float32)
+    lens = [200, 45]
+    model, caches, dec, ql, qr = run_gpu(kk, w, seq_lens=lens, t_cap=224)
+    worst = 0.0
+    for s in range(w.batch):
+        src = {a: source_cpu(w, a, s) for a in w.anchors()}
+        for l in range(w.n_layers):
+            worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, lens[s], src))
+    print(f"fp32 queries, K = 576: worst err ratio {worst:.2e}")
+
+
 def test_softmax_scale_sign_zero_and_extremes(kk):
     """Per-layer softmax scales that are negative (the logits flip sign), zero
     (uniform weights), tiny, and large (close to an argmax), on ragged lengths
