@@ -237,6 +237,25 @@ def test_fp32_queries_at_full_k(kk):
     print(f"fp32 queries, K = 576: worst err ratio {worst:.2e}")
 
 
+def test_most_splits_per_sequence(kk):
+    """Two long sequences and few rows: the planner cuts each sequence into
+    the most splits it allows (64, checked through the workspace size), so the
+    merge combines 64 partials per output; the second length is ragged."""
+    table = [[0, 64, 4], [1, 32, 8]]
+    w = synth.small_workload(22, len(table), 4, 2, 16384, 64, 16, table)
+    lens = [16384, 9001]
+    model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+    slot_bytes = lambda d: (32 * d + 192) * 4       # fp16 O/l of 64 rows, then m, l and the unit
+    assert kk.workspace_bytes(model, w.batch, 16384) == 64 * w.batch * (slot_bytes(64) + slot_bytes(32))
+    model, caches, dec, ql, qr = run_gpu(kk, w, seq_lens=lens)
+    worst = 0.0
+    for s in range(w.batch):
+        src = {a: source_cpu(w, a, s) for a in w.anchors()}
+        for l in range(w.n_layers):
+            worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, lens[s], src))
+    print(f"64 splits: worst err ratio {worst:.2e}")
+
+
 def test_softmax_scale_sign_zero_and_extremes(kk):
     """Per-layer softmax scales that are negative (the logits flip sign), zero
     (uniform weights), tiny, and large (close to an argmax), on ragged lengths
