@@ -126,7 +126,9 @@ def traffic_from(fetch_csv, write_csv, copy_mib, workload_name):
     out = {}
     for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
         rows = _counter_rows(path, name)
-        copies = [v for k, v in rows if COPY_KERNEL in k and v * 1024 > 0.5 * copy_mib * 2 ** 20]
+        # the calibration copies: FETCH_SIZE counts about half of a copy's
+        # bytes here, so the cut sits well below that (smaller copies stay out)
+        copies = [v for k, v in rows if COPY_KERNEL in k and v * 1024 > 0.25 * copy_mib * 2 ** 20]
         if not copies:
             raise SystemExit(f"no calibration copy dispatch found in {path}")
         factor = copy_mib * 2 ** 20 / (sum(copies) / len(copies) * 1024)
