@@ -100,11 +100,11 @@ template <int BB>
 __global__ void __launch_bounds__(256) gemm_kernel(EpiArgs) {
   KEpi& A = *(KEpi*)(__builtin_amdgcn_kernarg_segment_ptr());
   const int lane = threadIdx.x & 63;
-  // XCD-aware numbering: blocks are dealt round-robin to the 8 XCDs, so
-  // logical block (b % 8) * (grid / 8) + b / 8 gives each XCD a contiguous run
-  // of problems, whose activations then stay in that XCD's L2 (grid % 8 == 0).
-  const int per_xcd = gridDim.x >> 3;
-  const int lblock = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  // Blocks in launch order: the hardware deals them round-robin to the 8
+  // XCDs, which spreads the layers (whose cost grows with their width d)
+  // evenly; a head's activations are read only by its own workgroup, so a
+  // contiguous run of layers per XCD would buy no L2 reuse, only imbalance.
+  const int lblock = blockIdx.x;
   const int wave = lblock * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   if (wave >= A.total_waves) return;
   KProb& P = A.p[find_problem(A, wave)];
@@ -226,7 +226,11 @@ __global__ void __launch_bounds__(256) gemm_lds_kernel(EpiArgs) {
   extern __shared__ __attribute__((aligned(16))) char lds[];
   KEpi& A = *(KEpi*)(__builtin_amdgcn_kernarg_segment_ptr());
   const int per_xcd = gridDim.x >> 3;
-  const int lblock = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);   // XCD-aware (see gemm_kernel)
+  // XCD-aware numbering: blocks are dealt round-robin to the 8 XCDs, so
+  // logical block (b % 8) * (grid / 8) + b / 8 gives each XCD a contiguous run
+  // of workgroups of one layer, whose activations then stay in that XCD's L2
+  // (every layer costs the same here: K = n_heads * d_v).
+  const int lblock = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (lblock >= A.total_waves) return;                      // here total_waves counts workgroups
   KProb& P = A.p[find_problem(A, lblock)];
   const int local = lblock - P.wave_base;
@@ -330,7 +334,7 @@ hipError_t launch_epilogue_gemm_wide(const EpiArgs& a, hipStream_t stream) {
 hipError_t launch_epilogue_gemm(const EpiArgs& a, hipStream_t stream) {
   static_assert(sizeof(EpiArgs) < 7600, "kernel argument block too large");
   if (a.total_waves <= 0) return hipSuccess;
-  const int blocks = ((a.total_waves + 3) / 4 + 7) / 8 * 8;     // a multiple of the 8 XCDs
+  const int blocks = (a.total_waves + 3) / 4;
   const int bb = a.batch >= 64 ? 4 : (a.batch + 15) / 16;
   switch (bb) {
     case 1: hipLaunchKernelGGL(gemm_kernel<1>, dim3(blocks), dim3(256), 0, stream, a); break;
