@@ -145,6 +145,87 @@ def test_quantizer_zero_token():
 
 
 # ----------------------------------------------------------------------------
+# rank axis: the cache keeps the FIRST d of the r latent coordinates
+# ----------------------------------------------------------------------------
+
+def _rank_pin_failures(write, lat, rope, d, bits):
+    """Checks of a cache writer against the rank item of "Three Non-Eviction
+    Compression Axes" (keep the first d latent coordinates, then the RoPE
+    key), stated without the oracle: the reconstruction bound element by
+    element against [lat[:, :d] || rope], the scale as fl32(amax / qmax)
+    over exactly those values (exact rationals), invariance under any change
+    of the dropped coordinates d..r-1, and sensitivity to every kept one.
+    Returns the list of failed checks (empty: the writer passes)."""
+    fails = []
+    n, dr = rope.shape
+    qm = (1 << (bits - 1)) - 1
+    packed, scales, codes = write(lat, rope, d, bits)
+    if codes.shape != (n, d + dr):
+        return ["shape"]
+    v = np.concatenate([lat[:, :d], rope], axis=1).astype(np.float64)
+    xhat = codes.astype(np.float64) * scales.astype(np.float64)[:, None]
+    if not np.all(np.abs(v - xhat) <= scales.astype(np.float64)[:, None] / 2 + np.abs(v) * 2.0 ** -23):
+        fails.append("reconstruction")
+    for i in range(0, n, max(1, n // 8)):
+        amax = max(abs(Fraction(float(x))) for x in v[i])
+        if scales[i] != f32_round(amax / qm):
+            fails.append("scale")
+            break
+    bumped = lat.copy()
+    bumped[:, d:] = 1e6 * np.sign(RNG.standard_normal(bumped[:, d:].shape)).astype(np.float32)
+    p2, s2, _ = write(bumped, rope, d, bits)
+    if not (np.array_equal(p2, packed) and np.array_equal(s2.view(np.uint32), scales.view(np.uint32))):
+        fails.append("dropped coordinates matter")
+    for j in (0, d // 2, d - 1):
+        moved = lat.copy()
+        moved[:, j] = 3.0 * np.abs(lat).max() + 1.0
+        p3, _, _ = write(moved, rope, d, bits)
+        if np.array_equal(p3, packed):
+            fails.append(f"kept coordinate {j} ignored")
+    return fails
+
+
+def _rank_pin_inputs(n=64, r=64, dr=16):
+    rng = np.random.default_rng(77)
+    lat = (rng.standard_normal((n, r)) / np.sqrt(1 + np.arange(r) / 8)).astype(np.float32)
+    rope = rng.standard_normal((n, dr)).astype(np.float32)
+    return lat, rope
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8, 16])
+@pytest.mark.parametrize("d", [16, 32, 48])
+def test_write_cache_keeps_first_d_latent_coordinates(bits, d):
+    lat, rope = _rank_pin_inputs()
+    # the largest value of every row sits just past the kept width: a writer
+    # that kept one coordinate too many would take its scale from it
+    lat[:, d] = 10.0 * np.abs(lat).max(axis=1)
+    assert _rank_pin_failures(ko.write_cache, lat, rope, d, bits) == []
+
+
+@pytest.mark.parametrize("bits", [8, 16])
+def test_rank_pin_rejects_wrong_latent_slices(bits):
+    # planted mistakes (writers built from the oracle's quantizer and packer
+    # with a wrong slice of the latent): the pin above must reject each one
+    def writer(select):
+        def w(latent, rope, d, b):
+            v = np.concatenate([select(np.asarray(latent, np.float32), d), np.asarray(rope, np.float32)], axis=1)
+            codes, scales = ko.quantize_rows(v, b)
+            return ko.pack_rows(codes, b), scales, codes
+        return w
+    mutants = {
+        "shifted by one": lambda x, d: x[:, 1:d + 1],
+        "last d": lambda x, d: x[:, x.shape[1] - d:],
+        "reversed": lambda x, d: x[:, d - 1::-1],
+        "every other": lambda x, d: x[:, 0:2 * d:2],
+    }
+    lat, rope = _rank_pin_inputs()
+    d = 32
+    assert _rank_pin_failures(writer(lambda x, d: x[:, :d]), lat, rope, d, bits) == []
+    for name, sel in mutants.items():
+        assert _rank_pin_failures(writer(sel), lat, rope, d, bits), name
+
+
+# ----------------------------------------------------------------------------
 # packing
 # ----------------------------------------------------------------------------
 
