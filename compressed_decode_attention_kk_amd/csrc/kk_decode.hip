@@ -76,9 +76,10 @@ __device__ inline int group_layer_at(KArgs& A, int i) {
 }
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kQFrac = 13;           // query fixed point: |q'| < 1 -> |q'| * 2^13 <= 8192
+constexpr float kQMax = 16256.0f;    // latent query fixed point: |q'| <= 127 * 128, two int8 limbs
+constexpr float kQMaxRope = 16256.0f * 128.0f;   // RoPE query: |q'| <= 127 * 128^2, three int8 limbs
+constexpr int kMaxRopeChunks = 2;    // d_R <= 128
 constexpr int kScaleHeadroom = 6;    // scales may exceed 2^E by 2^6 before E is raised
-constexpr int kMaxChunks64 = (kMaxK + 63) / 64;
 // Copy instructions (1 KB each) per tile: a tile holds at most 32 * K bytes of
 // codes (32 tokens of 8-bit codes or 16 tokens of 16-bit codes), shared
 // round-robin by the waves, so each wave issues at most kCopyRounds of them.
@@ -93,15 +94,21 @@ constexpr int kMiscBytes = 2 * 64 * 4 + 2 * 4 * 4 + 64 * 8 + 64;
 __host__ __device__ inline int pbuf_bytes(int rb, int tile_blocks) { return 2 * rb * 64 * 8 * tile_blocks; }
 
 __host__ __device__ inline int nseg_of(int row_stride) { return row_stride >> 4; }
-__host__ __device__ inline int chunks64_of(int K) { return (K + 63) >> 6; }
-// 16-byte segments read by the Q.K chunks (whole 64-feature chunks)
-__host__ __device__ inline int nsegpad_of(int K, int bits) { return (chunks64_of(K) * bits + 1) >> 1; }
+// 16-byte segments a tile row needs for the Q.K reads: latent chunks read 64
+// fields from field 0, RoPE chunks 64 fields from field d, so reads reach field
+// F = max(64 * latent chunks, d + 64 * RoPE chunks) (past the row's own fields
+// they meet zero query values); b = 16 reads both byte planes (low plane at K).
+__host__ __device__ inline int nsegpad_of(int d, int d_rope, int bits) {
+  const int fl = ((d + 63) >> 6) * 64, fr = d + ((d_rope + 63) >> 6) * 64;
+  const int F = fl > fr ? fl : fr;
+  return bits == 16 ? (d + d_rope + F + 15) >> 4 : (F * bits / 8 + 15) >> 4;
+}
 // 16-token blocks per tile (see tile_blocks below)
 __host__ __device__ inline int tile_blocks_of(int bits) { return bits == 16 ? 1 : 2; }
 // Tile buffer: all but the last token block at full pitch, the last one padded
 // for whole-chunk Q.K reads, then the tile's fp32 scales (4 bytes per token).
-__host__ __device__ inline int tilebuf_bytes(int row_stride, int K, int bits) {
-  const int nseg = nseg_of(row_stride), pad = nsegpad_of(K, bits), tb = tile_blocks_of(bits);
+__host__ __device__ inline int tilebuf_bytes(int row_stride, int d, int d_rope, int bits) {
+  const int nseg = nseg_of(row_stride), pad = nsegpad_of(d, d_rope, bits), tb = tile_blocks_of(bits);
   return ((tb - 1) * nseg + (pad > nseg ? pad : nseg)) * 256 + 64 * tb;
 }
 
@@ -293,7 +300,7 @@ static_assert(tile_blocks<16>() == 1 && tile_blocks<8>() == 2, "tile_blocks and 
 // CU).  Lean and grouped-query rows have at most 8 and 4 output units.  (A
 // lean 3-row-block item spills: it is left to the full variant.)
 template <int RB, int V>
-constexpr int qk_units_max() { return V == kGqa ? 1 : V == kLean ? 2 : 3; }
+constexpr int qk_units_max() { return V == kGqa ? 1 : V == kLean ? 1 : 3; }
 template <int RB, int V>
 constexpr int pv_units_max() { return V == kGqa ? 2 : V == kLean ? 4 : RB == 3 ? 7 : 5; }
 // 64-field chunks of a row that enter Q.K
@@ -325,9 +332,13 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   constexpr int TILE = 16 * TB;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int g = lane >> 4, n = lane & 15;
-  const int d = E.d, K = d + A.d_rope, KC = chunks64_of(K);
+  const int d = E.d, K = d + A.d_rope;
+  // Q.K chunks: NRq RoPE chunks (three query limbs, fields from d), then NLq
+  // latent chunks (two query limbs, fields from 0).  Grouped-query rows [V || K]
+  // have one part only, the keys: two-limb chunks from field d.
+  const int NRq = GQA ? 0 : (A.d_rope + 63) >> 6, NLq = GQA ? (A.d_rope + 63) >> 6 : (d + 63) >> 6, KC = NLq + NRq;
   const int NSEG = nseg_of(E.row_stride), PITCH = NSEG * 256;
-  const int bufbytes = tilebuf_bytes(E.row_stride, K, BITS);
+  const int bufbytes = tilebuf_bytes(E.row_stride, d, A.d_rope, BITS);
   const int nbuf = E.nbuf;                    // >= 3 tile buffers
   constexpr int PSLOT = 8 * TB;               // P' bytes per lane and row block
   constexpr int PPAR = RB * 64 * PSLOT;       // P' bytes per tile parity
@@ -374,11 +385,16 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
     const int tok0 = it * TILE;
     const int tlast = min(TILE, ntok - tok0) - 1;
     const void* tbase = item_codes + (int64_t)tok0 * rstride;
+    // the per-copy lane offsets are recomputed at each issue (a few VALU ops)
+    // rather than hoisted out of the stage loop, where they would hold
+    // registers for the whole loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int k = 0; k < kCopyRounds; ++k) {       // straight-line: one exit branch, not a loop
       const int i = wave_u + kWaves * k;
       if (i >= ninst) break;
-      const int p = i * 64 + lane;
+      const int p = i * 64 + ln;
       const int tb = (TB == 2 && p >= block_pieces) ? 1 : 0;
       const int rem = p - tb * block_pieces;
       const int seg = rem >> 4, slot = rem & 15;
@@ -427,12 +443,21 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
     constexpr bool QKW = decltype(qkw_tag)::value;
     constexpr int UMAX = decltype(umax_tag)::value;
     const int my_row = 16 * wave + n;
+    const int rope_field0 = d + 16 * g;           // first RoPE field of this lane's Q.K features
+    const int lat_field0 = (GQA ? d : 0) + 16 * g;  // first field of its two-limb chunks
 
-    // ---- q as two int8 limbs of a 14-bit fixed-point number per row ------------------
-    // chunk c, lane (g, n): row 16*wave + n, features 64c + 16g + qk_slot_feature(i).
-    i4 qh[QKW ? kMaxC : 1], ql[QKW ? kMaxC : 1];
-    float rowf = 1.0f;
-    int qbias = 0;
+    // ---- q as int8 limbs of a fixed-point number per row and part -------------------
+    // Q.K chunk c < NRq covers RoPE features 64c + 16g + qk_slot_feature(i) (q = 0
+    // past d_R), read from the row at field d + 64c + ...; chunk NRq + c' covers
+    // latent features 64c' + 16g + ... (q = 0 at and past d).  The two parts of a
+    // row each get their own prescale: the latent part is a 15-bit number (two
+    // limbs), the RoPE part a 22-bit one (three limbs: hi, mid, lo), so that a
+    // RoPE query far larger than the latent one (or the reverse) keeps its
+    // logits accurate.  The integer scores of the parts are joined in fp32
+    // (S = S_lat + ratio * S_rope, in units of the latent prescale).
+    i4 qh[QKW ? kMaxC : 1], ql[QKW ? kMaxC : 1], qm[QKW ? kMaxRopeChunks : 1];
+    float rowf = 1.0f, ratio = 0.0f;
+    int qbiasL = 0, qbiasR = 0;
     if constexpr (QKW) {
       int my_layer = -1, my_head = 0;
       if (my_row < nrows) {
@@ -440,94 +465,115 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
         my_layer = group_layer_at(A, E.lay_begin + gr / A.heads);
         my_head = gr % A.heads;
       }
-      int qsum = 0;                               // sum of the fixed-point q of this row
-      float qv[kMaxC][16];
-      float mx = 0.0f;
       // The loads of every chunk are issued before any of them is used, so the
-      // query costs one memory round trip: a chunk outside the row or past K
-      // reads the (valid) first query element and is zeroed afterwards.
+      // query costs one memory round trip: a chunk outside the row or past the
+      // part's width reads the (valid) first query element and is zeroed afterwards.
       const bool row_ok = my_layer >= 0;
       const int64_t qrow =
           row_ok ? ((int64_t)(my_layer - E.layer_base) * A.batch + E.seq_base + s) * A.heads + my_head : 0;
-      bool ok[kMaxC];
+      bool ok[kMaxC], lat[kMaxC];
       int64_t off[kMaxC];
-      bool lat[kMaxC];
 #pragma unroll
       for (int c = 0; c < kMaxC; ++c) {
-        const int f0 = 64 * c + 16 * g;
-        ok[c] = row_ok && f0 < K && (!GQA || c >= E.qk_c0);   // grouped-query: value chunks hold no keys
-        lat[c] = !ok[c] || f0 < d;
-        off[c] = !ok[c] ? 0 : f0 < d ? qrow * A.r + f0 : qrow * A.d_rope + (f0 - d);
+        lat[c] = c >= NRq;
+        const int f0 = lat[c] ? 64 * (c - NRq) + 16 * g : 64 * c + 16 * g;
+        ok[c] = row_ok && c < KC && f0 < (lat[c] && !GQA ? d : A.d_rope);
+        off[c] = !ok[c] ? 0 : lat[c] && !GQA ? qrow * A.r + f0 : qrow * A.d_rope + f0;
       }
-      float x[kMaxC][16];
-      if (A.q_is_f32) {
-        f4 raw[kMaxC][4];
-#pragma unroll
-        for (int c = 0; c < kMaxC; ++c) {
-          const f4* p = (const f4*)((const float*)(lat[c] ? A.q_lat : A.q_rope) + off[c]);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) raw[c][v] = p[v];
-        }
-#pragma unroll
-        for (int c = 0; c < kMaxC; ++c)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[c][4 * v + i] = raw[c][v][i];
-      } else {
-        u4 raw[kMaxC][2];
-#pragma unroll
-        for (int c = 0; c < kMaxC; ++c) {
-          const u4* p = (const u4*)((const uint16_t*)(lat[c] ? A.q_lat : A.q_rope) + off[c]);
-#pragma unroll
-          for (int v = 0; v < 2; ++v) raw[c][v] = p[v];
-        }
-#pragma unroll
-        for (int c = 0; c < kMaxC; ++c)
-#pragma unroll
-          for (int v = 0; v < 2; ++v)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              x[c][8 * v + 2 * i] = __uint_as_float(raw[c][v][i] << 16);
-              x[c][8 * v + 2 * i + 1] = __uint_as_float(raw[c][v][i] & 0xFFFF0000u);
-            }
-      }
-#pragma unroll
-      for (int c = 0; c < kMaxC; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float xi = ok[c] ? x[c][qk_slot_feature<BITS>(i)] : 0.0f;
-          qv[c][i] = xi;
-          mx = fmaxf(mx, fabsf(xi));
-        }
-      mx = max_xor_16_32(mx);
-      int e = 0;
-      if (mx > 0.0f) (void)frexpf(mx, &e);          // mx * 2^-e in [0.5, 1)
-      // A negative softmax scale is carried by q (z = |scale| * (-q) . k), so the
-      // row factor below is positive, as the softmax needs.
+      // Two passes over the query: the part maxima, then the limbs.  bf16 queries
+      // are loaded once and kept packed (8 dwords per chunk); fp32 queries are
+      // loaded again for the second pass (a second round trip, which keeps 16
+      // floats per chunk out of the registers).  Each dtype has its own
+      // straight-line copy of the code.
       const float sm = my_layer >= 0 ? layer_at(A, my_layer).sm_scale : 0.0f;
-      const float pre = ldexpf(sm < 0.0f ? -1.0f : 1.0f, kQFrac - e);
+      float preL = 0.0f, preR = 0.0f, mxL = 0.0f, mxR = 0.0f;
+      int qsumL = 0, qsumR = 0;                   // sums of the fixed-point q per part
+      auto quantize = [&](auto f32_tag) {
+        constexpr bool F32 = decltype(f32_tag)::value;
+        u4 raw[F32 ? 1 : kMaxC][2];
+        auto get = [&](int c, float (&x)[16]) {
+          if constexpr (F32) {
+            const f4* p = (const f4*)((const float*)(lat[c] && !GQA ? A.q_lat : A.q_rope) + off[c]);
 #pragma unroll
-      for (int c = 0; c < kMaxC; ++c) {
-        uint32_t hw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
+            for (int v = 0; v < 4; ++v) {
+              const f4 t = p[v];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = (int)rintf(qv[c][i] * pre);    // |qi| <= 8192
-          const int hi = (qi + 64) >> 7;                // floor division, in [-64, 64]
-          const int lo = qi - (hi << 7);                // in [-64, 63]
-          qsum += qi;
-          hw[i >> 2] |= ((uint32_t)hi & 0xFFu) << (8 * (i & 3));
-          lw[i >> 2] |= ((uint32_t)lo & 0xFFu) << (8 * (i & 3));
+              for (int i = 0; i < 4; ++i) x[4 * v + i] = ok[c] ? t[i] : 0.0f;
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < 2; ++v)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                x[8 * v + 2 * i] = ok[c] ? __uint_as_float(raw[c][v][i] << 16) : 0.0f;
+                x[8 * v + 2 * i + 1] = ok[c] ? __uint_as_float(raw[c][v][i] & 0xFFFF0000u) : 0.0f;
+              }
+          }
+        };
+        if constexpr (!F32) {
+#pragma unroll
+          for (int c = 0; c < kMaxC; ++c) {
+            const u4* p = (const u4*)((const uint16_t*)(lat[c] && !GQA ? A.q_lat : A.q_rope) + off[c]);
+#pragma unroll
+            for (int v = 0; v < 2; ++v) raw[c][v] = p[v];
+          }
         }
-        qh[c] = i4{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3]};
-        ql[c] = i4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
-      }
-      qsum = isum_xor_16_32(qsum);
-      // rowf >= FLT_MIN: a zero scale (or a padding row, q = 0) still maps the
-      // masked tokens' t = -inf to z = -inf; its logits are then below 1e-29.
-      rowf = fmaxf(fabsf(sm) * kLog2e * ldexpf(qk_code_scale<BITS>(), e - kQFrac), FLT_MIN);
+#pragma unroll
+        for (int c = 0; c < kMaxC; ++c) {
+          float x[16];
+          get(c, x);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            if (lat[c]) mxL = fmaxf(mxL, fabsf(x[i]));
+            else mxR = fmaxf(mxR, fabsf(x[i]));
+          }
+        }
+        mxL = max_xor_16_32(mxL);
+        mxR = max_xor_16_32(mxR);
+        // A negative softmax scale is carried by q (z = |scale| * (-q) . k), so the
+        // row factor below is positive, as the softmax needs.
+        const float sgn = sm < 0.0f ? -1.0f : 1.0f;
+        preL = mxL > 0.0f ? sgn * (kQMax / mxL) : 0.0f;
+        preR = mxR > 0.0f ? sgn * (kQMaxRope / mxR) : 0.0f;
+#pragma unroll
+        for (int c = 0; c < kMaxC; ++c) {
+          float x[16];
+          get(c, x);
+          uint32_t hw[4] = {0, 0, 0, 0}, mw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
+          const float pre = lat[c] ? preL : preR;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            // latent: qi = 128 hi + lo, |qi| <= 16256; RoPE: qi = 16384 hi + 128 mid + lo,
+            // |qi| <= 16256 * 128 (floor divisions: hi in [-127, 127], mid in [-64, 64],
+            // lo in [-64, 63])
+            const int qi = (int)rintf(x[qk_slot_feature<BITS>(i)] * pre);
+            const int hi = lat[c] ? (qi + 64) >> 7 : (qi + 8192) >> 14;
+            const int rest = lat[c] ? 0 : qi - (hi << 14);
+            const int mid = (rest + 64) >> 7;
+            const int lo = lat[c] ? qi - (hi << 7) : rest - (mid << 7);
+            if (lat[c]) qsumL += qi; else qsumR += qi;
+            hw[i >> 2] |= ((uint32_t)hi & 0xFFu) << (8 * (i & 3));
+            mw[i >> 2] |= ((uint32_t)mid & 0xFFu) << (8 * (i & 3));
+            lw[i >> 2] |= ((uint32_t)lo & 0xFFu) << (8 * (i & 3));
+          }
+          qh[c] = i4{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3]};
+          ql[c] = i4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
+          if (c < kMaxRopeChunks) qm[c < kMaxRopeChunks ? c : 0] = i4{(int)mw[0], (int)mw[1], (int)mw[2], (int)mw[3]};
+        }
+      };
+      if (A.q_is_f32) quantize(std::true_type{});
+      else quantize(std::false_type{});
+      // scores are taken in units of the latent prescale (the RoPE one when the
+      // latent part is zero); rowf >= FLT_MIN: a zero scale (or a padding row,
+      // q = 0) still maps the masked tokens' t = -inf to z = -inf.
+      const float pref = fabsf(mxL > 0.0f ? preL : preR);
+      ratio = mxR > 0.0f ? fabsf(pref / preR) : 0.0f;
+      rowf = fmaxf(pref > 0.0f ? fabsf(sm) * kLog2e * qk_code_scale<BITS>() / pref : 0.0f, FLT_MIN);
       // b = 16: offset-binary bias of the low-byte operand (exact integer correction)
-      qbias = BITS == 16 ? 128 * qsum : 0;
+      if constexpr (BITS == 16) {
+        qbiasL = isum_xor_16_32(qsumL);
+        qbiasR = isum_xor_16_32(qsumR);
+      }
     }
 
     f4 oacc[UMAX][2][RB];
@@ -539,6 +585,13 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
         for (int rb = 0; rb < RB; ++rb) oacc[u][f][rb] = f4{0.f, 0.f, 0.f, 0.f};
 
     int slot_qk = 0, slot_pv = nbuf - 1, slot_issue = nbuf - 2;   // buffers of tiles st+1, st, st+nbuf-1
+    // The stage loop is instantiated for the common row shapes with the unit
+    // count UC and the chunk counts NC (NR of them RoPE) as compile-time
+    // constants, so that a stage is one block of straight-line code the
+    // scheduler can interleave; UC < 0 is the generic loop (runtime counts).
+    auto stage_loop = [&](auto nc_tag, auto nr_tag, auto uc_tag) {
+      constexpr int NC_CT = decltype(nc_tag)::value, NR_CT = decltype(nr_tag)::value;
+      constexpr int UC_CT = decltype(uc_tag)::value;
     for (int st = -1; st < ntiles; ++st) {
       if (st + 1 < ntiles) vm_wait(min(nbuf - 3, ntiles - 2 - st) * copies);  // tile st+1 has landed
       lds_barrier();                  // tile st+1 visible; P'(st) written; P.V(st-1) done everywhere
@@ -649,7 +702,9 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
             }
           }
         };
-        switch (ucount) {
+        if constexpr (UC_CT == 0) {
+        } else if constexpr (UC_CT > 0) pv_units(std::integral_constant<int, UC_CT>{});
+        else switch (ucount) {
           case 0: break;
           case 1: pv_units(std::integral_constant<int, 1>{}); break;
           case 2: if constexpr (UMAX >= 2) pv_units(std::integral_constant<int, 2>{}); break;
@@ -667,83 +722,133 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           const char* buf = lds + slot_qk * bufbytes;
           const float* sc = (const float*)(buf + TB * PITCH);
           const int tvalid = min(TILE, ntok - tq * TILE);
-          // code x q_hi, code x q_lo; b = 16: high byte x (q_hi, q_lo) and low byte x q_hi.
-          // The low byte x q_lo product is left out: its weight is 2^-15 of the
-          // leading term, below the 14-bit rounding of q itself.
-          constexpr int NACC = BITS == 16 ? 3 : 2;
-          float sqv[TB][4];                         // integer scores (exact in fp32 for b < 16)
+          // Latent chunks: code x q_hi, code x q_lo; b = 16: high byte x (q_hi, q_lo) and
+          // low byte x q_hi (the low byte x q_lo product is left out: its weight is
+          // 2^-15 of the leading term, the size of the 15-bit rounding of q).
+          // RoPE chunks: code x (q_hi, q_mid, q_lo); b = 16: high byte x (q_hi, q_mid,
+          // q_lo) and low byte x (q_hi, q_mid) (left out: 2^-22 of the leading term).
+          constexpr int NACC_L = BITS == 16 ? 3 : 2, NACC_R = BITS == 16 ? 5 : 3;
+          float sqv[TB][4];                         // scores in units of the latent prescale
           f4 scv[TB];                               // this lane's 4 token scales per token block
-          // The chunk count is a compile-time constant in each case below, so every
-          // LDS read of the tile is straight-line code the scheduler can hoist
-          // ahead of the MFMAs that consume it.
-          auto qk_chunks = [&](auto c0, auto nc) {
-            constexpr int C0 = decltype(c0)::value, NC = decltype(nc)::value;
+          // NC chunks, of which the first NR are RoPE chunks: compile-time counts in
+          // each case below, so every LDS read of the tile is straight-line code
+          // the scheduler can hoist ahead of the MFMAs that consume it.
+          auto qk_chunks = [&](auto nc_tag, auto nr_tag) {
+            constexpr int NC = decltype(nc_tag)::value, NR = decltype(nr_tag)::value, NL = NC - NR;
             // the scales are read with the codes, not after the MFMAs
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) scv[tb] = *(const f4*)(sc + 16 * tb + 4 * g);
-            i4 acc[TB][NACC];
+            // RoPE chunks first: their integer score is turned into fp32 before
+            // the latent chunks run, so the two parts never hold accumulators
+            // at the same time
+            auto run_chunks = [&](auto c_begin, auto c_end, auto rope_tag, auto& acc) {
+              constexpr int CB = decltype(c_begin)::value, CE = decltype(c_end)::value;
+              constexpr bool ROPE = decltype(rope_tag)::value;
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
+              for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-              for (int k = 0; k < NACC; ++k) acc[tb][k] = i4{0, 0, 0, 0};
+                for (int k = 0; k < (ROPE ? NACC_R : NACC_L); ++k) acc[tb][k] = i4{0, 0, 0, 0};
 #pragma unroll
-            for (int c = C0; c < NC; ++c) {
-              const int fbyte = (64 * c + 16 * g) * BITS / 8;   // first byte of this lane's 16 features
+              for (int c = CB; c < CE; ++c) {
+                // first field of this lane's 16 features in the row
+                const int field = ROPE ? rope_field0 + 64 * c : lat_field0 + 64 * (c - NR);
 #pragma unroll
-              for (int tb = 0; tb < TB; ++tb) {
-                const char* p = buf + tile_off(PITCH, tb, fbyte >> 4, n) + (fbyte & 15);
-                if constexpr (BITS == 8) {
-                  const i4 a = *(const i4*)p;
-                  acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
-                  acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
-                } else if constexpr (BITS == 4) {
-                  const u2 x = *(const u2*)p;
-                  const i4 a = qk_b4(x[0], x[1]);
-                  acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
-                  acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
-                } else if constexpr (BITS == 2) {
-                  const i4 a = qk_b2(*(const uint32_t*)p);
-                  acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
-                  acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
-                } else {
-                  // byte planes: signed high bytes and offset-binary low bytes of
-                  // these 16 features are each one 16-byte row (low plane: slot n ^ 8)
-                  const i4 hi = *(const i4*)(buf + tile_off(PITCH, 0, 4 * c + g, n));
-                  const i4 lo = *(const i4*)(buf + tile_off(PITCH, 0, (NSEG >> 1) + 4 * c + g, n ^ 8));
-                  acc[tb][0] = mfma_i8(hi, qh[c], acc[tb][0]);
-                  acc[tb][1] = mfma_i8(hi, ql[c], acc[tb][1]);
-                  acc[tb][2] = mfma_i8(lo, qh[c], acc[tb][2]);
+                for (int tb = 0; tb < TB; ++tb) {
+                  if constexpr (BITS == 16) {
+                    // byte planes: signed high bytes and offset-binary low bytes of
+                    // these 16 features are each one 16-byte row (low plane: slot n ^ 8)
+                    const i4 hi = *(const i4*)(buf + tile_off(PITCH, 0, field >> 4, n));
+                    const i4 lo = *(const i4*)(buf + tile_off(PITCH, 0, (K >> 4) + (field >> 4), n ^ 8));
+                    acc[tb][0] = mfma_i8(hi, qh[c], acc[tb][0]);
+                    acc[tb][1] = mfma_i8(hi, ql[c], acc[tb][1]);
+                    acc[tb][2] = mfma_i8(lo, qh[c], acc[tb][2]);
+                    if constexpr (ROPE) {
+                      acc[tb][3] = mfma_i8(hi, qm[c < kMaxRopeChunks ? c : 0], acc[tb][3]);
+                      acc[tb][4] = mfma_i8(lo, qm[c < kMaxRopeChunks ? c : 0], acc[tb][4]);
+                    }
+                  } else {
+                    const int fbyte = field * BITS / 8;   // first byte of this lane's 16 features
+                    const char* p = buf + tile_off(PITCH, tb, fbyte >> 4, n) + (fbyte & 15);
+                    i4 a;
+                    if constexpr (BITS == 8) a = *(const i4*)p;
+                    else if constexpr (BITS == 4) { const u2 x = *(const u2*)p; a = qk_b4(x[0], x[1]); }
+                    else a = qk_b2(*(const uint32_t*)p);
+                    acc[tb][0] = mfma_i8(a, qh[c], acc[tb][0]);
+                    acc[tb][1] = mfma_i8(a, ql[c], acc[tb][1]);
+                    if constexpr (ROPE) acc[tb][2] = mfma_i8(a, qm[c < kMaxRopeChunks ? c : 0], acc[tb][2]);
+                  }
                 }
               }
+            };
+            // the parts are exact integers (b = 16: up to the left-out products),
+            // joined in fp32: S = S_lat + ratio * S_rope
+            float sr[TB][4];
+            if constexpr (NR == 0) {
+#pragma unroll
+              for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sr[tb][j] = 0.0f;
+            } else {
+              i4 acc[TB][NACC_R];
+              run_chunks(std::integral_constant<int, 0>{}, std::integral_constant<int, NR>{}, std::true_type{}, acc);
+#pragma unroll
+              for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  float v;
+                  if constexpr (BITS == 16)   // 2^22 hh + 2^15 hm + 2^8 hl + 2^14 lh + 2^7 (lm + sum q)
+                    v = fmaf(4194304.0f, (float)acc[tb][0][j],
+                             fmaf(256.0f, (float)(128 * acc[tb][3][j] + acc[tb][1][j]),
+                                  fmaf(16384.0f, (float)acc[tb][2][j], 128.0f * (float)(acc[tb][4][j] + qbiasR))));
+                  else                        // 2^14 hi + 2^7 mid + lo
+                    v = fmaf(16384.0f, (float)acc[tb][0][j], (float)(128 * acc[tb][2][j] + acc[tb][1][j]));
+                  sr[tb][j] = v * ratio;
+                }
             }
+            if constexpr (NL > 0) {
+              // keep the two phases apart: interleaved, their accumulators would
+              // be live at the same time
+              if constexpr (NR > 0) __builtin_amdgcn_sched_barrier(0);
+              i4 acc[TB][NACC_L];
+              run_chunks(std::integral_constant<int, NR>{}, std::integral_constant<int, NC>{}, std::false_type{}, acc);
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
+              for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                if constexpr (BITS == 16)
-                  sqv[tb][j] = 256.0f * (float)(128 * acc[tb][0][j] + acc[tb][1][j]) + (float)(128 * acc[tb][2][j] + qbias);
-                else
-                  sqv[tb][j] = (float)(128 * acc[tb][0][j] + acc[tb][1][j]);
-              }
+                for (int j = 0; j < 4; ++j) {
+                  float v;
+                  if constexpr (BITS == 16)   // 2^8 (2^7 hi + lo) + 2^7 (lh + sum q)
+                    v = fmaf(256.0f, (float)(128 * acc[tb][0][j] + acc[tb][1][j]), 128.0f * (float)(acc[tb][2][j] + qbiasL));
+                  else
+                    v = (float)(128 * acc[tb][0][j] + acc[tb][1][j]);
+                  sqv[tb][j] = v + sr[tb][j];
+                }
+            } else {
+#pragma unroll
+              for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sqv[tb][j] = sr[tb][j];
+            }
           };
-          using Z = std::integral_constant<int, 0>;
           if constexpr (GQA) {
-            if (KC == 2)                      // d_h = 64: [V 64 || K 64]
-              qk_chunks(std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{});
-            else                              // d_h = 128: [V 128 || K 128]
-              qk_chunks(std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{});
+            if (KC == 1) qk_chunks(std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});   // d_h = 64
+            else qk_chunks(std::integral_constant<int, 2>{}, std::integral_constant<int, 0>{});           // d_h = 128
           } else {
-            switch (KC) {
-              case 1: qk_chunks(Z{}, std::integral_constant<int, 1>{}); break;
-              case 2: qk_chunks(Z{}, std::integral_constant<int, 2>{}); break;
-              case 3: qk_chunks(Z{}, std::integral_constant<int, 3>{}); break;
-              case 4: qk_chunks(Z{}, std::integral_constant<int, 4>{}); break;
-              case 5: if constexpr (kMaxC >= 5) qk_chunks(Z{}, std::integral_constant<int, 5>{}); break;
-              case 6: if constexpr (kMaxC >= 6) qk_chunks(Z{}, std::integral_constant<int, 6>{}); break;
-              case 7: if constexpr (kMaxC >= 7) qk_chunks(Z{}, std::integral_constant<int, 7>{}); break;
-              case 8: if constexpr (kMaxC >= 8) qk_chunks(Z{}, std::integral_constant<int, 8>{}); break;
-              default: qk_chunks(Z{}, std::integral_constant<int, kMaxC>{}); break;
+#define KK_QK_CASE(k)                                                                           \
+  case k:                                                                                       \
+    if constexpr (kMaxC >= k) {                                                                 \
+      if (NRq == 1 || k < 3) qk_chunks(std::integral_constant<int, k>{}, std::integral_constant<int, 1>{}); \
+      else qk_chunks(std::integral_constant<int, k>{}, std::integral_constant<int, (k >= 3 ? 2 : 1)>{});    \
+    }                                                                                           \
+    break;
+            if constexpr (NC_CT > 0) {
+              qk_chunks(std::integral_constant<int, NC_CT>{}, std::integral_constant<int, NR_CT>{});
+            } else {
+              switch (KC) {
+                KK_QK_CASE(2) KK_QK_CASE(3) KK_QK_CASE(4) KK_QK_CASE(5) KK_QK_CASE(6) KK_QK_CASE(7) KK_QK_CASE(8)
+                default: KK_QK_CASE(9)
+              }
             }
+#undef KK_QK_CASE
           }
 
           // ---- online softmax for these rows ----
@@ -771,8 +876,9 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
               tmax = fmaxf(tmax, t[tb][j]);
             }
           // The running max and E usually stay: the exponentials are taken
-          // with them right away, in parallel with the row reductions, and are
-          // redone in the rare stage that moves either.
+          // with them right away, and only a lane-local test decides whether any
+          // row must move them (the row reductions run in that rare stage only,
+          // which also redoes the exponentials).
           float e[TB][4];
           {
             const float mE0 = m_run + (float)Ecur;    // P~ = 2^(z - m - E), P' = P~ * scale_t
@@ -781,12 +887,14 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
 #pragma unroll
               for (int j = 0; j < 4; ++j) e[tb][j] = __builtin_amdgcn_exp2f(fmaf(t[tb][j], rowf, -mE0));
           }
-          smax = max_xor_16_32(smax);
-          tmax = max_xor_16_32(tmax) * rowf;
-          const bool raise_e = smax > ldexpf(1.0f, Ecur + kScaleHeadroom);   // wave-uniform
-          const bool upd = __any(tmax > m_run + kLazyRescale) || raise_e;    // wave-uniform
+          const float e_limit = ldexpf(1.0f, Ecur + kScaleHeadroom);
+          const bool upd = __any(smax > e_limit || tmax * rowf > m_run + kLazyRescale);   // wave-uniform
           const int par = tq & 1;
           if (upd) {
+            // every row of a wave sees the same tokens, so smax is wave-uniform
+            smax = max_xor_16_32(smax);
+            tmax = max_xor_16_32(tmax) * rowf;
+            const bool raise_e = smax > e_limit;
             const float mnew = max_plain(m_run, tmax);
             int es = Ecur;
             (void)frexpf(smax, &es);
@@ -831,6 +939,38 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       slot_qk = slot_qk + 1 == nbuf ? 0 : slot_qk + 1;
       slot_pv = slot_pv + 1 == nbuf ? 0 : slot_pv + 1;
     }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using IG = std::integral_constant<int, -1>;
+    bool done = false;
+    if constexpr (QKW) {
+      // the Q.K waves of 40-head rows with d = 128, 256, 384, 512 and d_R <= 64
+      // (chunks 3, 5, 7, 9; output units 0, 1, 2, 3)
+      if constexpr (RB == 3 && V == kFull) {
+        if (NRq == 1 && KC == 3 && ucount == 0) { stage_loop(std::integral_constant<int, 3>{}, std::integral_constant<int, 1>{}, I0{}); done = true; }
+        else if (NRq == 1 && KC == 5 && ucount == 1) { stage_loop(std::integral_constant<int, 5>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 1>{}); done = true; }
+        else if (NRq == 1 && KC == 7 && ucount == 2) { stage_loop(std::integral_constant<int, 7>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 2>{}); done = true; }
+        else if (NRq == 1 && KC == 9 && ucount == 3) { stage_loop(std::integral_constant<int, 9>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, 3>{}); done = true; }
+      }
+      if (!done && NRq == 1 && KC == kMaxC && ucount == UMAX) {
+        stage_loop(std::integral_constant<int, kMaxC>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, UMAX>{});
+        done = true;
+      }
+    } else {
+      // waves without Q.K rows: one loop per unit count
+      switch (ucount) {
+        case 0: stage_loop(I0{}, I0{}, I0{}); done = true; break;
+        case 1: stage_loop(I0{}, I0{}, std::integral_constant<int, 1>{}); done = true; break;
+        case 2: if constexpr (UMAX >= 2) { stage_loop(I0{}, I0{}, std::integral_constant<int, 2>{}); done = true; } break;
+        case 3: if constexpr (UMAX >= 3) { stage_loop(I0{}, I0{}, std::integral_constant<int, 3>{}); done = true; } break;
+        case 4: if constexpr (UMAX >= 4) { stage_loop(I0{}, I0{}, std::integral_constant<int, 4>{}); done = true; } break;
+        case 5: if constexpr (UMAX >= 5) { stage_loop(I0{}, I0{}, std::integral_constant<int, 5>{}); done = true; } break;
+        case 6: if constexpr (UMAX >= 6) { stage_loop(I0{}, I0{}, std::integral_constant<int, 6>{}); done = true; } break;
+        case 7: if constexpr (UMAX >= 7) { stage_loop(I0{}, I0{}, std::integral_constant<int, 7>{}); done = true; } break;
+        default: break;
+      }
+    }
+    if (!done) stage_loop(I0{}, I0{}, IG{});
 
     // ---- finish: row sums, then normalized output or split partial -----------------
     if constexpr (QKW) {
@@ -1081,14 +1221,14 @@ hipError_t launch_one(const DecodeArgs& a, int n, int lds, hipStream_t stream) {
 
 // Tile buffers per workgroup: as many as fit in the workgroup's share of the
 // 160 KB LDS, 3 to 12 (two tiles are in use, the rest in flight).
-int decode_nbuf(int row_stride, int K, int bits, int rb, int variant) {
+int decode_nbuf(int row_stride, int d, int d_rope, int bits, int rb, int variant) {
   const int budget = 160 * 1024 / decode_wg_per_cu(variant) - pbuf_bytes(rb, tile_blocks_of(bits)) - kMiscBytes;
-  const int n = budget / tilebuf_bytes(row_stride, K, bits);
+  const int n = budget / tilebuf_bytes(row_stride, d, d_rope, bits);
   return n < 3 ? 3 : (n > 12 ? 12 : n);
 }
 
-int decode_lds_bytes(int row_stride, int K, int bits, int rb, int variant) {
-  return decode_nbuf(row_stride, K, bits, rb, variant) * tilebuf_bytes(row_stride, K, bits) +
+int decode_lds_bytes(int row_stride, int d, int d_rope, int bits, int rb, int variant) {
+  return decode_nbuf(row_stride, d, d_rope, bits, rb, variant) * tilebuf_bytes(row_stride, d, d_rope, bits) +
          pbuf_bytes(rb, tile_blocks_of(bits)) + kMiscBytes;
 }
 

@@ -38,6 +38,7 @@ kk_status check_model(const kk_model_cfg* c) {
     if (L.anchor == l) {
       if (!valid_bits(L.bits) || L.d < 1 || L.d > c->r) return KK_ERR_INVALID_ARGUMENT;
       if (L.d % 16 != 0 || L.d > KK_MAX_D || L.d + c->d_rope > KK_MAX_K) return KK_ERR_UNSUPPORTED;
+      if (kk::qk_chunks_of(L.d, c->d_rope) > kk::kMaxQkChunks) return KK_ERR_UNSUPPORTED;
     } else {
       if (l == 0 || L.anchor < 0 || L.anchor > l) return KK_ERR_INVALID_ARGUMENT;
       if (c->layers[L.anchor].anchor != L.anchor) return KK_ERR_INVALID_ARGUMENT;
@@ -51,6 +52,20 @@ size_t stride_of(int d, int dr, int bits) {
   const int64_t bitsum = (int64_t)(d + dr) * bits;
   if (bitsum % 8) return 0;
   return (size_t)((bitsum / 8 + 15) / 16 * 16);
+}
+
+// Compute units the automatic split choice plans for: those of the device that
+// runs `stream` (the current device for a null stream).  Only automatic splits
+// (split_tokens == 0) over a non-empty step depend on it; otherwise no device
+// is queried.
+kk_status plan_cus(hipStream_t stream, int split_tokens, int max_len, int* cus) {
+  *cus = 1;
+  if (split_tokens > 0 || max_len <= 0) return KK_OK;
+  int dev = 0;
+  if ((stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev)) != hipSuccess) return KK_ERR_DEVICE;
+  if (hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || *cus < 1)
+    return KK_ERR_DEVICE;
+  return KK_OK;
 }
 
 // One table of the step: its layers, its caches and the sequences that use it.
@@ -91,7 +106,7 @@ constexpr int64_t kItemOverhead = 40;   // per-item fixed cost (query setup, pip
 // Splits are chosen so that items carry similar byte counts; entries are
 // ordered by bytes per item, largest first.  The tables share n_layers,
 // n_heads, r and d_rope (checked by the callers).
-kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_tokens, Plan& P) {
+kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_tokens, int n_cus, Plan& P) {
   const kk_model_cfg* c0 = tabs[0].cfg;
   const int H = c0->n_heads, L = c0->n_layers;
   P.layers.assign((size_t)tabs.size() * L, kk::LayerArg{});
@@ -167,10 +182,11 @@ kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_to
     for (auto& T : tabs)
       for (int a = 0; a < L; ++a)
         if (T.cfg->layers[a].anchor == a &&
-            (T.cfg->layers[a].d > kk::kLeanMaxD || T.cfg->layers[a].d + T.cfg->d_rope > kk::kLeanMaxK))
+            (T.cfg->layers[a].d > kk::kLeanMaxD ||
+             kk::qk_chunks_of(T.cfg->layers[a].d, T.cfg->d_rope) > kk::kLeanMaxChunks))
           variant = kk::kFull;
   P.launch.variant = variant;
-  const int64_t slots = (int64_t)kk::kCUs * kk::decode_wg_per_cu(variant);
+  const int64_t slots = (int64_t)std::max(n_cus, 1) * kk::decode_wg_per_cu(variant);
   auto split_of = [&](const Ent& E, int waves) {
     const int64_t target = std::max<int64_t>(1, total_cost / (waves * slots));
     int64_t sp;
@@ -263,8 +279,8 @@ kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_to
       ws += (int64_t)e.nrc * e.n_seq * e.splits * kk::partial_slot_floats(e.d);
       merges += (int64_t)e.nrc * e.n_seq;
     }
-    e.nbuf = (int8_t)kk::decode_nbuf(e.row_stride, e.d + c0->d_rope, e.bits, RB, variant);
-    Lc.lds_bytes = std::max(Lc.lds_bytes, kk::decode_lds_bytes(e.row_stride, e.d + c0->d_rope, e.bits, RB, variant));
+    e.nbuf = (int8_t)kk::decode_nbuf(e.row_stride, e.d, c0->d_rope, e.bits, RB, variant);
+    Lc.lds_bytes = std::max(Lc.lds_bytes, kk::decode_lds_bytes(e.row_stride, e.d, c0->d_rope, e.bits, RB, variant));
     if (Lc.lds_bytes > 160 * 1024 / kk::decode_wg_per_cu(variant)) return KK_ERR_UNSUPPORTED;
     P.ents[i] = e;
     P.entry_anchor[i] = ents[i].anchor;
@@ -279,9 +295,9 @@ kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_to
 
 // Plan of one table whose arrays travel in the launch arguments.
 kk_status make_single_plan(const kk_model_cfg* c, const kk_cache* caches, int batch, int max_len, int split_tokens,
-                           Plan& P) {
+                           int n_cus, Plan& P) {
   std::vector<TableRef> tabs{TableRef{c, caches, batch, 0, 0, 0}};
-  const kk_status st = make_plan(tabs, max_len, split_tokens, P);
+  const kk_status st = make_plan(tabs, max_len, split_tokens, n_cus, P);
   if (st != KK_OK) return st;
   if (P.ents.size() > (size_t)kk::kMaxEntries) return KK_ERR_UNSUPPORTED;
   kk::DecodeArgs& A = P.args;
@@ -370,10 +386,36 @@ kk_status kk_decode_workspace_bytes(const kk_model_cfg* cfg, int32_t batch, int3
   if (st != KK_OK) return st;
   if (batch < 1 || max_seq_len < 0 || split_tokens < 0 || !bytes) return KK_ERR_INVALID_ARGUMENT;
   if (split_tokens % kk::kTile) return KK_ERR_INVALID_ARGUMENT;
+  int cus = 1;
+  st = plan_cus(nullptr, split_tokens, max_seq_len, &cus);
+  if (st != KK_OK) return st;
   Plan P;
-  st = make_single_plan(cfg, nullptr, batch, max_seq_len, split_tokens, P);
+  st = make_single_plan(cfg, nullptr, batch, max_seq_len, split_tokens, cus, P);
   if (st != KK_OK) return st;
   *bytes = (size_t)P.ws_floats * sizeof(float);
+  return KK_OK;
+}
+
+kk_status kk_decode_plan_info(const kk_model_cfg* cfg, int32_t batch, int32_t max_seq_len, int32_t split_tokens,
+                              int32_t n_cus, kk_plan_info* info) {
+  kk_status st = check_model(cfg);
+  if (st != KK_OK) return st;
+  if (batch < 1 || max_seq_len < 0 || split_tokens < 0 || split_tokens % kk::kTile || n_cus < 0 || !info)
+    return KK_ERR_INVALID_ARGUMENT;
+  int cus = n_cus;
+  if (cus == 0) {
+    st = plan_cus(nullptr, 0, 1, &cus);
+    if (st != KK_OK) return st;
+  }
+  Plan P;
+  st = make_single_plan(cfg, nullptr, batch, max_seq_len, split_tokens, cus, P);
+  if (st != KK_OK) return st;
+  info->n_cus = cus;
+  info->work_items = P.launch.items;
+  info->merge_blocks = P.launch.merge_blocks;
+  info->max_splits = 0;
+  for (const auto& e : P.ents) info->max_splits = std::max<int32_t>(info->max_splits, e.splits);
+  info->workspace_bytes = (size_t)P.ws_floats * sizeof(float);
   return KK_OK;
 }
 
@@ -382,7 +424,7 @@ namespace {
 kk_status prepare_decode(const kk_model_cfg* cfg, const kk_cache* caches, int32_t batch, int32_t t_cap,
                          const int32_t* seq_lens, int32_t max_seq_len, const void* q_lat, const void* q_rope,
                          kk_dtype q_dtype, float* out, int32_t split_tokens, void* workspace, size_t workspace_bytes,
-                         Plan& P) {
+                         hipStream_t stream, Plan& P) {
   kk_status st = check_model(cfg);
   if (st != KK_OK) return st;
   if (!caches || batch < 1 || t_cap < 1 || max_seq_len < 0 || max_seq_len > t_cap) return KK_ERR_INVALID_ARGUMENT;
@@ -397,7 +439,10 @@ kk_status prepare_decode(const kk_model_cfg* cfg, const kk_cache* caches, int32_
     if (!aligned(caches[l].codes, 16) || !aligned(caches[l].scales, 16)) return KK_ERR_INVALID_ARGUMENT;
   }
   if ((int64_t)cfg->n_layers * batch * cfg->n_heads > ((int64_t)1 << 31)) return KK_ERR_UNSUPPORTED;
-  st = make_single_plan(cfg, caches, batch, max_seq_len, split_tokens, P);
+  int cus = 1;
+  st = plan_cus(stream, split_tokens, max_seq_len, &cus);
+  if (st != KK_OK) return st;
+  st = make_single_plan(cfg, caches, batch, max_seq_len, split_tokens, cus, P);
   if (st != KK_OK) return st;
   const size_t need = (size_t)P.ws_floats * sizeof(float);
   if (need > 0) {
@@ -502,8 +547,11 @@ kk_status kk_multi_decode_workspace_bytes(const kk_table_batch* tables, int32_t 
   kk_status st = check_tables(tables, n_tables, false, tabs, &total);
   if (st != KK_OK) return st;
   if (max_seq_len < 0 || split_tokens < 0 || split_tokens % kk::kTile || !bytes) return KK_ERR_INVALID_ARGUMENT;
+  int cus = 1;
+  st = plan_cus(nullptr, split_tokens, max_seq_len, &cus);
+  if (st != KK_OK) return st;
   Plan P;
-  st = make_plan(tabs, max_seq_len, split_tokens, P);
+  st = make_plan(tabs, max_seq_len, split_tokens, cus, P);
   if (st != KK_OK) return st;
   *bytes = multi_layout(P).total;
   return KK_OK;
@@ -523,8 +571,11 @@ kk_status kk_multi_decode_attn(const kk_table_batch* tables, int32_t n_tables, i
   if (!seq_lens || !q_lat || !q_rope || !out) return KK_ERR_INVALID_ARGUMENT;
   if (!aligned(seq_lens, 4) || !aligned(q_lat, 16) || !aligned(q_rope, 16) || !aligned(out, 16))
     return KK_ERR_INVALID_ARGUMENT;
+  int cus = 1;
+  st = plan_cus(stream, split_tokens, max_seq_len, &cus);
+  if (st != KK_OK) return st;
   Plan P;
-  st = make_plan(tabs, max_seq_len, split_tokens, P);
+  st = make_plan(tabs, max_seq_len, split_tokens, cus, P);
   if (st != KK_OK) return st;
   const MultiLayout m = multi_layout(P);
   if (!workspace || !aligned(workspace, 256)) return KK_ERR_INVALID_ARGUMENT;
@@ -573,7 +624,7 @@ kk_status kk_decode_attn(const kk_model_cfg* cfg, const kk_cache* caches, int32_
                          hipStream_t stream) {
   Plan P;
   const kk_status st = prepare_decode(cfg, caches, batch, t_cap, seq_lens, max_seq_len, q_lat, q_rope, q_dtype, out,
-                                      split_tokens, workspace, workspace_bytes, P);
+                                      split_tokens, workspace, workspace_bytes, stream, P);
   if (st != KK_OK) return st;
   return kk::launch_decode(P.args, P.launch, stream) == hipSuccess ? KK_OK : KK_ERR_DEVICE;
 }
@@ -586,7 +637,7 @@ kk_status kk_append_decode(const kk_model_cfg* cfg, const kk_cache* caches, int3
   // every check of both steps runs before anything is enqueued
   Plan P;
   kk_status st = prepare_decode(cfg, caches, batch, t_cap, seq_lens, max_seq_len, q_lat, q_rope, q_dtype, out,
-                                split_tokens, workspace, workspace_bytes, P);
+                                split_tokens, workspace, workspace_bytes, stream, P);
   if (st != KK_OK) return st;
   if (src_dtype != KK_DTYPE_F32 && src_dtype != KK_DTYPE_BF16) return KK_ERR_INVALID_ARGUMENT;
   const size_t ea = src_dtype == KK_DTYPE_F32 ? 4 : 2;
@@ -701,9 +752,12 @@ kk_status kk_gqa_decode_workspace_bytes(const kk_gqa_cfg* cfg, int32_t batch, in
   if (batch < 1 || max_seq_len < 0 || split_tokens < 0 || split_tokens % kk::kTile || !bytes)
     return KK_ERR_INVALID_ARGUMENT;
   if ((int64_t)batch * cfg->n_kv_heads > 0x7fffffff) return KK_ERR_UNSUPPORTED;
+  int cus = 1;
+  st = plan_cus(nullptr, split_tokens, max_seq_len, &cus);
+  if (st != KK_OK) return st;
   Plan P;
   std::vector<TableRef> tabs{TableRef{&m.cfg, nullptr, batch * cfg->n_kv_heads, 0, 0, 0, cfg->d_head / 64}};
-  st = make_plan(tabs, max_seq_len, split_tokens, P);
+  st = make_plan(tabs, max_seq_len, split_tokens, cus, P);
   if (st != KK_OK) return st;
   if (P.ents.size() > (size_t)kk::kMaxEntries) return KK_ERR_UNSUPPORTED;
   *bytes = (size_t)P.ws_floats * sizeof(float);
@@ -729,9 +783,12 @@ kk_status kk_gqa_decode_attn(const kk_gqa_cfg* cfg, const kk_cache* caches, int3
   const int64_t nseq = (int64_t)batch * cfg->n_kv_heads;
   if (nseq > 0x7fffffff || (int64_t)cfg->n_layers * batch * cfg->n_q_heads > ((int64_t)1 << 31))
     return KK_ERR_UNSUPPORTED;
+  int cus = 1;
+  st = plan_cus(stream, split_tokens, max_seq_len, &cus);
+  if (st != KK_OK) return st;
   Plan P;
   std::vector<TableRef> tabs{TableRef{&m.cfg, caches, (int)nseq, 0, 0, 0, cfg->d_head / 64}};
-  st = make_plan(tabs, max_seq_len, split_tokens, P);
+  st = make_plan(tabs, max_seq_len, split_tokens, cus, P);
   if (st != KK_OK) return st;
   if (P.ents.size() > (size_t)kk::kMaxEntries) return KK_ERR_UNSUPPORTED;
   const size_t need = (size_t)P.ws_floats * sizeof(float);

@@ -16,15 +16,17 @@ constexpr int kMaxMergeSplits = 64;  // token splits of one sequence
 constexpr int kMaxK = 576;           // d + d_R (the ABI limit)
 constexpr int kMaxEntries = 88;      // group entries held in the launch arguments
 constexpr int kMaxLayers = 64;
-constexpr int kCUs = 256;
 // Decode kernel variants (register budgets) and workgroups per CU: kFull, any
 // latent row (256 VGPRs: two workgroups, the second hides the fixed latencies
-// of the first); kLean, steps whose anchors all have d <= 256 and K = d + d_R
-// <= 320, in items of at most 2 row blocks (three); kGqa, grouped-query rows
-// (four).
+// of the first); kLean, steps whose anchors all have d <= 256 and at most
+// five 64-field Q.K chunks, in items of at most 2 row blocks (three); kGqa,
+// grouped-query rows (four).
 constexpr int kFull = 0, kLean = 1, kGqa = 2;
 constexpr int decode_wg_per_cu(int variant) { return variant == kGqa ? 4 : variant == kLean ? 3 : 2; }
-constexpr int kLeanMaxD = 256, kLeanMaxK = 320;
+constexpr int kLeanMaxD = 256, kLeanMaxChunks = 5;
+// Q.K chunks of a row: the latent part and the RoPE part, each in chunks of 64 fields
+constexpr int qk_chunks_of(int d, int d_rope) { return ((d + 63) >> 6) + ((d_rope + 63) >> 6); }
+constexpr int kMaxQkChunks = (kMaxK + 63) / 64;
 constexpr float kLazyRescale = 8.0f; // log2 headroom before the running max is moved
 
 // One layer of one table: softmax scale, kept width of its anchor and the
@@ -169,8 +171,8 @@ struct DecodeLaunch {
   int variant = kFull;   // kernel variant (kGqa: row_blocks <= 2)
 };
 
-int decode_nbuf(int row_stride, int K, int bits, int row_blocks, int variant);
-int decode_lds_bytes(int row_stride, int K, int bits, int row_blocks, int variant);
+int decode_nbuf(int row_stride, int d, int d_rope, int bits, int row_blocks, int variant);
+int decode_lds_bytes(int row_stride, int d, int d_rope, int bits, int row_blocks, int variant);
 hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t stream);
 
 // Copies `words` 32-bit words from host memory to device memory `dst` by

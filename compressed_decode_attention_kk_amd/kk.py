@@ -40,6 +40,11 @@ class Cache(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
 
 
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("n_cus", ctypes.c_int32), ("work_items", ctypes.c_int32), ("merge_blocks", ctypes.c_int32),
+                ("max_splits", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+
+
 class GqaCfg(ctypes.Structure):
     _fields_ = [("n_layers", ctypes.c_int32), ("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
                 ("d_head", ctypes.c_int32), ("layers", ctypes.POINTER(LayerCfg))]
@@ -71,6 +76,8 @@ def lib():
                                         ctypes.c_void_p]
         L.kk_decode_workspace_bytes.argtypes = [ctypes.POINTER(ModelCfg), ctypes.c_int32, ctypes.c_int32,
                                                 ctypes.c_int32, ctypes.POINTER(ctypes.c_size_t)]
+        L.kk_decode_plan_info.argtypes = [ctypes.POINTER(ModelCfg), ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.POINTER(PlanInfo)]
         L.kk_decode_attn.argtypes = [ctypes.POINTER(ModelCfg), ctypes.POINTER(Cache), ctypes.c_int32, ctypes.c_int32,
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
@@ -105,7 +112,7 @@ def lib():
         L.kk_status_string.restype = ctypes.c_char_p
         L.kk_status_string.argtypes = [ctypes.c_int]
         for name in ("kk_validate_model", "kk_cache_bytes", "kk_out_offsets", "kk_quantize_write",
-                     "kk_decode_workspace_bytes", "kk_decode_attn", "kk_append_decode", "kk_multi_out_offsets",
+                     "kk_decode_workspace_bytes", "kk_decode_plan_info", "kk_decode_attn", "kk_append_decode", "kk_multi_out_offsets",
                      "kk_multi_decode_workspace_bytes", "kk_multi_decode_attn", "kk_latent_epilogue",
                      "kk_gqa_cache_bytes", "kk_gqa_quantize_write", "kk_gqa_decode_workspace_bytes",
                      "kk_gqa_decode_attn"):
@@ -268,6 +275,14 @@ def workspace_bytes(model: Model, batch: int, max_seq_len: int, split_tokens: in
     _check(lib().kk_decode_workspace_bytes(model.cfg, batch, max_seq_len, split_tokens, ctypes.byref(b)),
            "kk_decode_workspace_bytes")
     return b.value
+
+
+def plan_info(model: Model, batch: int, max_seq_len: int, split_tokens: int = 0, n_cus: int = 0) -> PlanInfo:
+    """The decode step's work plan for n_cus compute units (0: the current device's)."""
+    info = PlanInfo()
+    _check(lib().kk_decode_plan_info(model.cfg, batch, max_seq_len, split_tokens, n_cus, ctypes.byref(info)),
+           "kk_decode_plan_info")
+    return info
 
 
 class Decoder:

@@ -86,7 +86,9 @@ typedef enum { KK_DTYPE_F32 = 0, KK_DTYPE_BF16 = 1 } kk_dtype;
  * sm_scale is the layer's softmax scale (any finite value; the workloads use
  * 1/sqrt(d_eff + d_R)).
  * Rules: layer 0 is an anchor; 0 < d <= r, d % 16 == 0; bits in {2,4,8,16};
- * d_R % 16 == 0; d + d_R <= KK_MAX_K; d <= KK_MAX_D. */
+ * d_R % 16 == 0; d + d_R <= KK_MAX_K; d <= KK_MAX_D; ceil(d / 64) +
+ * ceil(d_R / 64) <= 9 (the decode reads the latent and the RoPE part of a row
+ * in separate 64-field chunks). */
 typedef struct {
   int32_t anchor;
   int32_t d;
@@ -110,23 +112,37 @@ typedef struct {
 
 /* Row stride in bytes of a (d, d_rope, bits) cache; 0 if the combination is
  * invalid (bits not in {2,4,8,16}, non-positive widths, or (d+d_rope)*bits
- * not a multiple of 8). */
+ * not a multiple of 8).
+ * Follows the per-token cost of an action on the KV-Kaizen summary page
+ * ("Action Space and Cost Model", cost equation: (d + d_R) * b bits), rounded
+ * up to whole 16-byte segments. */
 size_t kk_row_stride_bytes(int32_t d, int32_t d_rope, int32_t bits);
 
-/* Checks the table rules above. */
+/* Checks the table rules above (the action set of "Action Space and Cost
+ * Model"; the depth item of "Three Non-Eviction Compression Axes": an
+ * inheriting layer names an earlier anchor). */
 kk_status kk_validate_model(const kk_model_cfg* cfg);
 
-/* Bytes of the codes and scales buffers of anchor `layer` for [batch][t_cap].
- * Inheriting layers own no cache: KK_ERR_INVALID_ARGUMENT. */
+/* Bytes of the codes and scales buffers of anchor `layer` for [batch][t_cap]:
+ * batch * t_cap rows of kk_row_stride_bytes, and one float32 scale per token
+ * (precision item of "Three Non-Eviction Compression Axes": one scale per
+ * token).  Inheriting layers own no cache (depth item): KK_ERR_INVALID_ARGUMENT.
+ * Host outputs; no device access. */
 kk_status kk_cache_bytes(const kk_model_cfg* cfg, int32_t layer, int32_t batch, int32_t t_cap,
                          size_t* codes_bytes, size_t* scales_bytes);
 
 /* Float offsets of each layer's output block in the packed decode output:
  * offsets[l] for l in [0, n_layers], offsets[n_layers] = total floats.
- * `offsets` is a host array of n_layers + 1 entries. */
+ * `offsets` is a host array of n_layers + 1 entries.  Each layer's block is
+ * [batch][n_heads][d_eff]: the absorbed output lives in the latent space kept
+ * by the layer's anchor (rank item of "Three Non-Eviction Compression Axes"). */
 kk_status kk_out_offsets(const kk_model_cfg* cfg, int32_t batch, int64_t* offsets);
 
-/* Quantize-and-pack cache write (pre-fill and append) for anchor `layer`.
+/* Quantize-and-pack cache write (pre-fill and append) for anchor `layer`:
+ * the cache keeps the first d latent coordinates and the RoPE key (rank item
+ * of "Three Non-Eviction Compression Axes"), as b-bit symmetric uniform codes
+ * with one scale per token (precision item), quantized as stated at the top
+ * of this file.
  *
  * Source rows: latent [n_src][latent_ld] (first d of r coordinates used) and
  * rope [n_src][rope_ld] (first d_rope used), both `src_dtype` (float32, or
@@ -145,11 +161,36 @@ kk_status kk_quantize_write(const kk_model_cfg* cfg, int32_t layer,
 
 /* Workspace bytes kk_decode_attn needs for this model, batch and
  * max_seq_len, with the same split_tokens argument (0 = automatic).
- * The workspace holds split partials only; it need not be zeroed. */
+ * The workspace holds split partials only; it need not be zeroed.
+ * Automatic splits are planned for the compute units of the current HIP
+ * device (hipGetDevice); with no device, KK_ERR_DEVICE.  kk_decode_attn plans
+ * for the device of its stream, so size the workspace on that device. */
 kk_status kk_decode_workspace_bytes(const kk_model_cfg* cfg, int32_t batch, int32_t max_seq_len,
                                     int32_t split_tokens, size_t* bytes);
 
-/* One decode step of absorbed-MLA attention for every layer of the table.
+/* The work plan of one kk_decode_attn step (host only; no device access when
+ * n_cus > 0).  The decode step splits each sequence's tokens so that the work
+ * items fill the device (every decoded token reads the whole cache: "Background:
+ * The KV Cache Bottleneck"); the split count depends on the compute units.
+ * n_cus > 0 plans for that many compute units, n_cus == 0 for the current
+ * device's.  Outputs: the compute units used, the decode work items (one
+ * workgroup each), the merge workgroups, the largest split count of any
+ * (row chunk, sequence), and the workspace bytes (as kk_decode_workspace_bytes
+ * on a device with n_cus compute units). */
+typedef struct {
+  int32_t n_cus;
+  int32_t work_items;
+  int32_t merge_blocks;
+  int32_t max_splits;
+  size_t workspace_bytes;
+} kk_plan_info;
+kk_status kk_decode_plan_info(const kk_model_cfg* cfg, int32_t batch, int32_t max_seq_len, int32_t split_tokens,
+                              int32_t n_cus, kk_plan_info* info);
+
+/* One decode step of absorbed-MLA attention for every layer of the table
+ * (the step that reads the whole compressed cache for every generated token:
+ * "Background: The KV Cache Bottleneck"; the cache of the depth, rank and
+ * precision items of "Three Non-Eviction Compression Axes").
  *
  * For layer l with anchor a = cfg->layers[l].anchor, d = d_a, b = b_a, each
  * sequence s and head h, over the cached tokens t < len_s:
@@ -171,7 +212,23 @@ kk_status kk_decode_workspace_bytes(const kk_model_cfg* cfg, int32_t batch, int3
  *              the library choose; results agree across choices within
  *              floating-point rounding and are bitwise reproducible for a
  *              fixed choice.
- * workspace  : device, >= kk_decode_workspace_bytes, 256-byte aligned. */
+ * workspace  : device, >= kk_decode_workspace_bytes, 256-byte aligned.
+ *
+ * Arithmetic and the range it is checked over: the latent part of each query
+ * row is rounded once to a 15-bit fixed-point number relative to its largest
+ * magnitude (two int8 limbs) and the RoPE part to a 22-bit one relative to its
+ * own (three limbs); the integer scores of the two parts are exact (b = 16: up
+ * to a left-out low-byte term of 2^-15 resp. 2^-22 of the leading one) and are
+ * joined in fp32; softmax in fp32; the P.V operands are P' (numerator times
+ * token scale) in fp16 and the codes in fp16 (exact for b <= 8, rounded to 11
+ * significant bits for b = 16), accumulated in fp32.  Against an exact fp64
+ * evaluation of the formula above, the output stays within 2e-3 * max|out| per
+ * layer for N(0, 1) queries, for queries whose RoPE part is up to 256x the
+ * latent part or whose latent part is 64x the RoPE part, and for one
+ * coordinate per row scaled 64x in either part (all tested, with and without
+ * token splits).  The logit error is about 2^-15 of the latent part's largest
+ * term plus 2^-22 of the RoPE part's, so it grows with |q| * |cache|: queries
+ * far outside that range can exceed the bound. */
 kk_status kk_decode_attn(const kk_model_cfg* cfg, const kk_cache* caches, int32_t batch, int32_t t_cap,
                          const int32_t* seq_lens, int32_t max_seq_len,
                          const void* q_lat, const void* q_rope, kk_dtype q_dtype, float* out,

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
               "kk_out_offsets", "kk_validate_model", "kk_row_stride_bytes", "kk_status_string",
               "kk_append_decode", "kk_multi_out_offsets", "kk_multi_decode_workspace_bytes",
               "kk_multi_decode_attn", "kk_latent_epilogue", "kk_gqa_cache_bytes", "kk_gqa_quantize_write",
-              "kk_gqa_decode_workspace_bytes", "kk_gqa_decode_attn"):
+              "kk_gqa_decode_workspace_bytes", "kk_gqa_decode_attn", "kk_decode_plan_info"):
         assert n in names
 
 
@@ -114,6 +114,10 @@ def test_validate_model_rules(kk):
     assert status(kk, table([[0, 64, 4]], dr=24, kk=kk)) == kk.KK_ERR_UNSUPPORTED              # d_R % 16
     assert status(kk, table([[0, 512, 4]], dr=80, kk=kk)) == kk.KK_ERR_UNSUPPORTED             # d + d_R > 576
     assert status(kk, table([[0, 448, 4]], dr=128, kk=kk)) == kk.KK_OK                         # d + d_R = 576
+    # Q.K reads the latent part in 64-field chunks from field 0 and the RoPE part
+    # in 64-field chunks from field d: at most 9 chunks in all
+    assert status(kk, table([[0, 480, 4]], dr=96, kk=kk)) == kk.KK_ERR_UNSUPPORTED             # 8 + 2 chunks
+    assert status(kk, table([[0, 448, 4]], dr=80, kk=kk)) == kk.KK_OK                          # 7 + 2 chunks
     m = table([[0, 64, 4]], kk=kk)
     m._arr[0].sm_scale = float("nan")
     assert status(kk, m) == kk.KK_ERR_INVALID_ARGUMENT
@@ -149,6 +153,28 @@ def test_workspace_sizes(kk):
     assert kk.workspace_bytes(m, 4, 0, 0) == 0
     with pytest.raises(kk.KKError) as e:
         kk.workspace_bytes(m, 4, 1024, 48)                 # not a multiple of the 32-token tile
+    assert e.value.status == kk.KK_ERR_INVALID_ARGUMENT
+
+
+def test_plan_scales_with_compute_units(kk):
+    """Automatic splits are planned for the device's compute units: more units,
+    more (shorter) work items; an explicit split size ignores them."""
+    import synth
+    w = synth.workload(3)                                 # 48 layers, 40 heads, B = 32, T = 8192
+    m = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+    info = {c: kk.plan_info(m, w.batch, w.seq_len, 0, c) for c in (32, 64, 128, 256, 304, 512)}
+    items = [info[c].work_items for c in sorted(info)]
+    assert items == sorted(items) and items[0] < items[-1]
+    for c, i in info.items():
+        assert i.n_cus == c
+        # about four waves of items over 2 workgroups per compute unit (fewer, longer ones for few units)
+        assert i.work_items >= 2 * c or i.max_splits == 1
+        assert 1 <= i.max_splits <= 64
+    fixed = {c: kk.plan_info(m, w.batch, w.seq_len, 1024, c) for c in (64, 256)}
+    assert fixed[64].work_items == fixed[256].work_items and fixed[64].max_splits == 8
+    assert fixed[64].workspace_bytes == fixed[256].workspace_bytes
+    with pytest.raises(kk.KKError) as e:
+        kk.plan_info(m, w.batch, w.seq_len, 0, -1)
     assert e.value.status == kk.KK_ERR_INVALID_ARGUMENT
 
 
@@ -283,8 +309,8 @@ def test_multi_offsets_and_workspace(kk):
         base += one[-1]
     assert list(offs) == want + [base]
     ws = ctypes.c_size_t()
-    assert L.kk_multi_decode_workspace_bytes(arr, 2, 1024, 0, ctypes.byref(ws)) == kk.KK_OK
-    assert ws.value > 0 and ws.value % 256 == 0
+    assert L.kk_multi_decode_workspace_bytes(arr, 2, 1024, 1024, ctypes.byref(ws)) == kk.KK_OK
+    assert ws.value > 0 and ws.value % 256 == 0                         # the plan only (no splits)
     ws_split = ctypes.c_size_t()
     assert L.kk_multi_decode_workspace_bytes(arr, 2, 1024, 64, ctypes.byref(ws_split)) == kk.KK_OK
     assert ws_split.value > ws.value                                    # partials of 16 splits

@@ -434,23 +434,104 @@ def test_b16_full_rank_matches_unquantized_attention(kk):
         assert np.max(np.abs(got - ref)) <= TOL * np.max(np.abs(ref))
 
 
-@pytest.mark.parametrize("wid,samples", [(1, [(0, 0), (27, 31), (13, 7)]),
-                                         (2, [(0, 0), (27, 31), (11, 5)]),
-                                         (3, None),
-                                         (4, None)])
-def test_full_size_workloads_sampled(kk, wid, samples):
+# Queries whose latent and RoPE parts differ widely in size (or that carry one
+# outlier coordinate per row): the kernel rounds each part of a row to a 15-bit
+# fixed-point number with its own prescale, so the bar holds across this range.
+QRANGE_TABLE = [[0, 512, 2], [1, 384, 4], [1, 0, 0], [3, 256, 8], [4, 128, 16], [4, 0, 0], [6, 512, 16]]
+
+
+def _scale_queries(kind, ql, qr):
+    """Power-of-two scalings (exact in bf16) of seeded N(0, 1) queries."""
+    ql, qr = ql.clone(), qr.clone()
+    L, B, H, r = ql.shape
+    if kind == "rope_x64":
+        qr *= 64
+    elif kind == "rope_x256":
+        qr *= 256
+    elif kind == "lat_x64":
+        ql *= 64
+    elif kind == "lat_outlier_x64":
+        for l in range(L):
+            for h in range(H):
+                ql[l, :, h, (7 * h + 3 * l) % 128] *= 64
+    elif kind == "rope_outlier_x64":
+        for l in range(L):
+            for h in range(H):
+                qr[l, :, h, (5 * h + l) % qr.shape[-1]] *= 64
+    return ql.contiguous(), qr.contiguous()
+
+
+@pytest.mark.parametrize("split_tokens", [0, 256])
+@pytest.mark.parametrize("kind", ["rope_x64", "rope_x256", "lat_x64", "lat_outlier_x64", "rope_outlier_x64"])
+def test_query_dynamic_range(kk, kind, split_tokens):
+    w = synth.small_workload(23, len(QRANGE_TABLE), 40, 2, 2048, 512, 64, QRANGE_TABLE)
+    lens = [2048, 1333]
+    model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+    caches = build_caches(kk, model, w, 2048, seq_lens=lens)
+    ql, qr = _scale_queries(kind, *synth.queries(w, "cuda"))
+    dec = kk.Decoder(model, caches, w.batch, 2048, 2048, split_tokens=split_tokens)
+    dec(ql, qr, torch.tensor(lens, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    worst = 0.0
+    for s in range(w.batch):
+        src = {a: source_cpu(w, a, s) for a in w.anchors()}
+        for l in range(w.n_layers):
+            worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, lens[s], src))
+    print(f"query range {kind}, split_tokens {split_tokens}: worst err ratio {worst:.2e}")
+
+
+@pytest.mark.parametrize("split_tokens", [0, 64])
+@pytest.mark.parametrize("d_rope,table", [
+    (32, [[0, 48, 2], [1, 80, 4], [2, 208, 8], [2, 0, 0], [4, 48, 16], [5, 80, 16]]),
+    (80, [[0, 64, 2], [1, 448, 4], [2, 16, 8], [3, 448, 16], [3, 0, 0]]),
+])
+def test_widths_off_the_64_grid(kk, d_rope, table, split_tokens):
+    """Kept widths that are odd multiples of 16 (the last 32-wide P.V unit half
+    filled) and RoPE widths that are not multiples of 64 (the RoPE chunk reads
+    past the row), every bit width, split and unsplit, ragged lengths."""
+    w = synth.small_workload(24, len(table), 40, 2, 300, 512, d_rope, table)
+    lens = [300, 97]
+    model, caches, dec, ql, qr = run_gpu(kk, w, seq_lens=lens, t_cap=320, split_tokens=split_tokens)
+    worst = 0.0
+    for s in range(w.batch):
+        src = {a: source_cpu(w, a, s) for a in w.anchors()}
+        for l in range(w.n_layers):
+            worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, lens[s], src))
+    print(f"widths off the 64 grid (d_R {d_rope}, split {split_tokens}): worst err ratio {worst:.2e}")
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4])
+def test_full_size_workloads_every_anchor_and_layer(kk, wid):
+    """The four full-size workloads in the configuration bench.py times
+    (automatic splits): every anchor's codes and scales bit-exact on the first
+    and the last sequence, and every layer's output within the bar on one
+    sequence (layer l on sequence l mod B, so the layers of a group meet
+    different sequences)."""
     w = synth.workload(wid)
     model, caches, dec, ql, qr = run_gpu(kk, w)
-    if samples is None:
-        # one layer of every bit width, an inheritor of the largest group, first and last sequence
-        picks = []
-        for b in (2, 4, 8, 16):
-            l = next(l for l in range(w.n_layers) if w.bits_eff(l) == b)
-            picks.append(l)
-        grp = max(w.anchors(), key=lambda a: sum(1 for s in w.layers if s.anchor == a))
-        picks.append(max(l for l in range(w.n_layers) if w.layers[l].anchor == grp))
-        samples = [(l, s) for i, l in enumerate(picks) for s in ((0, w.batch - 1) if i % 2 == 0 else (w.batch // 2,))]
-    worst = 0.0
-    for (l, s) in samples:
-        worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, w.seq_len))
-    print(f"workload {wid}: worst err ratio {worst:.2e} over {len(samples)} (layer, seq) samples")
+    anchors = w.anchors()
+    seqs_for_codes = (0, w.batch - 1)
+    src = {}
+    for a in anchors:
+        for s in seqs_for_codes:
+            src[(a, s)] = source_cpu(w, a, s)
+    n_codes = 0
+    for a in anchors:
+        for s in seqs_for_codes:
+            lat, rope = src[(a, s)]
+            packed, scales, _ = ko.write_cache(lat, rope, w.layers[a].d, w.layers[a].bits)
+            codes_gpu, scales_gpu = caches[a]
+            assert np.array_equal(codes_gpu[s].cpu().numpy(), packed), f"codes differ: anchor {a} seq {s}"
+            assert np.array_equal(scales_gpu[s].cpu().numpy().view(np.uint32), scales.view(np.uint32)), \
+                f"scales differ: anchor {a} seq {s}"
+            n_codes += 1
+    worst, n_out = 0.0, 0
+    for l in range(w.n_layers):
+        s = l % w.batch
+        a = w.layers[l].anchor
+        lat_rope = src.get((a, s)) or source_cpu(w, a, s)
+        worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, w.seq_len, {a: lat_rope}))
+        n_out += 1
+    assert n_codes == 2 * len(anchors) and n_out == w.n_layers
+    print(f"workload {wid} ({w.name}): codes and scales of {len(anchors)} anchors x 2 sequences bit-exact; "
+          f"{n_out} of {w.n_layers} layers within the bar, worst err ratio {worst:.2e}")
