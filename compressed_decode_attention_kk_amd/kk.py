@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libkk.so")
 
 KK_OK, KK_ERR_INVALID_ARGUMENT, KK_ERR_UNSUPPORTED, KK_ERR_WORKSPACE_TOO_SMALL, KK_ERR_DEVICE = range(5)
 KK_DTYPE_F32, KK_DTYPE_BF16 = 0, 1
+KK_NOALLOC_SCRATCH_BYTES = 256 << 20      # size of the array behind kk_decode_attn_noalloc
 
 
 class KKError(RuntimeError):
@@ -82,6 +83,10 @@ def lib():
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_size_t,
                                      ctypes.c_void_p]
+        L.kk_decode_attn_noalloc.argtypes = [ctypes.POINTER(ModelCfg), ctypes.POINTER(Cache), ctypes.c_int32,
+                                             ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_int32,
+                                             ctypes.c_void_p]
         L.kk_append_decode.argtypes = [ctypes.POINTER(ModelCfg), ctypes.POINTER(Cache), ctypes.c_int32,
                                        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
@@ -112,7 +117,8 @@ def lib():
         L.kk_status_string.restype = ctypes.c_char_p
         L.kk_status_string.argtypes = [ctypes.c_int]
         for name in ("kk_validate_model", "kk_cache_bytes", "kk_out_offsets", "kk_quantize_write",
-                     "kk_decode_workspace_bytes", "kk_decode_plan_info", "kk_decode_attn", "kk_append_decode", "kk_multi_out_offsets",
+                     "kk_decode_workspace_bytes", "kk_decode_plan_info", "kk_decode_attn", "kk_decode_attn_noalloc",
+                     "kk_append_decode", "kk_multi_out_offsets",
                      "kk_multi_decode_workspace_bytes", "kk_multi_decode_attn", "kk_latent_epilogue",
                      "kk_gqa_cache_bytes", "kk_gqa_quantize_write", "kk_gqa_decode_workspace_bytes",
                      "kk_gqa_decode_attn"):
@@ -311,6 +317,18 @@ class Decoder:
                                   _ptr(q_lat), _ptr(q_rope), _dtype_code(q_lat.dtype), _ptr(self.out),
                                   self.split_tokens, ctypes.c_void_p(wptr), self.ws_bytes, _stream(stream))
         _check(st, "kk_decode_attn")
+        return self.out
+
+    def noalloc(self, q_lat: torch.Tensor, q_rope: torch.Tensor, seq_lens: torch.Tensor, stream=None):
+        """kk_decode_attn_noalloc: the same step with the split partials in the
+        library's static device array (this object's workspace is not used)."""
+        m = self.model
+        _check_queries(q_lat, q_rope, m.n_layers, self.batch, m.n_heads, m.r, m.d_rope)
+        _check_lens(seq_lens, self.batch)
+        st = lib().kk_decode_attn_noalloc(m.cfg, self._ctab, self.batch, self.t_cap, _ptr(seq_lens),
+                                          self.max_seq_len, _ptr(q_lat), _ptr(q_rope), _dtype_code(q_lat.dtype),
+                                          _ptr(self.out), self.split_tokens, _stream(stream))
+        _check(st, "kk_decode_attn_noalloc")
         return self.out
 
     def append(self, new_latent: torch.Tensor, new_rope: torch.Tensor, q_lat: torch.Tensor, q_rope: torch.Tensor,

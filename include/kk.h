@@ -23,7 +23,9 @@
  *   - All device pointers are HIP device allocations owned by the caller.
  *     The library never allocates or frees device memory, never
  *     synchronizes, and keeps no mutable global state (planning uses host
- *     memory local to the call); calls are thread-safe.
+ *     memory local to the call); calls are thread-safe.  The one exception is
+ *     kk_decode_attn_noalloc, which keeps its partials in a static device
+ *     array per device (see there).
  *   - Every call validates its arguments on the host before enqueueing
  *     anything; a non-KK_OK status means nothing was enqueued.
  *   - Work is enqueued on the caller's stream and returns asynchronously;
@@ -234,6 +236,38 @@ kk_status kk_decode_attn(const kk_model_cfg* cfg, const kk_cache* caches, int32_
                          const void* q_lat, const void* q_rope, kk_dtype q_dtype, float* out,
                          int32_t split_tokens, void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* Size of the device array that kk_decode_attn_noalloc keeps its split
+ * partials in: 256 MiB, held on each device the entry point runs on until the
+ * process ends.  It covers the automatic plan (split_tokens = 0) of 32
+ * sequences of 8192 tokens on the 7B (28 layers, d = 512, b = 16: 227 MiB)
+ * and 14B (48 layers, mixed table: 159 MiB) shapes on a 256-CU device;
+ * kk_decode_workspace_bytes gives the need of any other step. */
+#define KK_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+
+/* kk_decode_attn without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, checks, kernels, results
+ * and error statuses as kk_decode_attn; the split partials go to a static
+ * device array of KK_NOALLOC_SCRATCH_BYTES instead of a workspace.
+ *   - Calls no hipMalloc, hipFree or other device-allocating routine.  The
+ *     first call on a device looks the array's device address up
+ *     (hipGetSymbolAddress, device switched to the stream's device and back)
+ *     and may load its code object: make that first call outside stream
+ *     capture.
+ *   - KK_ERR_WORKSPACE_TOO_SMALL, with nothing enqueued, when the step needs
+ *     more than KK_NOALLOC_SCRATCH_BYTES (kk_decode_workspace_bytes with the
+ *     same batch, max_seq_len and split_tokens on the same device); pass a
+ *     larger split_tokens or use kk_decode_attn.
+ *   - Every call on one device shares that device's array: calls that overlap
+ *     in time on one device (two streams, or two host threads) race and give
+ *     wrong results.  Calls on one stream are ordered and safe.  Nothing in
+ *     the array has to start at zero: each step writes every partial it reads.
+ *   - KK_ERR_UNSUPPORTED for device ordinals >= 64. */
+kk_status kk_decode_attn_noalloc(const kk_model_cfg* cfg, const kk_cache* caches, int32_t batch, int32_t t_cap,
+                                 const int32_t* seq_lens, int32_t max_seq_len,
+                                 const void* q_lat, const void* q_rope, kk_dtype q_dtype, float* out,
+                                 int32_t split_tokens, hipStream_t stream);
 
 /* One generated token per sequence: append it to every anchor cache, then
  * attend (the decode step right after the write; KV-Kaizen summary page,

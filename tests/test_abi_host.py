@@ -40,6 +40,14 @@ def test_header_declares_the_entry_points():
         assert n in names
 
 
+def test_noalloc_scratch_size_matches_header(kk):
+    import re
+    hdr = open(os.path.join(ROOT, "include", "kk.h")).read()
+    m = re.search(r"#define KK_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", hdr)
+    assert m, "KK_NOALLOC_SCRATCH_BYTES not found in kk.h"
+    assert int(m.group(1)) << int(m.group(2)) == kk.KK_NOALLOC_SCRATCH_BYTES
+
+
 def test_library_exports_every_declared_function(kk):
     L = ctypes.CDLL(kk.LIB_PATH)
     missing = [n for n in declared_functions() if not hasattr(L, n)]
