@@ -86,31 +86,8 @@ constexpr int kScaleHeadroom = 6;    // scales may exceed 2^E by 2^6 before E is
 constexpr int kCopyRounds = 5;
 static_assert((32 * kMaxK / 1024 + kWaves - 1) / kWaves <= kCopyRounds, "copy rounds too few for K");
 
-// ---- LDS map (bytes, dynamic shared memory) ----------------------------------
-//  [0, nbuf*buf)  tile buffers: codes of token block 0 [| block 1] | slack | scales
-//  pbuf           P' fragments [tile parity][row block][64 lanes] 8 B per 16 tokens
-//  alpha[2][64] flags[2][4] ml[64][2] misc[16]
-constexpr int kMiscBytes = 2 * 64 * 4 + 2 * 4 * 4 + 64 * 8 + 64;
-__host__ __device__ inline int pbuf_bytes(int rb, int tile_blocks) { return 2 * rb * 64 * 8 * tile_blocks; }
-
-__host__ __device__ inline int nseg_of(int row_stride) { return row_stride >> 4; }
-// 16-byte segments a tile row needs for the Q.K reads: latent chunks read 64
-// fields from field 0, RoPE chunks 64 fields from field d, so reads reach field
-// F = max(64 * latent chunks, d + 64 * RoPE chunks) (past the row's own fields
-// they meet zero query values); b = 16 reads both byte planes (low plane at K).
-__host__ __device__ inline int nsegpad_of(int d, int d_rope, int bits) {
-  const int fl = ((d + 63) >> 6) * 64, fr = d + ((d_rope + 63) >> 6) * 64;
-  const int F = fl > fr ? fl : fr;
-  return bits == 16 ? (d + d_rope + F + 15) >> 4 : (F * bits / 8 + 15) >> 4;
-}
-// 16-token blocks per tile (see tile_blocks below)
-__host__ __device__ inline int tile_blocks_of(int bits) { return bits == 16 ? 1 : 2; }
-// Tile buffer: all but the last token block at full pitch, the last one padded
-// for whole-chunk Q.K reads, then the tile's fp32 scales (4 bytes per token).
-__host__ __device__ inline int tilebuf_bytes(int row_stride, int d, int d_rope, int bits) {
-  const int nseg = nseg_of(row_stride), pad = nsegpad_of(d, d_rope, bits), tb = tile_blocks_of(bits);
-  return ((tb - 1) * nseg + (pad > nseg ? pad : nseg)) * 256 + 64 * tb;
-}
+// The LDS map (tile buffers, P' fragments, softmax state) and its sizes are in
+// kk_internal.h, shared with the host planner.
 
 // ---- operand conversions ------------------------------------------------------
 __device__ inline h2 as_h2(uint32_t x) { return __builtin_bit_cast(h2, x); }
@@ -1221,17 +1198,6 @@ hipError_t launch_one(const DecodeArgs& a, int n, int lds, hipStream_t stream) {
 
 // Tile buffers per workgroup: as many as fit in the workgroup's share of the
 // 160 KB LDS, 3 to 12 (two tiles are in use, the rest in flight).
-int decode_nbuf(int row_stride, int d, int d_rope, int bits, int rb, int variant) {
-  const int budget = 160 * 1024 / decode_wg_per_cu(variant) - pbuf_bytes(rb, tile_blocks_of(bits)) - kMiscBytes;
-  const int n = budget / tilebuf_bytes(row_stride, d, d_rope, bits);
-  return n < 3 ? 3 : (n > 12 ? 12 : n);
-}
-
-int decode_lds_bytes(int row_stride, int d, int d_rope, int bits, int rb, int variant) {
-  return decode_nbuf(row_stride, d, d_rope, bits, rb, variant) * tilebuf_bytes(row_stride, d, d_rope, bits) +
-         pbuf_bytes(rb, tile_blocks_of(bits)) + kMiscBytes;
-}
-
 hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t stream) {
   static_assert(sizeof(DecodeArgs) < 7600, "kernel argument block too large");
   if (L.items > 0) {

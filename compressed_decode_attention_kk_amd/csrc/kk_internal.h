@@ -171,8 +171,43 @@ struct DecodeLaunch {
   int variant = kFull;   // kernel variant (kGqa: row_blocks <= 2)
 };
 
-int decode_nbuf(int row_stride, int d, int d_rope, int bits, int row_blocks, int variant);
-int decode_lds_bytes(int row_stride, int d, int d_rope, int bits, int row_blocks, int variant);
+// ---- LDS map of the decode kernel (bytes of dynamic shared memory) ----------------
+//  [0, nbuf*buf)  tile buffers: codes of token block 0 [| block 1] | slack | scales
+//  pbuf           P' fragments [tile parity][row block][64 lanes] 8 B per 16 tokens
+//  alpha[2][64] flags[2][4] ml[64][2] misc[16]
+constexpr int kMiscBytes = 2 * 64 * 4 + 2 * 4 * 4 + 64 * 8 + 64;
+__host__ __device__ inline int pbuf_bytes(int rb, int tile_blocks) { return 2 * rb * 64 * 8 * tile_blocks; }
+
+__host__ __device__ inline int nseg_of(int row_stride) { return row_stride >> 4; }
+// 16-byte segments a tile row needs for the Q.K reads: latent chunks read 64
+// fields from field 0, RoPE chunks 64 fields from field d, so reads reach field
+// F = max(64 * latent chunks, d + 64 * RoPE chunks) (past the row's own fields
+// they meet zero query values); b = 16 reads both byte planes (low plane at K).
+__host__ __device__ inline int nsegpad_of(int d, int d_rope, int bits) {
+  const int fl = ((d + 63) >> 6) * 64, fr = d + ((d_rope + 63) >> 6) * 64;
+  const int F = fl > fr ? fl : fr;
+  return bits == 16 ? (d + d_rope + F + 15) >> 4 : (F * bits / 8 + 15) >> 4;
+}
+// 16-token blocks per tile: 32 tokens of b <= 8 codes, 16 tokens of b = 16 codes
+__host__ __device__ inline int tile_blocks_of(int bits) { return bits == 16 ? 1 : 2; }
+// Tile buffer: all but the last token block at full pitch, the last one padded
+// for whole-chunk Q.K reads, then the tile's fp32 scales (4 bytes per token).
+__host__ __device__ inline int tilebuf_bytes(int row_stride, int d, int d_rope, int bits) {
+  const int nseg = nseg_of(row_stride), pad = nsegpad_of(d, d_rope, bits), tb = tile_blocks_of(bits);
+  return ((tb - 1) * nseg + (pad > nseg ? pad : nseg)) * 256 + 64 * tb;
+}
+// Tile buffers of an entry: as many as fit in the LDS share of one workgroup
+// (160 KiB per CU over the variant's workgroups), 3 to 12.
+inline int decode_nbuf(int row_stride, int d, int d_rope, int bits, int row_blocks, int variant) {
+  const int budget =
+      160 * 1024 / decode_wg_per_cu(variant) - pbuf_bytes(row_blocks, tile_blocks_of(bits)) - kMiscBytes;
+  const int n = budget / tilebuf_bytes(row_stride, d, d_rope, bits);
+  return n < 3 ? 3 : (n > 12 ? 12 : n);
+}
+inline int decode_lds_bytes(int row_stride, int d, int d_rope, int bits, int row_blocks, int variant) {
+  return decode_nbuf(row_stride, d, d_rope, bits, row_blocks, variant) * tilebuf_bytes(row_stride, d, d_rope, bits) +
+         pbuf_bytes(row_blocks, tile_blocks_of(bits)) + kMiscBytes;
+}
 hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t stream);
 
 // Copies `words` 32-bit words from host memory to device memory `dst` by

@@ -20,8 +20,17 @@ HEADER = os.path.join(ROOT, "include", "kk.h")
 @pytest.fixture(scope="module")
 def kk():
     import compressed_decode_attention_kk_amd as kk
+    alt = os.environ.get("KK_HOST_TEST_LIB")
+    if alt:
+        # the host-only sanitizer build (see test_host_sanitizers.py)
+        kk.kk._lib = None
+        kk.kk.LIB_PATH = kk.LIB_PATH = alt
     kk.lib()
     return kk
+
+
+def test_report_library(kk):
+    print("sanitized build" if os.environ.get("KK_HOST_TEST_LIB") else "library", kk.LIB_PATH)
 
 
 def declared_functions():
