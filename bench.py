@@ -147,6 +147,125 @@ def traffic_from(fetch_csv, write_csv, copy_mib, workload_name):
     return rec
 
 
+def _short_kernel(name):
+    """'void kk::(anonymous namespace)::decode_kernel<3, 0>(kk::DecodeArgs)' -> 'decode_kernel<3, 0>'."""
+    import re
+    m = re.search(r"(\w+(?:<[^()]*>)?)\(", name)
+    return m.group(1) if m else name[:60]
+
+
+STEP_KERNELS = ("append_kernel", "store_kernel", "decode_kernel", "merge_kernel", "gemm_kernel", "gemm_lds_kernel")
+
+
+def trace_summary(trace_csv, steps, warmup, kernels=STEP_KERNELS):
+    """Durations of the step's kernels in a rocprofv3 --kernel-trace CSV of
+    `bench.py --steps K --warmup W`: of each kernel in `kernels` (the cache
+    writes of the set-up are not among them), the last K * (calls per step)
+    dispatches are the timed ones.  Returns markdown."""
+    import csv
+    import statistics
+    with open(trace_csv) as f:
+        rows = [r for r in csv.DictReader(f) if "kk::" in r["Kernel_Name"] and
+                _short_kernel(r["Kernel_Name"]).split("<")[0] in kernels]
+    by = {}
+    for r in rows:
+        by.setdefault(_short_kernel(r["Kernel_Name"]), []).append(r)
+    lines = ["| kernel | VGPR | AGPR | SGPR | static LDS B | scratch B | workgroups | timed calls | avg us | min us | "
+             "p50 us | max us | all calls | all avg us |", "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    timed_all = []
+    for k, rs in sorted(by.items(), key=lambda kv: -sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                                                       for r in kv[1])):
+        rs.sort(key=lambda r: int(r["Start_Timestamp"]))
+        per_step = max(1, round(len(rs) / (steps + warmup)))
+        timed = rs[-steps * per_step:]
+        timed_all += timed
+        us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]
+        us_all = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rs]
+        r0 = rs[-1]
+        wgs = int(r0["Grid_Size_X"]) // max(int(r0["Workgroup_Size_X"]), 1)
+        lines.append(f"| {k} | {r0['VGPR_Count']} | {r0['Accum_VGPR_Count']} | {r0['SGPR_Count']} | "
+                     f"{r0['LDS_Block_Size']} | {r0['Scratch_Size']} | {wgs} | {len(us)} | "
+                     f"{sum(us) / len(us):.1f} | {min(us):.1f} | {statistics.median(us):.1f} | {max(us):.1f} | "
+                     f"{len(us_all)} | {sum(us_all) / len(us_all):.1f} |")
+    timed_all.sort(key=lambda r: int(r["Start_Timestamp"]))
+    n = len(timed_all) // steps
+    busy, span = [], []
+    for i in range(steps):
+        g = timed_all[i * n:(i + 1) * n]
+        busy.append(sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in g) / 1e3)
+        span.append((max(int(r["End_Timestamp"]) for r in g) - min(int(r["Start_Timestamp"]) for r in g)) / 1e3)
+    lines.append("")
+    lines.append(f"Timed steps: {steps} ({n} library dispatches each). Per step, sum of kernel durations: "
+                 f"avg {sum(busy) / steps:.1f} us (min {min(busy):.1f}, max {max(busy):.1f}); first start to "
+                 f"last end: avg {sum(span) / steps:.1f} us.")
+    return "\n".join(lines)
+
+
+def pmc_summary(csvs, kernel="decode_kernel", n_cus=256, n_xcds=8):
+    """Counters of the `kernel` dispatches in rocprofv3 --pmc CSVs (one pass per
+    file), averaged over those dispatches, with derived rates.  Returns markdown.
+    Normalisation (stated with each rate): GRBM_GUI_ACTIVE sums the 8 XCDs, so
+    kernel cycles = GRBM_GUI_ACTIVE / 8; the SQ *_CYCLES counters count per
+    SIMD in units of 4 cycles where noted."""
+    import csv
+    vals = {}
+    names = set()
+    for path in csvs:
+        per = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if kernel not in r["Kernel_Name"]:
+                    continue
+                names.add(_short_kernel(r["Kernel_Name"]))
+                key = (r["Dispatch_Id"], r["Counter_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (d, c), v in per.items():
+            vals.setdefault(c, []).append(v)
+    avg = {c: sum(v) / len(v) for c, v in vals.items()}
+    lines = [f"Kernel: {', '.join(sorted(names))}; dispatches per pass: "
+             f"{max(len(v) for v in vals.values()) if vals else 0}", "",
+             "| counter | mean per dispatch |", "|---|---|"]
+    for c in sorted(avg):
+        lines.append(f"| {c} | {avg[c]:.4g} |")
+    der = []
+    cyc = avg.get("GRBM_GUI_ACTIVE", 0.0) / n_xcds
+    simds = 4 * n_cus
+    waves = avg.get("SQ_WAVES")
+    if cyc:
+        der.append(("kernel cycles (GRBM_GUI_ACTIVE / 8 XCDs)", f"{cyc:.4g}"))
+    if waves:
+        for c in ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_SMEM",
+                  "SQ_INSTS_BRANCH"):
+            if c in avg:
+                der.append((f"{c} per wave", f"{avg[c] / waves:.1f}"))
+    if "SQ_INSTS_VALU" in avg and "SQ_INSTS_MFMA" in avg and avg["SQ_INSTS_MFMA"]:
+        der.append(("VALU instructions per MFMA instruction", f"{avg['SQ_INSTS_VALU'] / avg['SQ_INSTS_MFMA']:.2f}"))
+    if cyc and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        der.append(("MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x cycles)",
+                    f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / (simds * cyc):.3f}"))
+    if cyc and "SQ_ACTIVE_INST_VALU" in avg:
+        der.append(("VALU active: 4 x SQ_ACTIVE_INST_VALU / (SIMDs x cycles)",
+                    f"{4 * avg['SQ_ACTIVE_INST_VALU'] / (simds * cyc):.3f}"))
+    if cyc and "SQ_WAVE_CYCLES" in avg:
+        der.append(("mean resident waves per CU: 4 x SQ_WAVE_CYCLES / (CUs x cycles)",
+                    f"{4 * avg['SQ_WAVE_CYCLES'] / (n_cus * cyc):.2f}"))
+    if avg.get("SQ_ACTIVE_INST_LDS"):
+        der.append(("LDS bank-conflict cycles per LDS-active cycle: SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS",
+                    f"{avg.get('SQ_LDS_BANK_CONFLICT', 0.0) / avg['SQ_ACTIVE_INST_LDS']:.4f}"))
+    if cyc and "SQ_LDS_BANK_CONFLICT" in avg:
+        der.append(("LDS bank-conflict cycles per CU cycle: SQ_LDS_BANK_CONFLICT / (CUs x cycles)",
+                    f"{avg['SQ_LDS_BANK_CONFLICT'] / (n_cus * cyc):.4f}"))
+    if "TCC_HIT_sum" in avg and "TCC_MISS_sum" in avg and avg["TCC_HIT_sum"] + avg["TCC_MISS_sum"]:
+        der.append(("L2 hit rate: TCC_HIT / (TCC_HIT + TCC_MISS)",
+                    f"{avg['TCC_HIT_sum'] / (avg['TCC_HIT_sum'] + avg['TCC_MISS_sum']):.3f}"))
+    if "SQ_WAIT_INST_ANY" in avg and avg.get("SQ_WAVE_CYCLES"):
+        der.append(("share of wave time waiting on any dependency: SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES",
+                    f"{avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.3f}"))
+    if der:
+        lines += ["", "| derived | value |", "|---|---|"] + [f"| {a} | {b} |" for a, b in der]
+    return "\n".join(lines)
+
+
 def copy_bandwidth(torch, mib: int = 1024, reps: int = 5) -> float:
     """Measured device-to-device copy rate (GB/s, bytes read + written) on the
     launch stream: the practical streaming ceiling the achieved rate is set
@@ -245,7 +364,18 @@ def main():
                     help="after timing, run 3 device-to-device copies of this size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from two rocprofv3 counter CSVs and exit")
+    ap.add_argument("--trace-from", metavar="KERNEL_TRACE_CSV",
+                    help="summarize the timed dispatches of a rocprofv3 --kernel-trace CSV of a run with the same "
+                         "--steps and --warmup, and exit")
+    ap.add_argument("--pmc-from", nargs="+", metavar="COUNTER_CSV",
+                    help="summarize rocprofv3 --pmc CSVs (one pass each) for the decode kernel, and exit")
     args = ap.parse_args()
+    if args.trace_from:
+        print(trace_summary(args.trace_from, args.steps, args.warmup))
+        return
+    if args.pmc_from:
+        print(pmc_summary(args.pmc_from))
+        return
     if args.traffic_from:
         import synth
         w = synth.workload(args.workload)

@@ -77,3 +77,69 @@ def test_more_than_one_gpu_is_refused():
                        text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def _write_trace(path, rows):
+    cols = ["Kind", "Agent_Id", "Queue_Id", "Stream_Id", "Thread_Id", "Dispatch_Id", "Kernel_Id", "Kernel_Name",
+            "Correlation_Id", "Start_Timestamp", "End_Timestamp", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+            "Accum_VGPR_Count", "SGPR_Count", "Workgroup_Size_X", "Workgroup_Size_Y", "Workgroup_Size_Z",
+            "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"]
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(cols)
+        for i, (name, t0, t1) in enumerate(rows):
+            wr.writerow(["KERNEL_DISPATCH", "Agent 1", 1, 0, 1, i + 1, 7, name, i + 1, t0, t1, 0, 0, 128, 0, 96,
+                         256, 1, 1, 256 * 100, 1, 1])
+
+
+def test_trace_summary_times_the_timed_dispatches_only(tmp_path):
+    """Set-up writes, 2 warmup steps (slow), then 3 timed steps of decode +
+    merge: only the last 3 of each kernel are averaged; the per-step sums
+    and spans follow from the timestamps (ns)."""
+    dec = "void kk::(anonymous namespace)::decode_kernel<3, 0>(kk::DecodeArgs)"
+    mrg = "void kk::(anonymous namespace)::merge_kernel(kk::DecodeArgs)"
+    wr = "void kk::(anonymous namespace)::write_kernel<4>(kk::WriteArgs)"
+    rows, t = [], 0
+    for _ in range(5):
+        rows.append((wr, t, t + 1000)); t += 2000
+    for step, d in enumerate([9000, 8000, 1000, 1200, 1400]):     # warmup 2, timed 3 (us * 1000)
+        rows.append((dec, t, t + d)); t += d
+        rows.append((mrg, t, t + 100)); t += 100 + 50000
+    f = tmp_path / "trace.csv"
+    _write_trace(f, rows)
+    md = bench.trace_summary(str(f), steps=3, warmup=2)
+    line = [l for l in md.splitlines() if l.startswith("| decode_kernel<3, 0>")][0].split("|")
+    assert line[8].strip() == "3" and float(line[9]) == pytest.approx(1.2)       # timed calls, avg us
+    assert float(line[10]) == pytest.approx(1.0) and float(line[12]) == pytest.approx(1.4)
+    assert "write_kernel" not in md
+    assert "sum of kernel durations: avg 1.3 us" in md and "last end: avg 1.3 us" in md
+
+
+def test_pmc_summary_derives_the_rates(tmp_path):
+    """Two dispatches of the decode kernel with fixed counters: per-wave
+    counts and the normalised rates follow the stated formulas."""
+    dec = "void kk::(anonymous namespace)::decode_kernel<3, 0>(kk::DecodeArgs)"
+    cnt = {"SQ_WAVES": 1000.0, "SQ_INSTS_VALU": 5.0e6, "SQ_INSTS_MFMA": 1.0e6, "GRBM_GUI_ACTIVE": 8.0e6,
+           "SQ_VALU_MFMA_BUSY_CYCLES": 0.25 * 1024 * 1.0e6, "SQ_ACTIVE_INST_VALU": 0.5 / 4 * 1024 * 1.0e6,
+           "SQ_WAVE_CYCLES": 7.0 / 4 * 256 * 1.0e6, "TCC_HIT_sum": 30.0, "TCC_MISS_sum": 70.0,
+           "SQ_LDS_BANK_CONFLICT": 5.0, "SQ_ACTIVE_INST_LDS": 50.0}
+    cols = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+            "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+            "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    f = tmp_path / "pmc.csv"
+    with open(f, "w", newline="") as fh:
+        wr = csv.writer(fh)
+        wr.writerow(cols)
+        for disp in (1, 2):
+            for c, v in cnt.items():
+                wr.writerow([disp, disp, "Agent 1", 1, 1, 1, 256, 7, dec, 256, 0, 0, 128, 0, 96, c, v, 0, 1])
+            wr.writerow([disp, disp, "Agent 1", 1, 1, 1, 256, 8, "other", 256, 0, 0, 8, 0, 16, "SQ_WAVES", 1.0, 0, 1])
+    md = bench.pmc_summary([str(f)])
+    vals = {l.split("|")[1].strip(): l.split("|")[2].strip() for l in md.splitlines() if l.count("|") == 3}
+    assert float(vals["kernel cycles (GRBM_GUI_ACTIVE / 8 XCDs)"]) == pytest.approx(1.0e6)
+    assert float(vals["SQ_INSTS_VALU per wave"]) == pytest.approx(5000.0)
+    assert float(vals["VALU instructions per MFMA instruction"]) == pytest.approx(5.0)
+    assert float(vals["MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x cycles)"]) == pytest.approx(0.25)
+    assert float(vals["VALU active: 4 x SQ_ACTIVE_INST_VALU / (SIMDs x cycles)"]) == pytest.approx(0.5)
+    assert float(vals["mean resident waves per CU: 4 x SQ_WAVE_CYCLES / (CUs x cycles)"]) == pytest.approx(7.0)
+    assert float(vals["L2 hit rate: TCC_HIT / (TCC_HIT + TCC_MISS)"]) == pytest.approx(0.3)
