@@ -394,7 +394,11 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   static_assert(RB < kWaves, "at least one wave without Q.K rows");
   {
     const int npv = kWaves - RB;
-    int uq = max((NU * 3) / 16, (NU - npv * pv_units_max<RB, V>() + RB - 1) / RB);
+    // Q.K waves carry the longer stage, so they take output units only when
+    // the other waves cannot hold them all (the full variant keeps at least
+    // 3/16 of them on the Q.K waves: its P.V wave's registers are the limit)
+    int uq = (NU - npv * pv_units_max<RB, V>() + RB - 1) / RB;
+    if constexpr (V != kLean) uq = max((NU * 3) / 16, uq);
     uq = min(max(uq, 0), qk_units_max<RB, V>());
     const int rest = NU - RB * uq;
     const int per = (rest + npv - 1) / npv;
@@ -932,6 +936,13 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       if (!done && NRq == 1 && KC == kMaxC && ucount == UMAX) {
         stage_loop(std::integral_constant<int, kMaxC>{}, std::integral_constant<int, 1>{}, std::integral_constant<int, UMAX>{});
         done = true;
+      }
+      if constexpr (V == kLean) {
+        // lean Q.K waves without output units (their P.V waves hold them all)
+        if (!done && NRq == 1 && KC == kMaxC && ucount == 0) {
+          stage_loop(std::integral_constant<int, kMaxC>{}, std::integral_constant<int, 1>{}, I0{});
+          done = true;
+        }
       }
     } else {
       // waves without Q.K rows: one loop per unit count
