@@ -469,12 +469,16 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       const float sm = my_layer >= 0 ? layer_at(A, my_layer).sm_scale : 0.0f;
       float preL = 0.0f, preR = 0.0f, mxL = 0.0f, mxR = 0.0f;
       int qsumL = 0, qsumR = 0;                   // sums of the fixed-point q per part
-      auto quantize = [&](auto f32_tag) {
+      // NRQ >= 0: the RoPE chunk count known at compile time (bf16 queries), so
+      // that each chunk's limb code is its own; NRQ < 0: NRq at run time
+      auto quantize = [&](auto f32_tag, auto nrq_tag) {
         constexpr bool F32 = decltype(f32_tag)::value;
+        constexpr int NRQ = decltype(nrq_tag)::value;
+        auto is_lat = [&](int c) { return NRQ >= 0 ? c >= NRQ : lat[c]; };
         u4 raw[F32 ? 1 : kMaxC][2];
         auto get = [&](int c, float (&x)[16]) {
           if constexpr (F32) {
-            const f4* p = (const f4*)((const float*)(lat[c] && !GQA ? A.q_lat : A.q_rope) + off[c]);
+            const f4* p = (const f4*)((const float*)(is_lat(c) && !GQA ? A.q_lat : A.q_rope) + off[c]);
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               const f4 t = p[v];
@@ -494,7 +498,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
         if constexpr (!F32) {
 #pragma unroll
           for (int c = 0; c < kMaxC; ++c) {
-            const u4* p = (const u4*)((const uint16_t*)(lat[c] && !GQA ? A.q_lat : A.q_rope) + off[c]);
+            const u4* p = (const u4*)((const uint16_t*)(is_lat(c) && !GQA ? A.q_lat : A.q_rope) + off[c]);
 #pragma unroll
             for (int v = 0; v < 2; ++v) raw[c][v] = p[v];
           }
@@ -505,7 +509,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           get(c, x);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            if (lat[c]) mxL = fmaxf(mxL, fabsf(x[i]));
+            if (is_lat(c)) mxL = fmaxf(mxL, fabsf(x[i]));
             else mxR = fmaxf(mxR, fabsf(x[i]));
           }
         }
@@ -521,18 +525,18 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           float x[16];
           get(c, x);
           uint32_t hw[4] = {0, 0, 0, 0}, mw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
-          const float pre = lat[c] ? preL : preR;
+          const float pre = is_lat(c) ? preL : preR;
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             // latent: qi = 128 hi + lo, |qi| <= 16256; RoPE: qi = 16384 hi + 128 mid + lo,
             // |qi| <= 16256 * 128 (floor divisions: hi in [-127, 127], mid in [-64, 64],
             // lo in [-64, 63])
             const int qi = (int)rintf(x[qk_slot_feature<BITS>(i)] * pre);
-            const int hi = lat[c] ? (qi + 64) >> 7 : (qi + 8192) >> 14;
-            const int rest = lat[c] ? 0 : qi - (hi << 14);
+            const int hi = is_lat(c) ? (qi + 64) >> 7 : (qi + 8192) >> 14;
+            const int rest = is_lat(c) ? 0 : qi - (hi << 14);
             const int mid = (rest + 64) >> 7;
-            const int lo = lat[c] ? qi - (hi << 7) : rest - (mid << 7);
-            if (lat[c]) qsumL += qi; else qsumR += qi;
+            const int lo = is_lat(c) ? qi - (hi << 7) : rest - (mid << 7);
+            if (is_lat(c)) qsumL += qi; else qsumR += qi;
             hw[i >> 2] |= ((uint32_t)hi & 0xFFu) << (8 * (i & 3));
             mw[i >> 2] |= ((uint32_t)mid & 0xFFu) << (8 * (i & 3));
             lw[i >> 2] |= ((uint32_t)lo & 0xFFu) << (8 * (i & 3));
@@ -542,8 +546,10 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           if (c < kMaxRopeChunks) qm[c < kMaxRopeChunks ? c : 0] = i4{(int)mw[0], (int)mw[1], (int)mw[2], (int)mw[3]};
         }
       };
-      if (A.q_is_f32) quantize(std::true_type{});
-      else quantize(std::false_type{});
+      if (A.q_is_f32) quantize(std::true_type{}, std::integral_constant<int, -1>{});
+      else if constexpr (GQA) quantize(std::false_type{}, std::integral_constant<int, 0>{});
+      else if (NRq == 1) quantize(std::false_type{}, std::integral_constant<int, 1>{});
+      else quantize(std::false_type{}, std::integral_constant<int, 2>{});
       // scores are taken in units of the latent prescale (the RoPE one when the
       // latent part is zero); rowf >= FLT_MIN: a zero scale (or a padding row,
       // q = 0) still maps the masked tokens' t = -inf to z = -inf.
