@@ -351,13 +351,25 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   // The copy loop runs on scalar registers: wave index, tile base address and
   // LDS addresses are wave-uniform; each lane only adds its 32-bit offset.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int copies = __builtin_amdgcn_readfirstlane((ninst > wave_u ? (ninst - wave_u + kWaves - 1) / kWaves : 0) +
-                                                    (wave_u == kWaves - 1 ? 1 : 0));
+  // Copy i of a tile goes to wave i mod 4, except with three Q.K waves: their
+  // stages are the longest, so the P.V wave takes half of the copies (i mod 6
+  // in {3, 4, 5}) and Q.K wave w the copies i = w mod 6.
+  constexpr bool kPvCopies = RB == 3;
+  static_assert(!kPvCopies || (32 * kMaxK / 1024 + 1) / 2 <= 9, "copy rounds too few for K");
+  int my_copies;
+  if constexpr (kPvCopies) {
+    auto qk_share = [&](int w) { return ninst > w ? (ninst - w + 5) / 6 : 0; };
+    my_copies = wave_u < 3 ? qk_share(wave_u) : ninst - qk_share(0) - qk_share(1) - qk_share(2);
+  } else {
+    my_copies = ninst > wave_u ? (ninst - wave_u + kWaves - 1) / kWaves : 0;
+  }
+  const int copies = __builtin_amdgcn_readfirstlane(my_copies + (wave_u == kWaves - 1 ? 1 : 0));
   const uint32_t lds0 = lds_addr(lds);
   const int rstride = E.row_stride;
   const uint8_t* item_codes = (const uint8_t*)uniform_ptr(codes + row0 * (int64_t)rstride);
   const float* item_scales = (const float*)uniform_ptr(scales + row0);
-  auto issue_tile = [&](int it, int slotb) {
+  auto issue_tile = [&](int it, int slotb, auto qk_tag) {
+    constexpr bool QK_ROLE = decltype(qk_tag)::value;      // issued by a wave with Q.K rows
     const uint32_t buf = lds0 + slotb * bufbytes;
     const int tok0 = it * TILE;
     const int tlast = min(TILE, ntok - tok0) - 1;
@@ -368,8 +380,9 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int k = 0; k < kCopyRounds; ++k) {       // straight-line: one exit branch, not a loop
-      const int i = wave_u + kWaves * k;
+    for (int k = 0; k < (kPvCopies ? (QK_ROLE ? 3 : 9) : kCopyRounds); ++k) {   // straight-line: one exit branch
+      const int i = !kPvCopies ? wave_u + kWaves * k
+                               : QK_ROLE ? wave_u + 6 * k : 3 + 6 * (k / 3) + k % 3;   // increasing in k
       if (i >= ninst) break;
       const int p = i * 64 + ln;
       const int tb = (TB == 2 && p >= block_pieces) ? 1 : 0;
@@ -386,7 +399,8 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
       copy4_to_lds((uint32_t)(min(lane, tlast) * 4), item_scales + tok0, buf + TB * PITCH);
   };
   // prologue: tiles 0 .. nbuf-3; stage st issues tile st + nbuf - 1
-  for (int it = 0; it < nbuf - 2 && it < ntiles; ++it) issue_tile(it, it);
+  // (the prologue copies, tiles 0 .. nbuf-3, are issued by each role at the
+  // start of its pipeline below)
 
   // ---- P.V output units of this wave ---------------------------------------------
   const int NU = (d + 31) >> 5;
@@ -423,6 +437,8 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   auto pipeline = [&](auto qkw_tag, auto umax_tag) {
     constexpr bool QKW = decltype(qkw_tag)::value;
     constexpr int UMAX = decltype(umax_tag)::value;
+    // prologue: tiles 0 .. nbuf-3; stage st issues tile st + nbuf - 1
+    for (int it = 0; it < nbuf - 2 && it < ntiles; ++it) issue_tile(it, it, qkw_tag);
     const int my_row = 16 * wave + n;
     const int rope_field0 = d + 16 * g;           // first RoPE field of this lane's Q.K features
     const int lat_field0 = (GQA ? d : 0) + 16 * g;  // first field of its two-limb chunks
@@ -582,7 +598,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
     for (int st = -1; st < ntiles; ++st) {
       if (st + 1 < ntiles) vm_wait(min(nbuf - 3, ntiles - 2 - st) * copies);  // tile st+1 has landed
       lds_barrier();                  // tile st+1 visible; P'(st) written; P.V(st-1) done everywhere
-      if (st + nbuf - 1 < ntiles) issue_tile(st + nbuf - 1, slot_issue);
+      if (st + nbuf - 1 < ntiles) issue_tile(st + nbuf - 1, slot_issue, qkw_tag);
       slot_issue = slot_issue + 1 == nbuf ? 0 : slot_issue + 1;
 
       // ---- P.V of tile st (every wave, its own output units) ----
