@@ -351,18 +351,35 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   // The copy loop runs on scalar registers: wave index, tile base address and
   // LDS addresses are wave-uniform; each lane only adds its 32-bit offset.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  // Copy i of a tile goes to wave i mod 4, except with three Q.K waves: their
-  // stages are the longest, so the P.V wave takes half of the copies (i mod 6
-  // in {3, 4, 5}) and Q.K wave w the copies i = w mod 6.
-  constexpr bool kPvCopies = RB == 3;
-  static_assert(!kPvCopies || (32 * kMaxK / 1024 + 1) / 2 <= 9, "copy rounds too few for K");
-  int my_copies;
+  // Copy i of a tile goes to wave i mod 4, except with two or three Q.K
+  // waves: their stages are the longest, so over a period of kCopyPeriod
+  // copies Q.K wave w takes only copy w and the waves without Q.K rows share
+  // the rest (wave RB + j takes residues RB + j, RB + j + (4 - RB), ...).
+  // (a period of 6 measured best for two and three Q.K waves: 5, 7, 8 and 9
+  // were as fast or slower; at 9 the P.V wave becomes the last to arrive)
+  constexpr int kCopyPeriod = RB >= 2 ? 6 : kWaves;
+  constexpr bool kPvCopies = kCopyPeriod != kWaves;
+  constexpr int kNpv = kWaves - RB;
+  // residues of P.V wave j, and its copy index in round k
+  auto pv_residues = [&](int j) { return (kCopyPeriod - RB - j + kNpv - 1) / kNpv; };
+  auto pv_index = [&](int j, int k) {
+    const int R = pv_residues(j);
+    return kCopyPeriod * (k / R) + RB + j + kNpv * (k % R);
+  };
+  auto count_residue = [&](int r) { return ninst > r ? (ninst - r + kCopyPeriod - 1) / kCopyPeriod : 0; };
+  int my_copies = 0;
   if constexpr (kPvCopies) {
-    auto qk_share = [&](int w) { return ninst > w ? (ninst - w + 5) / 6 : 0; };
-    my_copies = wave_u < 3 ? qk_share(wave_u) : ninst - qk_share(0) - qk_share(1) - qk_share(2);
+    if (wave_u < RB) my_copies = count_residue(wave_u);
+    else
+      for (int t = 0; t < pv_residues(wave_u - RB); ++t) my_copies += count_residue(RB + wave_u - RB + kNpv * t);
   } else {
     my_copies = ninst > wave_u ? (ninst - wave_u + kWaves - 1) / kWaves : 0;
   }
+  // copy rounds of each role (straight-line code): at most 18 copies per tile
+  constexpr int kMaxCopies = 32 * kMaxK / 1024;
+  constexpr int kQkRounds = kPvCopies ? (kMaxCopies + kCopyPeriod - 1) / kCopyPeriod : kCopyRounds;
+  constexpr int kPvRounds = kPvCopies ? ((kMaxCopies + kCopyPeriod - 1) / kCopyPeriod) * ((kCopyPeriod - RB + kNpv - 1) / kNpv)
+                                      : kCopyRounds;
   const int copies = __builtin_amdgcn_readfirstlane(my_copies + (wave_u == kWaves - 1 ? 1 : 0));
   const uint32_t lds0 = lds_addr(lds);
   const int rstride = E.row_stride;
@@ -380,9 +397,9 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
     int ln = lane;
     asm volatile("" : "+v"(ln));
 #pragma unroll
-    for (int k = 0; k < (kPvCopies ? (QK_ROLE ? 3 : 9) : kCopyRounds); ++k) {   // straight-line: one exit branch
+    for (int k = 0; k < (QK_ROLE ? kQkRounds : kPvRounds); ++k) {   // straight-line: one exit branch
       const int i = !kPvCopies ? wave_u + kWaves * k
-                               : QK_ROLE ? wave_u + 6 * k : 3 + 6 * (k / 3) + k % 3;   // increasing in k
+                               : QK_ROLE ? wave_u + kCopyPeriod * k : pv_index(wave_u - RB, k);   // increasing in k
       if (i >= ninst) break;
       const int p = i * 64 + ln;
       const int tb = (TB == 2 && p >= block_pieces) ? 1 : 0;
