@@ -352,34 +352,31 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   // LDS addresses are wave-uniform; each lane only adds its 32-bit offset.
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   // Copy i of a tile goes to wave i mod 4, except with two or three Q.K
-  // waves: their stages are the longest, so over a period of kCopyPeriod
-  // copies Q.K wave w takes only copy w and the waves without Q.K rows share
-  // the rest (wave RB + j takes residues RB + j, RB + j + (4 - RB), ...).
-  // (a period of 6 measured best for two and three Q.K waves: 5, 7, 8 and 9
-  // were as fast or slower; at 9 the P.V wave becomes the last to arrive)
-  constexpr int kCopyPeriod = RB >= 2 ? 6 : kWaves;
-  constexpr bool kPvCopies = kCopyPeriod != kWaves;
+  // waves, whose stages are the longest: the waves without Q.K rows take the
+  // first n_pv copies of each tile (wave RB + j takes i = j, j + npv, ...) and
+  // Q.K wave w the copies n_pv + w, n_pv + w + RB, ...  n_pv follows the
+  // measured balance of the stage: every copy for b <= 4 (the narrow codes'
+  // short Q.K stages leave the other waves idle), else a share that leaves
+  // each Q.K wave one copy in six (half of them with three Q.K waves, two
+  // thirds with two).
+  constexpr bool kPvCopies = RB >= 2;
   constexpr int kNpv = kWaves - RB;
-  // residues of P.V wave j, and its copy index in round k
-  auto pv_residues = [&](int j) { return (kCopyPeriod - RB - j + kNpv - 1) / kNpv; };
-  auto pv_index = [&](int j, int k) {
-    const int R = pv_residues(j);
-    return kCopyPeriod * (k / R) + RB + j + kNpv * (k % R);
-  };
-  auto count_residue = [&](int r) { return ninst > r ? (ninst - r + kCopyPeriod - 1) / kCopyPeriod : 0; };
-  int my_copies = 0;
+  const int n_pv = !kPvCopies ? 0 : BITS <= 4 ? ninst : RB == 3 ? ninst / 2 : (2 * ninst) / 3;
+  int my_copies;
   if constexpr (kPvCopies) {
-    if (wave_u < RB) my_copies = count_residue(wave_u);
-    else
-      for (int t = 0; t < pv_residues(wave_u - RB); ++t) my_copies += count_residue(RB + wave_u - RB + kNpv * t);
+    const int n_qk = ninst - n_pv;
+    my_copies = wave_u < RB ? (n_qk > wave_u ? (n_qk - wave_u + RB - 1) / RB : 0)
+                            : (n_pv > wave_u - RB ? (n_pv - (wave_u - RB) + kNpv - 1) / kNpv : 0);
   } else {
     my_copies = ninst > wave_u ? (ninst - wave_u + kWaves - 1) / kWaves : 0;
   }
-  // copy rounds of each role (straight-line code): at most 18 copies per tile
+  // copy rounds of each role (straight-line code): at most 18 copies per tile,
+  // at most 9 of them for b <= 4
   constexpr int kMaxCopies = 32 * kMaxK / 1024;
-  constexpr int kQkRounds = kPvCopies ? (kMaxCopies + kCopyPeriod - 1) / kCopyPeriod : kCopyRounds;
-  constexpr int kPvRounds = kPvCopies ? ((kMaxCopies + kCopyPeriod - 1) / kCopyPeriod) * ((kCopyPeriod - RB + kNpv - 1) / kNpv)
+  constexpr int kQkRounds = kPvCopies ? (kMaxCopies - (RB == 3 ? kMaxCopies / 2 : 2 * kMaxCopies / 3) + RB - 1) / RB
                                       : kCopyRounds;
+  constexpr int kPvRounds = kPvCopies ? ((RB == 3 ? kMaxCopies / 2 : 2 * kMaxCopies / 3) + kNpv - 1) / kNpv : kCopyRounds;
+  static_assert(kMaxCopies == 18 && 32 * 4 * kMaxK / 8 / 1024 <= 9, "copy rounds sized for K = 576");
   const int copies = __builtin_amdgcn_readfirstlane(my_copies + (wave_u == kWaves - 1 ? 1 : 0));
   const uint32_t lds0 = lds_addr(lds);
   const int rstride = E.row_stride;
@@ -399,8 +396,8 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
 #pragma unroll
     for (int k = 0; k < (QK_ROLE ? kQkRounds : kPvRounds); ++k) {   // straight-line: one exit branch
       const int i = !kPvCopies ? wave_u + kWaves * k
-                               : QK_ROLE ? wave_u + kCopyPeriod * k : pv_index(wave_u - RB, k);   // increasing in k
-      if (i >= ninst) break;
+                               : QK_ROLE ? n_pv + wave_u + RB * k : (wave_u - RB) + kNpv * k;   // increasing in k
+      if (!kPvCopies || QK_ROLE ? i >= ninst : i >= n_pv) break;
       const int p = i * 64 + ln;
       const int tb = (TB == 2 && p >= block_pieces) ? 1 : 0;
       const int rem = p - tb * block_pieces;
