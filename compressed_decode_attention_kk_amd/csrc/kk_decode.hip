@@ -355,13 +355,13 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   // waves, whose stages are the longest: the waves without Q.K rows take the
   // first n_pv copies of each tile (wave RB + j takes i = j, j + npv, ...) and
   // Q.K wave w the copies n_pv + w, n_pv + w + RB, ...  n_pv follows the
-  // measured balance of the stage: every copy for b <= 4 (the narrow codes'
-  // short Q.K stages leave the other waves idle), else a share that leaves
-  // each Q.K wave one copy in six (half of them with three Q.K waves, two
-  // thirds with two).
+  // measured balance of the stage: with two Q.K waves, and for b <= 4 (the
+  // narrow codes' short Q.K stages), every copy (the other waves still idle
+  // otherwise); else half, which leaves each of the three Q.K waves one copy
+  // in six.
   constexpr bool kPvCopies = RB >= 2;
   constexpr int kNpv = kWaves - RB;
-  const int n_pv = !kPvCopies ? 0 : BITS <= 4 ? ninst : RB == 3 ? ninst / 2 : (2 * ninst) / 3;
+  const int n_pv = !kPvCopies ? 0 : (BITS <= 4 || RB == 2) ? ninst : ninst / 2;
   int my_copies;
   if constexpr (kPvCopies) {
     const int n_qk = ninst - n_pv;
@@ -373,9 +373,8 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
   // copy rounds of each role (straight-line code): at most 18 copies per tile,
   // at most 9 of them for b <= 4
   constexpr int kMaxCopies = 32 * kMaxK / 1024;
-  constexpr int kQkRounds = kPvCopies ? (kMaxCopies - (RB == 3 ? kMaxCopies / 2 : 2 * kMaxCopies / 3) + RB - 1) / RB
-                                      : kCopyRounds;
-  constexpr int kPvRounds = kPvCopies ? ((RB == 3 ? kMaxCopies / 2 : 2 * kMaxCopies / 3) + kNpv - 1) / kNpv : kCopyRounds;
+  constexpr int kQkRounds = kPvCopies ? (RB == 3 ? (kMaxCopies - kMaxCopies / 2 + RB - 1) / RB : 0) : kCopyRounds;
+  constexpr int kPvRounds = kPvCopies ? ((RB == 3 ? kMaxCopies / 2 : kMaxCopies) + kNpv - 1) / kNpv : kCopyRounds;
   static_assert(kMaxCopies == 18 && 32 * 4 * kMaxK / 8 / 1024 <= 9, "copy rounds sized for K = 576");
   const int copies = __builtin_amdgcn_readfirstlane(my_copies + (wave_u == kWaves - 1 ? 1 : 0));
   const uint32_t lds0 = lds_addr(lds);
