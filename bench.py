@@ -176,7 +176,9 @@ def trace_summary(trace_csv, steps, warmup, kernels=STEP_KERNELS):
     for k, rs in sorted(by.items(), key=lambda kv: -sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
                                                        for r in kv[1])):
         rs.sort(key=lambda r: int(r["Start_Timestamp"]))
-        per_step = max(1, round(len(rs) / (steps + warmup)))
+        per_step = round(len(rs) / (steps + warmup))
+        if per_step == 0:           # launched outside the steps (a set-up call)
+            continue
         timed = rs[-steps * per_step:]
         timed_all += timed
         us = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in timed]

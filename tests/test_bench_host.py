@@ -105,9 +105,11 @@ def test_trace_summary_times_the_timed_dispatches_only(tmp_path):
     for step, d in enumerate([9000, 8000, 1000, 1200, 1400]):     # warmup 2, timed 3 (us * 1000)
         rows.append((dec, t, t + d)); t += d
         rows.append((mrg, t, t + 100)); t += 100 + 50000
+    rows.append((dec.replace("decode_kernel", "gemm_kernel"), t, t + 99000))   # one set-up launch, not a step kernel
     f = tmp_path / "trace.csv"
     _write_trace(f, rows)
     md = bench.trace_summary(str(f), steps=3, warmup=2)
+    assert "gemm_kernel" not in md
     line = [l for l in md.splitlines() if l.startswith("| decode_kernel<3, 0>")][0].split("|")
     assert line[8].strip() == "3" and float(line[9]) == pytest.approx(1.2)       # timed calls, avg us
     assert float(line[10]) == pytest.approx(1.0) and float(line[12]) == pytest.approx(1.4)
