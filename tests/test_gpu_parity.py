@@ -500,6 +500,32 @@ def test_widths_off_the_64_grid(kk, d_rope, table, split_tokens):
     print(f"widths off the 64 grid (d_R {d_rope}, split {split_tokens}): worst err ratio {worst:.2e}")
 
 
+# Every bit width in one table.  NARROW keeps d <= 256, so 16- and 28-head
+# tables run the lean register budget; WIDE has d = 512 anchors, which need
+# the full one.
+ROWS_NARROW = [[0, 256, 16], [1, 128, 8], [1, 0, 0], [3, 192, 4], [4, 64, 2]]
+ROWS_WIDE = [[0, 512, 2], [1, 512, 16], [2, 256, 8], [3, 128, 4], [3, 0, 0]]
+
+
+@pytest.mark.parametrize("split_tokens", [0, 64])
+@pytest.mark.parametrize("r,table", [(256, ROWS_NARROW), (512, ROWS_WIDE)], ids=["narrow", "wide"])
+@pytest.mark.parametrize("heads", [16, 28, 40])
+def test_row_blocks_by_bit_width(kk, heads, r, table, split_tokens):
+    """One, two and three 16-row Q.K blocks per item (16, 28 and 40 heads),
+    each with every bit width: the tile copies are shared out between the
+    Q.K and P.V waves differently for each block count and for narrow
+    (b <= 4) and wide codes.  Ragged lengths, one a single token."""
+    w = synth.small_workload(25, len(table), heads, 3, 300, r, 64, table)
+    lens = [300, 97, 1]
+    model, caches, dec, ql, qr = run_gpu(kk, w, seq_lens=lens, t_cap=320, split_tokens=split_tokens)
+    worst = 0.0
+    for s in range(w.batch):
+        src = {a: source_cpu(w, a, s) for a in w.anchors()}
+        for l in range(w.n_layers):
+            worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, lens[s], src))
+    print(f"row blocks ({heads} heads, r {r}, split {split_tokens}): worst err ratio {worst:.2e}")
+
+
 @pytest.mark.parametrize("wid", [1, 2, 3, 4])
 def test_full_size_workloads_every_anchor_and_layer(kk, wid):
     """The four full-size workloads in the configuration bench.py times
