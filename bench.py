@@ -362,6 +362,9 @@ def main():
     ap.add_argument("--gqa", action="store_true",
                     help="time kk_gqa_decode_attn: the grouped-query 14B model (40 query / 8 KV heads of 128) with "
                          "the frozen 4x precision + depth table, 16 sequences x 16384 tokens")
+    ap.add_argument("--depth", choices=["shared", "own_cache", "anchors_only"], default="shared",
+                    help="decode step only: the table as is, with every inheriting layer given a cache of its own "
+                         "(same width and bits as its anchor), or with the inheriting layers left out")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="after timing, run 3 device-to-device copies of this size (counter calibration)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -403,6 +406,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     t_setup = time.perf_counter()
+    if args.depth != "shared" and (args.gqa or args.hetero or args.append or args.epilogue):
+        print("--depth applies to the decode step of one table", file=sys.stderr)
+        sys.exit(2)
     if args.gqa and (args.hetero or args.append or args.epilogue):
         print("--gqa times the grouped-query decode step alone", file=sys.stderr)
         sys.exit(2)
@@ -437,7 +443,7 @@ def main():
         dec = kk.MultiDecoder(runs, w.seq_len, w.seq_len, split_tokens=args.split_tokens)
         step = lambda: dec(ql, qr, seq_lens)
     else:
-        w = synth.workload(args.workload)
+        w = synth.depth_variant(synth.workload(args.workload), args.depth)
         runs_w = [w]
         model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
         caches = build_caches(kk, model, w)

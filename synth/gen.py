@@ -19,7 +19,7 @@ from __future__ import annotations
 import json
 import math
 import os
-from dataclasses import dataclass, field
+from dataclasses import dataclass, field, replace
 
 import numpy as np
 import torch
@@ -247,6 +247,25 @@ def hetero_workloads(batch_per_table: int = 8, seq_len: int = 8192, tables=None,
     tables = hetero_tables_14b() if tables is None else tables
     return [Workload(HETERO_WID + k, f"14b_hetero_run{k}", len(t), n_heads, batch_per_table, seq_len, r, d_rope,
                      torch.bfloat16, layers_from_table(t, d_rope)) for k, t in enumerate(tables)]
+
+
+def depth_variant(w: Workload, mode: str) -> Workload:
+    """The workload with its depth sharing changed, for measuring what sharing
+    costs and saves.  "own_cache": every inheriting layer becomes an anchor with
+    its former anchor's width and bit width (the same query rows and work; each
+    layer's bytes are read from a cache of its own).  "anchors_only": the
+    inheriting layers are left out.  "shared" returns w."""
+    if mode == "shared":
+        return w
+    if mode == "own_cache":
+        layers = [LayerSpec(l, w.layers[s.anchor].d, w.layers[s.anchor].bits, s.sm_scale)
+                  for l, s in enumerate(w.layers)]
+    elif mode == "anchors_only":
+        layers = [LayerSpec(i, w.layers[a].d, w.layers[a].bits, w.layers[a].sm_scale)
+                  for i, a in enumerate(w.anchors())]
+    else:
+        raise ValueError(f"depth mode {mode!r}: shared, own_cache or anchors_only")
+    return replace(w, name=f"{w.name}_{mode}", n_layers=len(layers), layers=layers)
 
 
 def small_workload(wid: int, n_layers: int, n_heads: int, batch: int, seq_len: int, r: int, d_rope: int,

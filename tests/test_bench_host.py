@@ -145,3 +145,28 @@ def test_pmc_summary_derives_the_rates(tmp_path):
     assert float(vals["VALU active: 4 x SQ_ACTIVE_INST_VALU / (SIMDs x cycles)"]) == pytest.approx(0.5)
     assert float(vals["mean resident waves per CU: 4 x SQ_WAVE_CYCLES / (CUs x cycles)"]) == pytest.approx(7.0)
     assert float(vals["L2 hit rate: TCC_HIT / (TCC_HIT + TCC_MISS)"]) == pytest.approx(0.3)
+
+
+def test_depth_variants_of_the_14b_table(kk):
+    """--depth: own_cache keeps every layer's rows and widths but gives each
+    inheriting layer its own cache (the cache bytes grow by the inheritors'
+    rows); anchors_only keeps the 33 anchors and their cache bytes."""
+    w = synth.workload(3)
+    own = synth.depth_variant(w, "own_cache")
+    only = synth.depth_variant(w, "anchors_only")
+    assert synth.depth_variant(w, "shared") is w
+    assert own.n_layers == w.n_layers == 48 and len(own.anchors()) == 48 and len(w.anchors()) == 33
+    assert [own.d_eff(l) for l in range(48)] == [w.d_eff(l) for l in range(48)]
+    assert [own.bits_eff(l) for l in range(48)] == [w.bits_eff(l) for l in range(48)]
+    assert [s.sm_scale for s in own.layers] == [s.sm_scale for s in w.layers]
+    assert only.n_layers == 33 and only.anchors() == list(range(33))
+    assert [(s.d, s.bits) for s in only.layers] == [(w.layers[a].d, w.layers[a].bits) for a in w.anchors()]
+    U, cache = bench.algorithmic_bytes(kk, w)
+    U_own, cache_own = bench.algorithmic_bytes(kk, own)
+    U_only, cache_only = bench.algorithmic_bytes(kk, only)
+    inh = [l for l in range(48) if w.layers[l].anchor != l]
+    extra = sum(w.batch * w.seq_len * (kk.row_stride_bytes(w.d_eff(l), w.d_rope, w.bits_eff(l)) + 4) for l in inh)
+    assert cache_own == cache + extra and U_own - U == extra
+    assert cache_only == cache and U_only < U
+    with pytest.raises(ValueError):
+        synth.depth_variant(w, "other")
