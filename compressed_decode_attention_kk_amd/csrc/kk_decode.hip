@@ -1122,13 +1122,17 @@ __global__ void __launch_bounds__(kThreads, decode_wg_per_cu(V)) decode_kernel(D
 }
 
 // Merge the split partials of one (entry, sequence, chunk) in a fixed order.
+// A merge may be cut into A.merge_parts workgroups, each owning a contiguous
+// range of the 8-feature vectors of every row (and computing the rows' split
+// weights itself); every output sums its splits in the same order either way.
 __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs) {
   __shared__ float wgt[kMaxMergeSplits][64];
   KArgs& A = kernel_args();
   const int blk = blockIdx.x;
   KEntry* ents = entry_array(A);
   KEntry& E = ents[find_entry<true>(A, ents, blk)];
-  const int local = blk - E.merge_base;
+  const int parts = A.merge_parts;
+  const int local = (blk - E.merge_base) / parts, part = (blk - E.merge_base) - local * parts;
   if (E.splits <= 1 || local >= E.n_seq * E.nrc) return;
   const int s = local / E.nrc, chunk = local - s * E.nrc;
   const int d = E.d, S = E.splits;
@@ -1159,9 +1163,19 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs) {
         }
       }
     }
-    for (int k = 0; k < S; ++k) {
-      const float* p = base + k * kstride + partial_ml_offset(d);
-      wgt[k][rl] = (L > 0.0f && p[64 + rl] > 0.0f) ? p[64 + rl] * exp2f(p[rl] - M) / L * p[128] : 0.0f;
+    // weights: again 8 splits' loads issued before any is used
+    for (int k0 = 0; k0 < S; k0 += 8) {
+      float mk[8], lk[8], uk[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float* p = base + min(k0 + j, S - 1) * kstride + partial_ml_offset(d);
+        mk[j] = p[rl];
+        lk[j] = p[64 + rl];
+        uk[j] = p[128];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < S) wgt[k0 + j][rl] = (L > 0.0f && lk[j] > 0.0f) ? lk[j] * exp2f(mk[j] - M) / L * uk[j] : 0.0f;
     }
   }
   __syncthreads();
@@ -1169,17 +1183,18 @@ __global__ void __launch_bounds__(256) merge_kernel(DecodeArgs) {
   // issues the loads of kSplitBatch splits before using any of them; every
   // output still sums its splits in order k = 0 .. S-1.
   const int d8 = d >> 3;
+  const int v0 = (part * d8) / parts, nv = ((part + 1) * d8) / parts - v0;   // this part's vectors of a row
   constexpr int kMergeVec = 2;
   constexpr int kSplitBatch = 4;
-  const int total = nrows * d8;
+  const int total = nrows * nv;
   for (int i0 = threadIdx.x; i0 < total; i0 += kMergeVec * 256) {
     int rl[kMergeVec], f[kMergeVec];
     f4 acc[kMergeVec][2];
 #pragma unroll
     for (int j = 0; j < kMergeVec; ++j) {
       const int idx = min(i0 + 256 * j, total - 1);
-      rl[j] = idx / d8;
-      f[j] = (idx - rl[j] * d8) * 8;
+      rl[j] = idx / nv;
+      f[j] = (v0 + idx - rl[j] * nv) * 8;
       acc[j][0] = acc[j][1] = f4{0.f, 0.f, 0.f, 0.f};
     }
     for (int k0 = 0; k0 < S; k0 += kSplitBatch) {

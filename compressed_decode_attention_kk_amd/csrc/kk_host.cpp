@@ -95,6 +95,7 @@ int bits_class(int bits) { return bits == 2 ? 0 : bits == 4 ? 1 : bits == 8 ? 2 
 // which stream 2-8x the bytes (measured on MI355X).
 int64_t tile_cost(int bits, int d) { return 10 + (bits == 16 ? (7 * d + 511) / 512 : 0); }
 constexpr int kItemWaves = 4;       // waves of items over the resident slots (mixed tables), at most
+constexpr int kMergeBlocksPerCU = 4; // merge workgroups per compute unit below which merges are cut up
 constexpr int kMinItemTiles = 96;   // ... fewer when items would average fewer tiles than this
 constexpr int kMinSplitTiles = 8;   // no split shorter than 8 tiles (256 tokens)
 constexpr int64_t kTailPercent = 15;  // share of the work (last dispatched) cut twice as fine
@@ -286,9 +287,19 @@ kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_to
     P.entry_anchor[i] = ents[i].anchor;
     P.entry_table[i] = ents[i].table;
   }
+  // A merge is a short chain of dependent loads.  When there are too few of
+  // them to give every compute unit kMergeBlocksPerCU workgroups, each is cut
+  // into feature ranges (the per-row weights are recomputed by every part).
+  int parts = 1;
+  if (merges > 0)
+    parts = (int)std::min<int64_t>(kk::kMaxMergeParts,
+                                   std::max<int64_t>(1, (kMergeBlocksPerCU * (int64_t)std::max(n_cus, 1) + merges - 1) / merges));
+  for (auto& e : P.ents) e.merge_base *= parts;
+  merges *= parts;
   if (items > 0x7fffffff || merges > 0x7fffffff) return KK_ERR_UNSUPPORTED;
   Lc.items = (int)items;
   Lc.merge_blocks = (int)merges;
+  Lc.merge_parts = parts;
   P.ws_floats = ws;
   return KK_OK;
 }
@@ -307,6 +318,7 @@ kk_status make_single_plan(const kk_model_cfg* c, const kk_cache* caches, int ba
   for (size_t i = 0; i < P.ents.size(); ++i) A.entries[i] = P.ents[i];
   A.n_entries = (int32_t)P.ents.size();
   A.total_items = P.launch.items;
+  A.merge_parts = P.launch.merge_parts;
   return KK_OK;
 }
 
@@ -599,6 +611,7 @@ kk_status kk_multi_decode_attn(const kk_table_batch* tables, int32_t n_tables, i
   A.plan.group_layers = reinterpret_cast<const uint16_t*>(ws + m.grp_off);
   A.n_entries = (int32_t)P.ents.size();
   A.total_items = P.launch.items;
+  A.merge_parts = P.launch.merge_parts;
   A.q_lat = q_lat;
   A.q_rope = q_rope;
   A.out = out;
@@ -807,6 +820,7 @@ kk_status kk_gqa_decode_attn(const kk_gqa_cfg* cfg, const kk_cache* caches, int3
   }
   A.n_entries = (int32_t)P.ents.size();
   A.total_items = P.launch.items;
+  A.merge_parts = P.launch.merge_parts;
   A.q_lat = q;                 // the value chunks are skipped: never read as queries
   A.q_rope = q;                // [L][B][n_kv * G][d_h] = [L][B * n_kv][G][d_h]
   A.out = out;                 // [L][B * n_kv][G][d_h] = [L][B][H][d_h]

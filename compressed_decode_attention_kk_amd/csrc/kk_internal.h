@@ -13,6 +13,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTile = 32;            // token granularity of splits (tiles are 32 or 16 tokens)
 constexpr int kMaxRowBlocks = 3;     // 16-row MFMA blocks per work item (<= 48 query rows)
 constexpr int kMaxMergeSplits = 64;  // token splits of one sequence
+constexpr int kMaxMergeParts = 4;    // merge workgroups of one (entry, sequence, row chunk)
 constexpr int kMaxK = 576;           // d + d_R (the ABI limit)
 constexpr int kMaxEntries = 88;      // group entries held in the launch arguments
 constexpr int kMaxLayers = 64;
@@ -83,6 +84,7 @@ struct DecodeArgs {
   int32_t n_entries, total_items;
   int32_t q_is_f32;
   int32_t seq_div;                    // sequence s reads seq_lens[s / seq_div] (grouped-query: n_kv)
+  int32_t merge_parts;                // merge workgroups per (entry, sequence, row chunk), feature ranges
   uint16_t group_layers[kMaxLayers];  // layers ordered by group
   LayerArg layers[kMaxLayers];
   EntryArg entries[kMaxEntries];
@@ -168,6 +170,7 @@ struct DecodeLaunch {
   int lds_bytes;         // dynamic LDS per workgroup: the largest entry's need
   int row_blocks;        // 16-row MFMA blocks per item (1..3), uniform for the step
   int merge_blocks;
+  int merge_parts = 1;   // merge workgroups per (entry, sequence, row chunk)
   int variant = kFull;   // kernel variant (kGqa: row_blocks <= 2)
 };
 

@@ -477,3 +477,19 @@ def test_status_strings(kk):
     seen = {kk.status_string(s) for s in range(5)}
     assert len(seen) == 5 and kk.status_string(0) == "ok"
     assert kk.status_string(99) == "unknown status"
+
+
+def test_merge_is_cut_into_parts_when_merges_are_few(kk):
+    """The merge launch runs one workgroup per (entry, sequence, row chunk),
+    or up to 4 per merge (feature ranges) when there are fewer merges than
+    4 workgroups per compute unit.  With 1024-token splits every one of the
+    48 one-layer chunks of the 40-head table is merged for every sequence."""
+    import synth
+    w = synth.workload(3)
+    m = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+    for batch, cus, blocks in ((32, 256, 1536), (8, 256, 384 * 3), (8, 64, 384), (2, 256, 96 * 4), (2, 16, 96)):
+        i = kk.plan_info(m, batch, w.seq_len, 1024, cus)
+        assert i.max_splits == 8
+        assert i.merge_blocks == blocks, (batch, cus, i.merge_blocks)
+    # no splits, no merge
+    assert kk.plan_info(m, 32, 1024, 1024, 256).merge_blocks == 0
