@@ -145,6 +145,12 @@ def test_pmc_summary_derives_the_rates(tmp_path):
     assert float(vals["VALU active: 4 x SQ_ACTIVE_INST_VALU / (SIMDs x cycles)"]) == pytest.approx(0.5)
     assert float(vals["mean resident waves per CU: 4 x SQ_WAVE_CYCLES / (CUs x cycles)"]) == pytest.approx(7.0)
     assert float(vals["L2 hit rate: TCC_HIT / (TCC_HIT + TCC_MISS)"]) == pytest.approx(0.3)
+    # the dispatch count is per pass, also when a counter is collected in several passes
+    assert "dispatches per pass: 2" in md
+    md2 = bench.pmc_summary([str(f), str(f)])
+    assert "dispatches per pass: 2" in md2
+    vals2 = {l.split("|")[1].strip(): l.split("|")[2].strip() for l in md2.splitlines() if l.count("|") == 3}
+    assert vals2 == vals
 
 
 def test_depth_variants_of_the_14b_table(kk):
