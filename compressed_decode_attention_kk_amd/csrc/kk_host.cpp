@@ -294,9 +294,9 @@ kk_status make_plan(const std::vector<TableRef>& tabs, int max_len, int split_to
   if (merges > 0)
     parts = (int)std::min<int64_t>(kk::kMaxMergeParts,
                                    std::max<int64_t>(1, (kMergeBlocksPerCU * (int64_t)std::max(n_cus, 1) + merges - 1) / merges));
-  for (auto& e : P.ents) e.merge_base *= parts;
+  if (items > 0x7fffffff || merges * parts > 0x7fffffff) return KK_ERR_UNSUPPORTED;
+  for (auto& e : P.ents) e.merge_base *= parts;   // no overflow: merge_base <= merges
   merges *= parts;
-  if (items > 0x7fffffff || merges > 0x7fffffff) return KK_ERR_UNSUPPORTED;
   Lc.items = (int)items;
   Lc.merge_blocks = (int)merges;
   Lc.merge_parts = parts;
