@@ -493,3 +493,84 @@ def test_merge_is_cut_into_parts_when_merges_are_few(kk):
         assert i.merge_blocks == blocks, (batch, cus, i.merge_blocks)
     # no splits, no merge
     assert kk.plan_info(m, 32, 1024, 1024, 256).merge_blocks == 0
+
+
+def _chunks_of_table(layers, heads):
+    """Row chunks per anchor group entry, as the planner documents them: RB =
+    min(3, ceil(min(H, 64) / 16)) blocks of 16 rows; chunks hold whole layers
+    when a layer fits (H <= 16 RB), else 16 RB rows; entries of at most 8
+    chunks.  Returns [(d, chunks)] per entry."""
+    rb = min(3, (min(heads, 64) + 15) // 16)
+    chunk_rows = heads * ((16 * rb) // heads) if heads <= 16 * rb else 16 * rb
+    out = []
+    for a, s in enumerate(layers):
+        if s.anchor != a:
+            continue
+        rows = sum(1 for t in layers if t.anchor == a) * heads
+        for r0 in range(0, rows, 8 * chunk_rows):
+            n = min(rows, r0 + 8 * chunk_rows) - r0
+            out.append((s.d, -(-n // chunk_rows)))
+    return out
+
+
+def test_plan_invariants_over_random_tables(kk):
+    """Property test of the planner over random valid tables, batches,
+    lengths, split sizes and compute-unit counts (run under ASan/UBSan by the
+    sanitizer test too).  With a fixed split size every count is predictable:
+    items = chunks x batch x splits, one merge (cut into up to 4 parts when
+    merges are fewer than 4 per compute unit) per (chunk, sequence), and the
+    workspace is one partial slot (32 d + 192 floats) per item.  Automatic
+    splits keep the same structure within bounds."""
+    hyp = pytest.importorskip("hypothesis")
+    st = pytest.importorskip("hypothesis.strategies")
+
+    @st.composite
+    def tables(draw):
+        L = draw(st.integers(1, 64))
+        H = draw(st.sampled_from([1, 3, 4, 8, 15, 16, 17, 24, 28, 32, 33, 40, 48, 49, 64, 100, 128]))
+        d_rope = draw(st.sampled_from([16, 32, 64, 128]))
+        r = 512
+        layers, anchors = [], []
+        for l in range(L):
+            if l > 0 and draw(st.booleans()) and draw(st.booleans()):
+                a = draw(st.sampled_from(anchors))
+                layers.append(ko.Layer(a, 0, 0, layers[a].sm_scale))
+            else:
+                d = draw(st.integers(1, min(512, 576 - d_rope) // 16)) * 16
+                b = draw(st.sampled_from([2, 4, 8, 16]))
+                layers.append(ko.Layer(l, d, b, 1.0 / math.sqrt(d + d_rope)))
+                anchors.append(l)
+        return layers, H, r, d_rope
+
+    @hyp.settings(max_examples=120, deadline=None, derandomize=True)
+    @hyp.given(tables(), st.integers(1, 64), st.integers(0, 70000), st.integers(0, 8), st.integers(1, 1024))
+    def check(tab, batch, max_len, split_mult, cus):
+        layers, H, r, d_rope = tab
+        m = kk.Model(layers, H, r, d_rope)
+        ents = _chunks_of_table(layers, H)
+        chunks = sum(c for _, c in ents)
+        split = 1024 * split_mult
+        try:
+            info = kk.plan_info(m, batch, max_len, split, cus)
+        except kk.KKError as e:
+            # only plans past the launch limits are refused
+            assert e.status == kk.KK_ERR_UNSUPPORTED and len(ents) > 88
+            return
+        assert len(ents) <= 88
+        assert info.n_cus == cus
+        assert 1 <= info.max_splits <= 64
+        assert chunks * batch <= info.work_items <= chunks * batch * info.max_splits
+        assert (info.max_splits == 1) == (info.merge_blocks == 0) == (info.workspace_bytes == 0)
+        if info.max_splits > 1:   # automatic splits may leave some entries unsplit (no merge)
+            assert 1 <= info.merge_blocks <= 4 * chunks * batch
+        if split > 0:
+            S = min(64, max(1, -(-max_len // split))) if max_len > 0 else 1
+            assert info.max_splits == S
+            assert info.work_items == chunks * batch * S
+            if S > 1:
+                parts = min(4, max(1, -(-4 * cus // (chunks * batch))))
+                assert info.merge_blocks == chunks * batch * parts
+                assert info.workspace_bytes == sum(c * batch * S * (32 * d + 192) * 4 for d, c in ents)
+            assert kk.workspace_bytes(m, batch, max_len, split) == info.workspace_bytes
+
+    check()
