@@ -526,6 +526,51 @@ def test_row_blocks_by_bit_width(kk, heads, r, table, split_tokens):
     print(f"row blocks ({heads} heads, r {r}, split {split_tokens}): worst err ratio {worst:.2e}")
 
 
+def _random_case(i):
+    """Seeded random table and step: head count (1 to 72, across the one-,
+    two- and three-block items and the 48-row chunks that cross layers),
+    1-6 layers with random inheritance, any d <= r (multiple of 16), every
+    code width, d_R in {16, 32, 64, 128}, 1-4 sequences of 0-300 tokens,
+    automatic or fixed splits, bf16 or fp32 queries."""
+    rng = np.random.default_rng(1000 + i)
+    H = int(rng.choice([1, 2, 5, 8, 13, 16, 20, 24, 31, 32, 36, 40, 47, 48, 56, 64, 72]))
+    L = int(rng.integers(1, 7))
+    d_rope = int(rng.choice([16, 32, 64, 128]))
+    r = int(rng.choice([256, 512]))
+    table, anchors = [], []
+    for l in range(L):
+        if l > 0 and rng.random() < 0.35:
+            table.append([int(rng.choice(anchors)), 0, 0])
+        else:
+            d = 16 * int(rng.integers(1, min(r, 576 - d_rope) // 16 + 1))
+            table.append([l, d, int(rng.choice([2, 4, 8, 16]))])
+            anchors.append(l)
+    B = int(rng.integers(1, 5))
+    lens = [int(x) for x in rng.integers(0, 301, B)]
+    if rng.random() < 0.3:
+        lens[int(rng.integers(0, B))] = int(rng.choice([0, 1, 31, 32, 33]))
+    split = int(rng.choice([0, 0, 32, 64, 128]))
+    q_dtype = torch.float32 if rng.random() < 0.25 else torch.bfloat16
+    return table, H, r, d_rope, B, lens, split, q_dtype
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_tables(kk, case):
+    """Randomized sweep: every (layer, sequence) of a seeded random table
+    against the oracle, codes and scales bit-exact."""
+    table, H, r, d_rope, B, lens, split, q_dtype = _random_case(case)
+    print(f"case {case}: H {H}, table {table}, r {r}, d_R {d_rope}, lens {lens}, split {split}, q {q_dtype}",
+          flush=True)
+    w = synth.small_workload(40 + case, len(table), H, B, 300, r, d_rope, table, q_dtype=q_dtype)
+    model, caches, dec, ql, qr = run_gpu(kk, w, seq_lens=lens, t_cap=320, split_tokens=split)
+    worst = 0.0
+    for s in range(w.batch):
+        src = {a: source_cpu(w, a, s) for a in w.anchors()}
+        for l in range(w.n_layers):
+            worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, s, lens[s], src))
+    print(f"case {case}: worst err ratio {worst:.2e}")
+
+
 @pytest.mark.parametrize("wid", [1, 2, 3, 4])
 def test_full_size_workloads_every_anchor_and_layer(kk, wid):
     """The four full-size workloads in the configuration bench.py times
