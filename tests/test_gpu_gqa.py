@@ -129,3 +129,47 @@ def test_full_size_14b_sampled(kk):
             n += 1
         del k, v
     print(f"gqa 14B: worst err ratio {worst:.2e} over {n} samples")
+
+
+def _random_gqa_case(i):
+    """Seeded random grouped-query table and step: d_h 64 or 128, 1-8 KV
+    heads with groups of 1-32 query heads, 1-6 layers with random inheritance
+    and code widths, 1-3 sequences of 0-300 tokens, automatic or fixed
+    splits, bf16 or fp32 queries."""
+    rng = np.random.default_rng(2000 + i)
+    d_head = int(rng.choice([64, 128]))
+    n_kv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 3, 5, 8, 16, 17, 32]))
+    L = int(rng.integers(1, 7))
+    table, anchors = [], []
+    for l in range(L):
+        if l > 0 and rng.random() < 0.35:
+            table.append([int(rng.choice(anchors)), 0, 0])
+        else:
+            table.append([l, 0, int(rng.choice([2, 4, 8, 16]))])
+            anchors.append(l)
+    B = int(rng.integers(1, 4))
+    lens = [int(x) for x in rng.integers(0, 301, B)]
+    split = int(rng.choice([0, 0, 32, 96]))
+    q_dtype = torch.float32 if rng.random() < 0.25 else torch.bfloat16
+    return table, d_head, G * n_kv, n_kv, B, lens, split, q_dtype
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_gqa_tables(kk, case):
+    """Randomized sweep of the grouped-query path: every (layer, sequence)
+    against the oracle's direct grouped-query attention."""
+    table, d_head, n_q, n_kv, B, lens, split, q_dtype = _random_gqa_case(case)
+    print(f"gqa case {case}: d_h {d_head}, H {n_q}, n_kv {n_kv}, table {table}, lens {lens}, split {split}, "
+          f"q {q_dtype}", flush=True)
+    w = synth.small_gqa_workload(300 + case, table, n_q, n_kv, d_head, B, 300, q_dtype=q_dtype)
+    model, caches, q, dec = run(kk, w, lens, 320, split)
+    worst = 0.0
+    for s in range(w.batch):
+        src = {}
+        for a in w.anchors():
+            k, v = synth.gqa_source(w, a, "cuda")
+            src[a] = (k[s].cpu().numpy(), v[s].cpu().numpy())
+        for l in range(w.n_layers):
+            worst = max(worst, check(w, caches, q, dec, l, s, lens[s], src))
+    print(f"gqa case {case}: worst err ratio {worst:.2e}")

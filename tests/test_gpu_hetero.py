@@ -158,3 +158,47 @@ def test_hetero_full_size_sampled(kk):
                 worst = max(worst, check(w, dec.layer_out(k, l)[s], runs[k][1], qs[k], l, s, w.seq_len, src))
                 n += 1
     print(f"heterogeneous 14B batch: worst err ratio {worst:.2e} over {n} samples")
+
+
+def _random_hetero_case(i):
+    """Seeded random heterogeneous batch: one model shape (1-6 layers, 1-64
+    heads, d_R 16-128), 2-4 runs each with its own random table (inheritance,
+    widths, code widths), 1-3 sequences per run of 0-300 tokens, automatic or
+    fixed splits."""
+    rng = np.random.default_rng(3000 + i)
+    L = int(rng.integers(1, 7))
+    H = int(rng.choice([1, 4, 13, 16, 24, 32, 40, 48, 64]))
+    d_rope = int(rng.choice([16, 32, 64, 128]))
+    r = 256
+    tables = []
+    for _ in range(int(rng.integers(2, 5))):
+        t, anchors = [], []
+        for l in range(L):
+            if l > 0 and rng.random() < 0.35:
+                t.append([int(rng.choice(anchors)), 0, 0])
+            else:
+                t.append([l, 16 * int(rng.integers(1, min(r, 576 - d_rope) // 16 + 1)), int(rng.choice([2, 4, 8, 16]))])
+                anchors.append(l)
+        tables.append(t)
+    batches = [int(rng.integers(1, 4)) for _ in tables]
+    lens = [[int(x) for x in rng.integers(0, 301, b)] for b in batches]
+    split = int(rng.choice([0, 0, 32, 128]))
+    return L, H, r, d_rope, tables, batches, lens, split
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_random_hetero_batches(kk, case):
+    """Randomized sweep of kk_multi_decode_attn: every (run, layer, sequence)
+    against the oracle with that run's table."""
+    L, H, r, d_rope, tables, batches, lens, split = _random_hetero_case(case)
+    print(f"hetero case {case}: L {L}, H {H}, d_R {d_rope}, tables {tables}, lens {lens}, split {split}", flush=True)
+    ws = [synth.small_workload(400 + 10 * case + k, L, H, b, 300, r, d_rope, t)
+          for k, (t, b) in enumerate(zip(tables, batches))]
+    runs, dec, qs = run_multi(kk, ws, lens, 320, split)
+    worst = 0.0
+    for k, w in enumerate(ws):
+        for s in range(w.batch):
+            src = {a: source_cpu(w, a, s) for a in w.anchors()}
+            for l in range(w.n_layers):
+                worst = max(worst, check(w, dec.layer_out(k, l)[s], runs[k][1], qs[k], l, s, lens[k][s], src))
+    print(f"hetero case {case}: worst err ratio {worst:.2e}")
