@@ -176,7 +176,9 @@ kk_status kk_decode_workspace_bytes(const kk_model_cfg* cfg, int32_t batch, int3
  * The KV Cache Bottleneck"); the split count depends on the compute units.
  * n_cus > 0 plans for that many compute units, n_cus == 0 for the current
  * device's.  Outputs: the compute units used, the decode work items (one
- * workgroup each), the merge workgroups, the largest split count of any
+ * workgroup each), the merge workgroups (one per split (row chunk, sequence),
+ * or up to 4 feature ranges of one when merges are fewer than 4 per compute
+ * unit), the largest split count of any
  * (row chunk, sequence), and the workspace bytes (as kk_decode_workspace_bytes
  * on a device with n_cus compute units). */
 typedef struct {
