@@ -62,7 +62,6 @@ defined in fp32); dequantization and attention run in float64.
 
 from __future__ import annotations
 
-import math
 from dataclasses import dataclass
 
 import numpy as np

@@ -4,7 +4,6 @@ Bar: codes and scales bit-exact; decode output per layer (and here per
 sampled (layer, sequence)) within max-abs 2e-3 * max|o_oracle|.
 """
 
-import math
 
 import numpy as np
 import pytest
@@ -26,10 +25,6 @@ def kk():
     import compressed_decode_attention_kk_amd as kk
     kk.lib()
     return kk
-
-
-def oracle_layers(w):
-    return [ko.Layer(s.anchor, s.d, s.bits, s.sm_scale) for s in w.layers]
 
 
 def source_cpu(w, a, s):
