@@ -77,7 +77,7 @@ def useful_flops(w):
 
 
 # sources the decode step is built from (its kernels, launch descriptors and planner)
-DECODE_SOURCES = ("kk_decode.hip", "kk_internal.h", "kk_host.cpp")
+DECODE_SOURCES = ("kk_decode_kernel.h", "kk_decode.hip", "kk_internal.h", "kk_host.cpp")
 
 
 def kernel_source_digest():

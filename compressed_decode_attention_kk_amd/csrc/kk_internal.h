@@ -212,6 +212,9 @@ inline int decode_lds_bytes(int row_stride, int d, int d_rope, int bits, int row
          pbuf_bytes(row_blocks, tile_blocks_of(bits)) + kMiscBytes;
 }
 hipError_t launch_decode(const DecodeArgs& a, const DecodeLaunch& L, hipStream_t stream);
+// One decode kernel variant (RB row blocks, register budget V).
+template <int RB, int V>
+hipError_t launch_decode_items(const DecodeArgs& a, int n, int lds, hipStream_t stream);
 
 // Copies `words` 32-bit words from host memory to device memory `dst` by
 // kernel launches whose arguments carry the data (stream-ordered, no host
