@@ -350,6 +350,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--uniform", metavar="D,B", default=None,
+                    help="time 8 anchor layers of kept width D and bit width B in the 14B shape "
+                         "(40 heads, B=32, T=8192) instead of a numbered workload")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--append", action="store_true",
@@ -391,6 +394,9 @@ def main():
             json.dump(rec, f, indent=1)
         print(json.dumps(rec))
         return
+    if args.uniform and (args.gqa or args.hetero or args.append or args.epilogue or args.depth != "shared"):
+        print("--uniform times the decode step of one uniform table", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (the decode path has no multi-GPU mode); got --gpus {args.gpus}",
               file=sys.stderr)
@@ -443,7 +449,11 @@ def main():
         dec = kk.MultiDecoder(runs, w.seq_len, w.seq_len, split_tokens=args.split_tokens)
         step = lambda: dec(ql, qr, seq_lens)
     else:
-        w = synth.depth_variant(synth.workload(args.workload), args.depth)
+        if args.uniform:
+            ud, ub = (int(x) for x in args.uniform.split(","))
+            w = synth.uniform_workload(ud, ub)
+        else:
+            w = synth.depth_variant(synth.workload(args.workload), args.depth)
         runs_w = [w]
         model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
         caches = build_caches(kk, model, w)

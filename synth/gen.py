@@ -268,6 +268,14 @@ def depth_variant(w: Workload, mode: str) -> Workload:
     return replace(w, name=f"{w.name}_{mode}", n_layers=len(layers), layers=layers)
 
 
+def uniform_workload(d: int, bits: int, n_layers: int = 8) -> Workload:
+    """n_layers anchors of one (d, b) in the 14B shape (40 heads, B = 32,
+    T = 8192, r = 512, d_R = 64), drawn from the 14B workload's generators:
+    the cost of one layer at each kept width and bit width."""
+    return Workload(3, f"uniform_{n_layers}x_d{d}_b{bits}", n_layers, 40, 32, 8192, 512, 64, torch.bfloat16,
+                    _uniform_layers(n_layers, d, bits, 64))
+
+
 def small_workload(wid: int, n_layers: int, n_heads: int, batch: int, seq_len: int, r: int, d_rope: int,
                    table, q_dtype=torch.bfloat16, name="small") -> Workload:
     return Workload(wid, name, n_layers, n_heads, batch, seq_len, r, d_rope, q_dtype,

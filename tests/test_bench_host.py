@@ -39,6 +39,22 @@ def test_algorithmic_bytes_of_the_uniform_workloads(kk):
     assert bench.algorithmic_bytes(kk, synth.workload(2))[0] == 2_419_916_800
 
 
+def test_uniform_table_mode(kk):
+    """--uniform D,B: eight anchors of one (d, b) in the 14B shape; U written
+    out by hand for d = 512, b = 4 (rows of 288 B), and the mode refuses the
+    other steps before touching a GPU."""
+    w = synth.uniform_workload(512, 4)
+    assert (w.n_layers, w.n_heads, w.batch, w.seq_len, w.r, w.d_rope) == (8, 40, 32, 8192, 512, 64)
+    assert w.anchors() == list(range(8)) and all(l.d == 512 and l.bits == 4 for l in w.layers)
+    L, H, B, T = 8, 40, 32, 8192
+    U, cache = bench.algorithmic_bytes(kk, w)
+    assert cache == L * B * T * (288 + 4)
+    assert U == cache + L * B * H * 576 * 2 + L * B * H * 512 * 4 == 645_136_384
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--uniform", "512,4", "--gqa"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "--uniform" in r.stderr
+
+
 def _write_counters(path, counter, rows):
     with open(path, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"])
