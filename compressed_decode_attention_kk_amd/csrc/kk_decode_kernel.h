@@ -20,8 +20,9 @@
 //      that moves each field to the top of its byte (b = 4, 2), or (b = 16)
 //      as the row's two byte planes: signed high bytes and offset-binary low
 //      bytes, with an exact integer bias correction.
-//      The query is a per-row fixed-point number (power-of-two prescale,
-//      14 bits) held as two int8 limbs, so scores accumulate exactly in int32;
+//      Each part of a query row is a fixed-point number relative to its own
+//      largest magnitude (15 bits latent, 22 bits RoPE) held as int8 limbs, so
+//      scores accumulate exactly in int32;
 //   3. online softmax in the same wave (no exchange): per-token scale and
 //      sm_scale applied in fp32, running max in the log2 domain moved lazily,
 //      P' = exp2(z - m - E) * scale_t written to LDS as fp16, with E a
@@ -57,6 +58,7 @@ typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 typedef int i2 __attribute__((ext_vector_type(2)));
 typedef short s4 __attribute__((ext_vector_type(4)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 #define LDS_PTR(T, p) ((__attribute__((address_space(3))) T*)(p))
 
@@ -534,14 +536,34 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
             for (int v = 0; v < 2; ++v) raw[c][v] = p[v];
           }
         }
+        if constexpr (!F32) {
+          // bf16: |x| orders as its bit pattern without the sign, so the maxima
+          // are taken two elements at a time on the packed words
+          us2 m2L = us2{0, 0}, m2R = us2{0, 0};
 #pragma unroll
-        for (int c = 0; c < kMaxC; ++c) {
-          float x[16];
-          get(c, x);
+          for (int c = 0; c < kMaxC; ++c) {
+            const uint32_t msk = ok[c] ? 0x7FFF7FFFu : 0u;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            if (is_lat(c)) mxL = fmaxf(mxL, fabsf(x[i]));
-            else mxR = fmaxf(mxR, fabsf(x[i]));
+            for (int v = 0; v < 2; ++v)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const us2 t = __builtin_bit_cast(us2, raw[c][v][i] & msk);
+                if (is_lat(c)) m2L = __builtin_elementwise_max(m2L, t);
+                else m2R = __builtin_elementwise_max(m2R, t);
+              }
+          }
+          mxL = __uint_as_float((uint32_t)(m2L[0] > m2L[1] ? m2L[0] : m2L[1]) << 16);
+          mxR = __uint_as_float((uint32_t)(m2R[0] > m2R[1] ? m2R[0] : m2R[1]) << 16);
+        } else {
+#pragma unroll
+          for (int c = 0; c < kMaxC; ++c) {
+            float x[16];
+            get(c, x);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              if (is_lat(c)) mxL = fmaxf(mxL, fabsf(x[i]));
+              else mxR = fmaxf(mxR, fabsf(x[i]));
+            }
           }
         }
         mxL = max_xor_16_32(mxL);
@@ -557,9 +579,27 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
           get(c, x);
           uint32_t hw[4] = {0, 0, 0, 0}, mw[4] = {0, 0, 0, 0}, lw[4] = {0, 0, 0, 0};
           const float pre = is_lat(c) ? preL : preR;
+          if (BITS != 16 && is_lat(c)) {
+            // Latent part, codes of b <= 8: base-256 limbs, qi = 256 hi + lo with
+            // lo in [-128, 127] and hi = floor((qi + 128) / 256) in [-63, 64].
+            // One fma rounds x * pre to the nearest integer (ties to even) in
+            // the low bits of a float near 1.5 * 2^23: its bits are
+            // 0x4B400000 + qi + 128, so byte 0 is lo + 128 and byte 1 is hi
+            // (two's complement), and v_perm gathers them four at a time.
+            uint32_t zb[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) zb[i] = __float_as_uint(fmaf(x[qk_slot_feature<BITS>(i)], pre, 12583040.0f));
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+              const uint32_t a = perm(zb[4 * w + 1], zb[4 * w], 0x05010400u);       // lo0 lo1 hi0 hi1
+              const uint32_t b = perm(zb[4 * w + 3], zb[4 * w + 2], 0x05010400u);   // lo2 lo3 hi2 hi3
+              lw[w] = perm(b, a, 0x05040100u) ^ 0x80808080u;
+              hw[w] = perm(b, a, 0x07060302u);
+            }
+          } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            // latent: qi = 128 hi + lo, |qi| <= 16256; RoPE: qi = 16384 hi + 128 mid + lo,
+            // latent (b = 16): qi = 128 hi + lo, |qi| <= 16256; RoPE: qi = 16384 hi + 128 mid + lo,
             // |qi| <= 16256 * 128 (floor divisions: hi in [-127, 127], mid in [-64, 64],
             // lo in [-64, 63])
             const int qi = (int)rintf(x[qk_slot_feature<BITS>(i)] * pre);
@@ -571,6 +611,7 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
             hw[i >> 2] |= ((uint32_t)hi & 0xFFu) << (8 * (i & 3));
             mw[i >> 2] |= ((uint32_t)mid & 0xFFu) << (8 * (i & 3));
             lw[i >> 2] |= ((uint32_t)lo & 0xFFu) << (8 * (i & 3));
+          }
           }
           qh[c] = i4{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3]};
           ql[c] = i4{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
@@ -836,8 +877,8 @@ __device__ __forceinline__ void run_item(KArgs& A, KEntry& E, int s, int ksplit,
                   float v;
                   if constexpr (BITS == 16)   // 2^8 (2^7 hi + lo) + 2^7 (lh + sum q)
                     v = fmaf(256.0f, (float)(128 * acc[tb][0][j] + acc[tb][1][j]), 128.0f * (float)(acc[tb][2][j] + qbiasL));
-                  else
-                    v = (float)(128 * acc[tb][0][j] + acc[tb][1][j]);
+                  else                        // base-256 limbs: |256 hi + lo| < 2^31 up to d = 512
+                    v = (float)(256 * acc[tb][0][j] + acc[tb][1][j]);
                   sqv[tb][j] = v + sr[tb][j];
                 }
             } else {
