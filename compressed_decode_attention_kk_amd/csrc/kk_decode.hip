@@ -5,6 +5,16 @@
 #include "kk_decode_kernel.h"
 
 namespace kk {
+// The decode kernel variants are instantiated in their own translation units
+// only (this one sees the template's definition but must not compile it again).
+extern template hipError_t launch_decode_items<1, kFull>(const DecodeArgs&, int, int, hipStream_t);
+extern template hipError_t launch_decode_items<2, kFull>(const DecodeArgs&, int, int, hipStream_t);
+extern template hipError_t launch_decode_items<3, kFull>(const DecodeArgs&, int, int, hipStream_t);
+extern template hipError_t launch_decode_items<1, kLean>(const DecodeArgs&, int, int, hipStream_t);
+extern template hipError_t launch_decode_items<2, kLean>(const DecodeArgs&, int, int, hipStream_t);
+extern template hipError_t launch_decode_items<1, kGqa>(const DecodeArgs&, int, int, hipStream_t);
+extern template hipError_t launch_decode_items<2, kGqa>(const DecodeArgs&, int, int, hipStream_t);
+
 namespace {
 // Merge the split partials of one (entry, sequence, chunk) in a fixed order.
 // A merge may be cut into A.merge_parts workgroups, each owning a contiguous
