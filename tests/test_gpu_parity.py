@@ -373,6 +373,42 @@ def test_outliers_and_zero_tokens(kk):
         check_layer_seq(w, dec, caches, ql, qr, l, 0, 200, src)
 
 
+@pytest.mark.parametrize("split_tokens", [0, 64])
+def test_largest_integer_scores(kk, split_tokens):
+    """The largest integer Q.K scores the kernel can meet: d = 512 with d_R = 64
+    (K = 576), every cache element +-1 (so every code is +-qmax) and every query
+    element 1 (so every fixed-point query element is at its maximum, 16256),
+    40 heads (three row blocks), each bit width.  The latent score then reaches
+    about 2^30 in int32 (|256 hi + lo| summed over 512 features), half the
+    int32 range.  Tokens carry a seeded sign, so the logits are +-24 and the
+    softmax sits on the positive tokens; 200 tokens span several tiles and a
+    ragged tail.  Compared with the oracle like every other case."""
+    table = [[0, 512, 2], [1, 512, 4], [2, 512, 8], [3, 512, 16]]
+    T = 200
+    w = synth.small_workload(15, 4, 40, 1, T, 512, 64, table)
+    model = kk.Model(w.layers, w.n_heads, w.r, w.d_rope)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    sign = torch.where(torch.rand(T, 1, generator=g, device="cuda") < 0.5, -1.0, 1.0)
+    lat = sign.expand(T, 512).contiguous()
+    rope = sign.expand(T, 64).contiguous()
+    caches, src = {}, {}
+    for a in w.anchors():
+        codes, scales = kk.alloc_cache(model, a, 1, T)
+        kk.quantize_write(model, a, lat, rope, codes, scales, torch.arange(T, device="cuda"))
+        caches[a] = (codes, scales)
+        src[a] = (lat.cpu().numpy(), rope.cpu().numpy())
+    ql = torch.ones(4, 1, 40, 512, dtype=torch.bfloat16, device="cuda")
+    qr = torch.ones(4, 1, 40, 64, dtype=torch.bfloat16, device="cuda")
+    dec = kk.Decoder(model, caches, 1, T, T, split_tokens=split_tokens)
+    dec(ql, qr, torch.tensor([T], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    worst = 0.0
+    for l in range(4):
+        worst = max(worst, check_layer_seq(w, dec, caches, ql, qr, l, 0, T, src))
+    print(f"largest integer scores, split_tokens {split_tokens}: worst err ratio {worst:.2e}")
+
+
 def test_zero_tokens_at_item_start_and_all_zero_sequences(kk):
     """Tokens whose stored values are all zero have scale 0 and score 0; they
     still weigh in the softmax.  Sequence 0 is all zero tokens (the output is
